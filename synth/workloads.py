@@ -1,0 +1,400 @@
+"""Workload recipes: the five measured configurations plus small random cases.
+
+Every recipe is seeded; the same (name, seed) always yields the same arrays.
+Shapes and distributions follow the workloads the operator pages describe
+(sparse_flash_mla examples, the SparseAttnSharedKV example, the QSFA decode
+test) at the sizes used for measurement.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .problem import (Problem, banked_rows, bf16_bits, normal_bf16,
+                      packed_rows)
+
+
+def _seqs(seed, n):
+    return np.random.SeedSequence(seed).spawn(n)
+
+
+def _gen(seq):
+    return np.random.Generator(np.random.PCG64(seq))
+
+
+def _base_params(**kw):
+    p = dict(
+        num_heads_q=1, num_heads_kv=1, head_dim=512, rope_head_dim=0,
+        batch_size=1, layout_q="BSND", layout_kv="BSND", q_s=0, q_t=0,
+        ori_kv_s=0, cmp_kv_s=0, ori_block_size=0, cmp_block_size=0,
+        max_seqlen_q=0, max_seqlen_ori_kv=0, max_seqlen_cmp_kv=0,
+        ori_topk=0, cmp_topk=0, cmp_ratio=1, ori_mask_mode=4,
+        cmp_mask_mode=0, ori_win_left=-1, ori_win_right=-1, has_ori_kv=True,
+        has_cmp_kv=False, kv_dtype="bf16", separate_v=False,
+        softmax_scale=1.0, return_softmax_lse=True,
+    )
+    for k, v in kw.items():
+        if k not in p:
+            raise KeyError(k)
+        p[k] = v
+    return p
+
+
+def _prefix(lens):
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lens, dtype=np.int64))
+    return cu
+
+
+def _paged(g, lens, bs, spare_blocks=1):
+    """Random block assignment: returns (block table, number of pool blocks).
+
+    Batch b owns ceil(len_b / bs) blocks drawn from a random permutation of
+    the pool; table entries past a batch's own blocks are 0 (never read).
+    """
+    need = [max(1, -(-int(n) // bs)) for n in lens]
+    total = sum(need) + spare_blocks
+    perm = g.permutation(total).astype(np.int32)
+    width = max(need)
+    table = np.zeros((len(lens), width), dtype=np.int32)
+    pos = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[pos:pos + nb]
+        pos += nb
+    return table, total
+
+
+# ---------------------------------------------------------------------------
+# The five measured configurations.
+# ---------------------------------------------------------------------------
+
+def swa_decode(seed=1):
+    """SWA decode: B=2, q_s=1, q_n=16, d=512, BSND; ori_kv length 512,
+    window (127, 0); no cmp_kv, no sinks; scale 1/sqrt(512); O and LSE."""
+    s_q, s_kv = _seqs(seed, 2)
+    B, qs, qn, d, S = 2, 1, 16, 512, 512
+    arrays = dict(
+        q=normal_bf16(s_q, (B * qs, qn, d)),
+        ori_kv=normal_bf16(s_kv, (B * S, d)),
+    )
+    params = _base_params(
+        num_heads_q=qn, batch_size=B, layout_q="BSND", layout_kv="BSND",
+        q_s=qs, q_t=B * qs, ori_kv_s=S, max_seqlen_q=qs, max_seqlen_ori_kv=S,
+        ori_mask_mode=4, ori_win_left=127, ori_win_right=0, cmp_mask_mode=0,
+        cmp_ratio=1, has_cmp_kv=False, softmax_scale=1.0 / math.sqrt(d))
+    return Problem("swa_decode", seed, params, arrays,
+                   "q, ori_kv ~ N(0,1) bf16; query at position 511")
+
+
+def csa_decode_paged(seed=2):
+    """CSA decode, paged: B=4, q_n=64, d=512; context 32768, window 128;
+    cmp_ratio 4 so 8192 compressed rows; TopK 512 drawn without replacement
+    from the 8192 (all visible at position 32767); PA block 128 with random
+    permutation block tables; sinks ~ N(0,1)."""
+    s_q, s_ori, s_cmp, s_tab, s_idx, s_sink = _seqs(seed, 6)
+    B, qn, d, bs, L, C, r, K = 4, 64, 512, 128, 32768, 8192, 4, 512
+    g_tab = _gen(s_tab)
+    ori_bt = g_tab.permutation(B * L // bs).astype(np.int32).reshape(B, L // bs)
+    cmp_blocks = B * L // bs // 4              # pool of 256 blocks
+    cmp_bt = g_tab.permutation(cmp_blocks).astype(np.int32).reshape(B, cmp_blocks // B)
+    g_idx = _gen(s_idx)
+    idx = np.stack([g_idx.choice(C, K, replace=False) for _ in range(B)]).astype(np.int32)
+    arrays = dict(
+        q=normal_bf16(s_q, (B, qn, d)),
+        ori_kv=banked_rows(s_ori, B * L, lambda s, n: normal_bf16(s, (n, d))),
+        cmp_kv=banked_rows(s_cmp, cmp_blocks * bs, lambda s, n: normal_bf16(s, (n, d))),
+        ori_block_table=ori_bt, cmp_block_table=cmp_bt,
+        seqused_ori_kv=np.full(B, L, np.int32),
+        seqused_cmp_kv=np.full(B, C, np.int32),
+        cmp_residual_kv=np.zeros(B, np.int32),
+        cmp_sparse_indices=idx.reshape(B, 1, K),
+        sinks=_gen(s_sink).standard_normal(qn, dtype=np.float32),
+    )
+    params = _base_params(
+        num_heads_q=qn, batch_size=B, layout_q="BSND", layout_kv="PA_BSND",
+        q_s=1, q_t=B, ori_block_size=bs, cmp_block_size=bs, max_seqlen_q=1,
+        max_seqlen_ori_kv=L, max_seqlen_cmp_kv=C, cmp_topk=K, cmp_ratio=r,
+        ori_mask_mode=4, ori_win_left=127, ori_win_right=0, cmp_mask_mode=3,
+        has_cmp_kv=True, softmax_scale=1.0 / math.sqrt(d))
+    return Problem("csa_decode_paged", seed, params, arrays,
+                   "q, kv ~ N(0,1) bf16; 512 of 8192 compressed rows per query")
+
+
+def _varlen_lengths(seed):
+    (s_len,) = _seqs(seed * 1000 + 7, 1)
+    return _gen(s_len).integers(16384, 131072 + 1, size=8).astype(np.int64)
+
+
+def hca_varlen(seed=3):
+    """HCA varlen TND: B=8, q_n=128, d=512; contexts ~ U[16384, 131072];
+    window 128; cmp_ratio 128 with every causally visible compressed row;
+    kv ~ N(0,1), q ~ N(0, 0.5^2); sinks ~ N(0,1); LSE returned."""
+    s_q, s_ori, s_cmp, s_sink = _seqs(seed, 4)
+    B, qn, d, r = 8, 128, 512, 128
+    L = _varlen_lengths(seed)
+    C = L // r
+    arrays = dict(
+        q=normal_bf16(s_q, (B, qn, d), std=0.5),
+        ori_kv=banked_rows(s_ori, int(L.sum()), lambda s, n: normal_bf16(s, (n, d))),
+        cmp_kv=banked_rows(s_cmp, int(C.sum()), lambda s, n: normal_bf16(s, (n, d))),
+        cu_seqlens_q=np.arange(B + 1, dtype=np.int32),
+        cu_seqlens_ori_kv=_prefix(L), cu_seqlens_cmp_kv=_prefix(C),
+        cmp_residual_kv=(L % r).astype(np.int32),
+        sinks=_gen(s_sink).standard_normal(qn, dtype=np.float32),
+    )
+    params = _base_params(
+        num_heads_q=qn, batch_size=B, layout_q="TND", layout_kv="TND", q_t=B,
+        max_seqlen_q=1, max_seqlen_ori_kv=int(L.max()),
+        max_seqlen_cmp_kv=int(C.max()), cmp_ratio=r, ori_mask_mode=4,
+        ori_win_left=127, ori_win_right=0, cmp_mask_mode=3, has_cmp_kv=True,
+        softmax_scale=1.0 / math.sqrt(d))
+    return Problem("hca_varlen", seed, params, arrays,
+                   "contexts %s" % L.tolist())
+
+
+def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64):
+    """Token-wise sparse MLA-absorb with rope: B=32, q_s=2, q_n=128, Q_D=576,
+    separate K (576) and V (512) bf16 pools, PA block 64, kv length 65536,
+    TopK 2048 drawn uniformly from the causal positions, scale 1/sqrt(576)."""
+    s_q, s_k, s_v, s_tab, s_idx = _seqs(seed, 5)
+    qn, dq = 128, 576
+    nblk = batch * kv_len // bs
+    g_tab = _gen(s_tab)
+    bt = g_tab.permutation(nblk).astype(np.int32).reshape(batch, kv_len // bs)
+    g_idx = _gen(s_idx)
+    rows = []
+    for _b in range(batch):
+        for s in range(q_s):
+            # query s of a q_s-token step sits at position kv_len - q_s + s,
+            # so positions 0 .. kv_len - q_s + s are its causal range
+            rows.append(g_idx.choice(kv_len - q_s + s + 1, topk, replace=False))
+    idx = np.stack(rows).astype(np.int32).reshape(batch * q_s, 1, topk)
+    arrays = dict(
+        q=normal_bf16(s_q, (batch * q_s, qn, dq)),
+        ori_kv=banked_rows(s_k, nblk * bs, lambda s, n: normal_bf16(s, (n, dq))),
+        ori_v=banked_rows(s_v, nblk * bs, lambda s, n: normal_bf16(s, (n, 512))),
+        ori_block_table=bt,
+        seqused_ori_kv=np.full(batch, kv_len, np.int32),
+        ori_sparse_indices=idx,
+    )
+    params = _base_params(
+        num_heads_q=qn, rope_head_dim=64, batch_size=batch, layout_q="BSND",
+        layout_kv="PA_BSND", q_s=q_s, q_t=batch * q_s, ori_block_size=bs,
+        max_seqlen_q=q_s, max_seqlen_ori_kv=kv_len, ori_topk=topk,
+        ori_mask_mode=3, has_cmp_kv=False, separate_v=True,
+        softmax_scale=1.0 / math.sqrt(dq))
+    return Problem("sfa_mla_rope", seed, params, arrays,
+                   "q, K, V ~ N(0,1) bf16; %d of the causal positions" % topk)
+
+
+def c8_packed(seed=5, fmt="int8", topk=2048):
+    """Quantised packed KV: the HCA-varlen shapes (TND, B=8, q_n=128, the same
+    context lengths) with Q_D=576 and 656-byte packed rows (512 INT8 or
+    FP8-E4M3 codes, 64 bf16 rope values, 4 fp32 per-128-tile scales), V =
+    dequantised nope; TopK 2048 over each sequence's positions."""
+    s_q, s_kv, s_idx = _seqs(seed, 3)
+    B, qn, dq = 8, 128, 576
+    L = _varlen_lengths(3)
+    g_idx = _gen(s_idx)
+    idx = np.stack([g_idx.choice(int(n), topk, replace=False) for n in L]).astype(np.int32)
+    arrays = dict(
+        q=normal_bf16(s_q, (B, qn, dq), std=0.5),
+        ori_kv=banked_rows(s_kv, int(L.sum()), lambda s, n: packed_rows(s, n, 64, fmt)),
+        cu_seqlens_q=np.arange(B + 1, dtype=np.int32),
+        cu_seqlens_ori_kv=_prefix(L),
+        ori_sparse_indices=idx.reshape(B, 1, topk),
+    )
+    params = _base_params(
+        num_heads_q=qn, rope_head_dim=64, batch_size=B, layout_q="TND",
+        layout_kv="TND", q_t=B, max_seqlen_q=1,
+        max_seqlen_ori_kv=int(L.max()), ori_topk=topk, ori_mask_mode=3,
+        has_cmp_kv=False,
+        kv_dtype="int8_packed" if fmt == "int8" else "fp8_e4m3_packed",
+        softmax_scale=1.0 / math.sqrt(dq))
+    return Problem("c8_packed_" + fmt, seed, params, arrays,
+                   "packed %s rows, contexts %s" % (fmt, L.tolist()))
+
+
+WORKLOADS = {
+    "swa_decode": swa_decode,
+    "csa_decode_paged": csa_decode_paged,
+    "hca_varlen": hca_varlen,
+    "sfa_mla_rope": sfa_mla_rope,
+    "c8_packed_int8": lambda seed=5: c8_packed(seed, "int8"),
+    "c8_packed_fp8": lambda seed=5: c8_packed(seed, "fp8"),
+}
+
+
+def make_workload(name, seed=None, **kw):
+    fn = WORKLOADS[name]
+    return fn(**kw) if seed is None else fn(seed=seed, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Small random problems (edge cases, every layout and mode).
+# ---------------------------------------------------------------------------
+
+def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
+                num_heads_q=None, rope_head_dim=None, kv_dtype=None,
+                batch=None, max_q=4, max_kv=64, block_size=None,
+                cmp_ratio=None, sinks=None, dist="normal", topk=None,
+                separate_v=None, q_lens=None, ori_lens=None,
+                seqused_q=None, duplicates=False, win=None, masks=None):
+    """A small random problem.
+
+    family: "swa" (ori window only), "csa" (window + TopK compressed rows),
+    "hca" (window + all compressed rows) or "sfa" (TopK over one KV, the
+    token-wise sparse MLA-absorb form).  Lengths, windows, mask modes,
+    layouts and index tails are drawn at random unless given.  dist "p4" uses
+    the SparseAttnSharedKV example's draws (q ~ U(-10,10), kv ~ U(-5,10),
+    sinks ~ U(0,1)), which give very peaked softmaxes.
+    """
+    ss = np.random.SeedSequence(seed)
+    s_cfg, s_q, s_ori, s_v, s_cmp, s_idx, s_tab, s_sink = ss.spawn(8)
+    g = _gen(s_cfg)
+    family = family or g.choice(["swa", "csa", "hca", "sfa"])
+    B = batch or int(g.integers(1, 4))
+    layout_q = layout_q or str(g.choice(["BSND", "TND"]))
+    if layout_kv is None:
+        layout_kv = str(g.choice([layout_q, "PA_BSND"]))
+    qn = num_heads_q or int(g.choice([1, 2, 3, 4, 16]))
+    rope = rope_head_dim if rope_head_dim is not None else (
+        int(g.choice([0, 64])) if family == "sfa" else 0)
+    kv_dtype = kv_dtype or "bf16"
+    packed = kv_dtype != "bf16"
+    if separate_v is None:
+        separate_v = bool(family == "sfa" and not packed and g.integers(0, 2))
+    bs = block_size or int(g.choice([1, 2, 16]))
+    r = cmp_ratio or (1 if family in ("swa", "sfa") else int(g.choice([1, 2, 4])))
+    has_cmp = family in ("csa", "hca")
+
+    q_lens = list(q_lens) if q_lens is not None else [int(g.integers(1, max_q + 1)) for _ in range(B)]
+    ori_lens = list(ori_lens) if ori_lens is not None else [
+        int(g.integers(q_lens[b], max_kv + 1)) for b in range(B)]
+    cmp_lens = [n // r for n in ori_lens] if has_cmp else [0] * B
+    residual = [n % r for n in ori_lens]
+
+    if win is None:
+        win = (int(g.choice([-1, 0, 1, 3, 7, 127])), int(g.choice([-1, 0, 0, 2])))
+    if masks is None:
+        if family == "sfa":
+            masks = (int(g.choice([0, 3])), 0)
+        else:
+            masks = (int(g.choice([0, 3, 4])), int(g.choice([0, 3])) if has_cmp else 0)
+    d_qk = 512 + rope
+
+    # queries
+    if layout_q == "BSND":
+        q_s = max(q_lens)
+        rows = B * q_s
+        use_seqused_q = seqused_q if seqused_q is not None else (
+            any(n != q_s for n in q_lens) or bool(g.integers(0, 4) == 0))
+    else:
+        q_s = 0
+        rows = sum(q_lens)
+        use_seqused_q = False
+    if dist == "p4":
+        qv = _gen(s_q).uniform(-10, 10, (rows, qn, d_qk)).astype(np.float32)
+        q = bf16_bits(qv)
+    else:
+        q = normal_bf16(s_q, (rows, qn, d_qk))
+
+    def kv_rows(seq, n, width_elems):
+        if packed:
+            return packed_rows(seq, n, rope, "int8" if kv_dtype == "int8_packed" else "fp8")
+        if dist == "p4":
+            return bf16_bits(_gen(seq).uniform(-5, 10, (n, width_elems)).astype(np.float32))
+        return normal_bf16(seq, (n, width_elems))
+
+    g_tab = _gen(s_tab)
+    arrays = dict(q=q)
+    params = _base_params(
+        num_heads_q=qn, rope_head_dim=rope, batch_size=B, layout_q=layout_q,
+        layout_kv=layout_kv, q_s=q_s, q_t=rows, max_seqlen_q=max(q_lens),
+        max_seqlen_ori_kv=max(ori_lens), max_seqlen_cmp_kv=max(cmp_lens) if has_cmp else 0,
+        cmp_ratio=r, ori_mask_mode=masks[0], cmp_mask_mode=masks[1],
+        ori_win_left=win[0], ori_win_right=win[1], has_cmp_kv=has_cmp,
+        kv_dtype=kv_dtype, separate_v=separate_v,
+        softmax_scale=(1.0 / 24.0) if dist == "p4" else 1.0 / math.sqrt(d_qk))
+    if layout_q == "TND":
+        arrays["cu_seqlens_q"] = _prefix(q_lens)
+    elif use_seqused_q:
+        arrays["seqused_q"] = np.asarray(q_lens, np.int32)
+
+    def place(name, lens, seq, bs_key, s_key, width):
+        if layout_kv == "BSND":
+            S = max(1, max(lens) + int(g.integers(0, 3)))
+            params[s_key] = S
+            arrays[name] = kv_rows(seq, B * S, width)
+            return "seqused", None
+        if layout_kv == "TND":
+            arrays[name] = kv_rows(seq, max(1, int(sum(lens))), width)
+            return "cu", None
+        table, nblocks = _paged(g_tab, lens, bs)
+        params[bs_key] = bs
+        arrays[name] = kv_rows(seq, nblocks * bs, width)
+        return "pa", table
+
+    kind, table = place("ori_kv", ori_lens, s_ori, "ori_block_size", "ori_kv_s", d_qk)
+    if kind == "cu":
+        arrays["cu_seqlens_ori_kv"] = _prefix(ori_lens)
+    elif kind == "pa":
+        arrays["ori_block_table"] = table
+        arrays["seqused_ori_kv"] = np.asarray(ori_lens, np.int32)
+    elif any(n != params["ori_kv_s"] for n in ori_lens) or g.integers(0, 2):
+        arrays["seqused_ori_kv"] = np.asarray(ori_lens, np.int32)
+    if separate_v:
+        arrays["ori_v"] = kv_rows(s_v, arrays["ori_kv"].shape[0], 512)
+
+    if has_cmp:
+        kind, table = place("cmp_kv", cmp_lens, s_cmp,
+                            "cmp_block_size", "cmp_kv_s", d_qk)
+        if kind == "cu":
+            arrays["cu_seqlens_cmp_kv"] = _prefix(cmp_lens)
+        elif kind == "pa":
+            arrays["cmp_block_table"] = table
+            arrays["seqused_cmp_kv"] = np.asarray(cmp_lens, np.int32)
+        else:
+            arrays["seqused_cmp_kv"] = np.asarray(cmp_lens, np.int32)
+        arrays["cmp_residual_kv"] = np.asarray(residual, np.int32)
+
+    # TopK index lists: draws over the whole sequence (some beyond the causal
+    # limit), optional duplicates, and a -1 tail of random length.
+    g_idx = _gen(s_idx)
+
+    def index_rows(lens_for_draw, K):
+        out = np.full((rows, 1, K), -1, dtype=np.int32)
+        for b in range(B):
+            n_rows_b = q_s if layout_q == "BSND" else q_lens[b]
+            base = b * q_s if layout_q == "BSND" else sum(q_lens[:b])
+            for i in range(n_rows_b):
+                n = lens_for_draw[b]
+                if n <= 0:
+                    continue
+                k = int(g_idx.integers(0, K + 1))
+                if duplicates:
+                    vals = g_idx.integers(0, n, size=k)
+                else:
+                    k = min(k, n)
+                    vals = g_idx.choice(n, k, replace=False)
+                out[base + i, 0, :k] = vals
+        return out
+
+    if family == "sfa":
+        K = topk or int(g.integers(1, max_kv + 1))
+        params["ori_topk"] = K
+        arrays["ori_sparse_indices"] = index_rows(ori_lens, K)
+    if family == "csa":
+        K = topk or int(g.integers(1, 2 * max(1, max(cmp_lens)) + 2))
+        params["cmp_topk"] = K
+        arrays["cmp_sparse_indices"] = index_rows(cmp_lens, K)
+
+    use_sinks = sinks if sinks is not None else bool(g.integers(0, 2))
+    if use_sinks:
+        gs = _gen(s_sink)
+        arrays["sinks"] = (gs.uniform(0, 1, qn) if dist == "p4"
+                           else gs.standard_normal(qn)).astype(np.float32)
+    return Problem("tiny_%s_%d" % (family, seed), seed, params, arrays,
+                   "random tiny %s" % family)
