@@ -1,0 +1,419 @@
+// Host side of libsfmla: parameter validation, plan / workspace sizing, the
+// parameter fingerprint, kernel selection and the extern "C" entry points.
+//
+// The validation rules restate the sparse_flash_mla API page's 约束说明
+// (constraints) that can be decided from shapes and attributes alone; rules
+// that depend on tensor values are the caller's, as the page says.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "sfmla_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sfmla_status fail(sfmla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+sfmla_status ok() {
+  g_err.clear();
+  return SFMLA_OK;
+}
+
+#define REQUIRE(cond, ...)                                           \
+  do {                                                               \
+    if (!(cond)) return fail(SFMLA_ERR_INVALID_ARGUMENT, __VA_ARGS__); \
+  } while (0)
+
+// FNV-1a over every field, one at a time (no padding bytes enter the hash).
+uint32_t fingerprint(const sfmla_params& p) {
+  uint32_t h = 2166136261u;
+  auto mix = [&h](int64_t v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (uint32_t)((v >> (8 * i)) & 0xff);
+      h *= 16777619u;
+    }
+  };
+  const int32_t f32[] = {
+      p.num_heads_q, p.num_heads_kv, p.head_dim, p.rope_head_dim, p.batch_size, p.layout_q,
+      p.layout_kv, p.q_s, p.q_t, p.ori_kv_s, p.cmp_kv_s, p.ori_block_size, p.cmp_block_size,
+      p.ori_block_table_cols, p.cmp_block_table_cols, p.max_seqlen_q, p.max_seqlen_ori_kv,
+      p.max_seqlen_cmp_kv, p.ori_topk, p.cmp_topk, p.cmp_ratio, p.ori_mask_mode,
+      p.cmp_mask_mode, p.ori_win_left, p.ori_win_right, p.has_ori_kv, p.has_cmp_kv,
+      p.kv_dtype, p.has_separate_v, p.has_sinks, p.return_softmax_lse, p.has_seqused_q,
+      p.has_seqused_ori_kv, p.has_seqused_cmp_kv, p.has_cmp_residual_kv};
+  for (int32_t v : f32) mix(v);
+  mix(p.ori_kv_rows);
+  mix(p.cmp_kv_rows);
+  return h;
+}
+
+sfmla_status validate(const sfmla_params* pp) {
+  REQUIRE(pp != nullptr, "params is NULL");
+  const sfmla_params& p = *pp;
+  REQUIRE(p.num_heads_q >= 1 && p.num_heads_q <= 128, "num_heads_q must be in 1..128 (got %d)",
+          p.num_heads_q);
+  REQUIRE(p.num_heads_kv == 1, "num_heads_kv must be 1 (got %d)", p.num_heads_kv);
+  REQUIRE(p.head_dim == 512, "head_dim must be 512 (got %d)", p.head_dim);
+  REQUIRE(p.rope_head_dim == 0 || p.rope_head_dim == 64, "rope_head_dim must be 0 or 64 (got %d)",
+          p.rope_head_dim);
+  REQUIRE(p.batch_size > 0, "batch_size must be > 0");
+  REQUIRE(p.layout_q == SFMLA_LAYOUT_BSND || p.layout_q == SFMLA_LAYOUT_TND,
+          "layout_q must be BSND or TND");
+  REQUIRE(p.layout_kv == SFMLA_LAYOUT_BSND || p.layout_kv == SFMLA_LAYOUT_TND ||
+              p.layout_kv == SFMLA_LAYOUT_PA_BSND,
+          "layout_kv must be BSND, TND or PA_BSND");
+  REQUIRE(p.layout_kv == SFMLA_LAYOUT_PA_BSND || p.layout_kv == p.layout_q,
+          "a non-paged layout_kv must equal layout_q");
+  if (p.layout_q == SFMLA_LAYOUT_BSND) {
+    REQUIRE(p.q_s > 0, "BSND q needs q_s > 0");
+    REQUIRE((int64_t)p.q_t == (int64_t)p.batch_size * p.q_s, "BSND q_t must be batch_size*q_s");
+  } else {
+    REQUIRE(p.q_t > 0, "TND q needs q_t > 0");
+  }
+  REQUIRE(p.max_seqlen_q > 0, "max_seqlen_q must be > 0");
+  REQUIRE(p.has_ori_kv == 1, "ori_kv is required");
+  REQUIRE(p.max_seqlen_ori_kv > 0, "max_seqlen_ori_kv must be > 0");
+  REQUIRE(p.ori_kv_rows > 0, "ori_kv_rows must be > 0");
+  REQUIRE(p.ori_kv_rows < ((int64_t)1 << 40), "ori_kv_rows too large");
+  REQUIRE(p.ori_win_left >= -1 && p.ori_win_right >= -1, "window bounds must be -1 or >= 0");
+  REQUIRE(p.ori_topk >= 0 && p.cmp_topk >= 0, "topk must be >= 0");
+  REQUIRE(p.ori_mask_mode == 0 || p.ori_mask_mode == 3 || p.ori_mask_mode == 4,
+          "ori_mask_mode must be 0, 3 or 4");
+  REQUIRE(p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_INT8_PACKED ||
+              p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED,
+          "unknown kv_dtype");
+  REQUIRE(!(p.has_separate_v && p.kv_dtype != SFMLA_KV_BF16),
+          "a separate V is only supported for bf16 KV (packed V is the dequantised nope)");
+  if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.ori_kv_s > 0, "BSND ori_kv needs ori_kv_s > 0");
+  if (p.layout_kv == SFMLA_LAYOUT_PA_BSND) {
+    REQUIRE(p.ori_block_size >= 1 && p.ori_block_size <= 1024, "ori_block_size must be in 1..1024");
+    REQUIRE(p.ori_block_table_cols > 0, "PA needs ori_block_table_cols > 0");
+    REQUIRE(p.has_seqused_ori_kv, "PA needs seqused_ori_kv");
+  }
+  if (p.has_cmp_kv) {
+    REQUIRE(p.has_cmp_kv == 1, "has_cmp_kv must be 0 or 1");
+    REQUIRE(p.cmp_ratio >= 1, "cmp_ratio must be >= 1");
+    REQUIRE(p.cmp_mask_mode == 0 || p.cmp_mask_mode == 3, "cmp_mask_mode must be 0 or 3");
+    REQUIRE(p.cmp_kv_rows > 0 && p.cmp_kv_rows < ((int64_t)1 << 40), "cmp_kv_rows out of range");
+    if (p.cmp_mask_mode == 3)
+      REQUIRE(p.has_cmp_residual_kv, "cmp_mask_mode 3 needs cmp_residual_kv");
+    if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.cmp_kv_s > 0, "BSND cmp_kv needs cmp_kv_s > 0");
+    if (p.layout_kv == SFMLA_LAYOUT_PA_BSND) {
+      REQUIRE(p.cmp_block_size >= 1 && p.cmp_block_size <= 1024, "cmp_block_size must be in 1..1024");
+      REQUIRE(p.cmp_block_table_cols > 0, "PA cmp_kv needs cmp_block_table_cols > 0");
+      REQUIRE(p.has_seqused_cmp_kv, "PA cmp_kv needs seqused_cmp_kv");
+    }
+  } else {
+    REQUIRE(p.cmp_topk == 0, "cmp_topk must be 0 without cmp_kv");
+    REQUIRE(p.cmp_ratio == 1, "cmp_ratio must be 1 without cmp_kv");
+  }
+  return ok();
+}
+
+int64_t max_list(const sfmla_params& p) {
+  int64_t n;
+  if (p.ori_topk > 0) {
+    n = p.ori_topk;
+  } else if (p.ori_mask_mode == 4 && p.ori_win_left >= 0 && p.ori_win_right >= 0) {
+    n = std::min<int64_t>(p.max_seqlen_ori_kv, (int64_t)p.ori_win_left + p.ori_win_right + 1);
+  } else {
+    n = p.max_seqlen_ori_kv;
+  }
+  if (p.has_cmp_kv) n += p.cmp_topk > 0 ? p.cmp_topk : p.max_seqlen_cmp_kv;
+  return n;
+}
+
+int max_splits(const sfmla_params& p) {
+  const int64_t n = max_list(p);
+  const int64_t s = (n + sfmla::kSplitRows - 1) / sfmla::kSplitRows;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 4096));
+}
+
+size_t metadata_ints(const sfmla_params& p) {
+  return (size_t)sfmla::kHeaderInts + (size_t)sfmla::kRecInts * (size_t)p.q_t;
+}
+
+size_t workspace_bytes(const sfmla_params& p) {
+  const int s = max_splits(p);
+  if (s <= 1) return 0;
+  const size_t slots = (size_t)p.q_t * s * p.num_heads_q;
+  return slots * 512 * sizeof(float) + ((slots * sizeof(float) + 255) / 256) * 256;
+}
+
+// Waves per workgroup (16 heads each) and head groups: as many heads per
+// workgroup as possible while the grid still has about one workgroup per CU.
+void choose_groups(const sfmla_params& p, int* nw, int* groups) {
+  const int64_t units = (int64_t)p.q_t * max_splits(p);
+  int w = std::min(8, (p.num_heads_q + 15) / 16);
+  while (w > 1 && units * ((p.num_heads_q + 16 * w - 1) / (16 * w)) < 256) w /= 2;
+  *nw = w;
+  *groups = (p.num_heads_q + 16 * w - 1) / (16 * w);
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const int32_t* meta,
+                           size_t n_ints, float scale, sfmla::FwdArgs* a) {
+  REQUIRE(t != nullptr, "tensors is NULL");
+  REQUIRE(meta != nullptr, "metadata is NULL");
+  if (n_ints < metadata_ints(p))
+    return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "metadata holds %zu int32, needs %zu", n_ints,
+                metadata_ints(p));
+  REQUIRE(std::isfinite(scale), "softmax_scale must be finite");
+  REQUIRE(t->q && aligned16(t->q), "q must be a 16-byte aligned device pointer");
+  REQUIRE(t->ori_kv && aligned16(t->ori_kv), "ori_kv must be a 16-byte aligned device pointer");
+  const bool packed = p.kv_dtype != SFMLA_KV_BF16;
+  const int64_t need_row = packed ? 512 + 2 * p.rope_head_dim + 16
+                                  : (p.rope_head_dim && !t->ori_rope ? 1152 : 1024);
+  REQUIRE(t->ori_kv_stride >= need_row && t->ori_kv_stride % 16 == 0,
+          "ori_kv_stride must be >= %lld bytes and a multiple of 16", (long long)need_row);
+  if (t->ori_rope) {
+    REQUIRE(!packed && p.rope_head_dim == 64, "ori_rope is only used with bf16 KV and rope 64");
+    REQUIRE(aligned16(t->ori_rope) && t->ori_rope_stride >= 128 && t->ori_rope_stride % 16 == 0,
+            "ori_rope must be 16-byte aligned with a stride >= 128, multiple of 16");
+  }
+  REQUIRE((p.has_separate_v != 0) == (t->ori_v != nullptr), "has_separate_v must match ori_v");
+  if (t->ori_v)
+    REQUIRE(aligned16(t->ori_v) && t->ori_v_stride >= 1024 && t->ori_v_stride % 16 == 0,
+            "ori_v must be 16-byte aligned with a stride >= 1024, multiple of 16");
+  if (p.has_cmp_kv) {
+    REQUIRE(t->cmp_kv && aligned16(t->cmp_kv), "cmp_kv must be a 16-byte aligned device pointer");
+    const int64_t need_c = packed ? 512 + 2 * p.rope_head_dim + 16
+                                  : (p.rope_head_dim && !t->cmp_rope ? 1152 : 1024);
+    REQUIRE(t->cmp_kv_stride >= need_c && t->cmp_kv_stride % 16 == 0,
+            "cmp_kv_stride must be >= %lld bytes and a multiple of 16", (long long)need_c);
+    if (t->cmp_rope)
+      REQUIRE(!packed && p.rope_head_dim == 64 && aligned16(t->cmp_rope) &&
+                  t->cmp_rope_stride >= 128 && t->cmp_rope_stride % 16 == 0,
+              "cmp_rope needs bf16 KV, rope 64, 16-byte alignment and stride >= 128");
+  } else {
+    REQUIRE(t->cmp_kv == nullptr, "cmp_kv given but has_cmp_kv is 0");
+  }
+  if (p.layout_kv == SFMLA_LAYOUT_PA_BSND) {
+    REQUIRE(t->ori_block_table, "PA needs ori_block_table");
+    if (p.has_cmp_kv) REQUIRE(t->cmp_block_table, "PA needs cmp_block_table");
+  }
+  REQUIRE((p.ori_topk > 0) == (t->ori_sparse_indices != nullptr),
+          "ori_sparse_indices must be given exactly when ori_topk > 0");
+  REQUIRE((p.cmp_topk > 0) == (t->cmp_sparse_indices != nullptr),
+          "cmp_sparse_indices must be given exactly when cmp_topk > 0 (CSA) and not for HCA");
+  REQUIRE((p.has_sinks != 0) == (t->sinks != nullptr), "has_sinks must match sinks");
+  REQUIRE((p.return_softmax_lse != 0) == (t->softmax_lse != nullptr),
+          "return_softmax_lse must match softmax_lse");
+  REQUIRE(t->attention_out && ((uintptr_t)t->attention_out & 7) == 0,
+          "attention_out must be an 8-byte aligned device pointer");
+
+  sfmla::FwdArgs& f = *a;
+  std::memset(&f, 0, sizeof f);
+  f.qn = p.num_heads_q;
+  f.q_t = p.q_t;
+  f.layout_kv = p.layout_kv;
+  f.rope = p.rope_head_dim;
+  f.ori_bs = p.ori_block_size;
+  f.cmp_bs = p.cmp_block_size;
+  f.ori_bt_cols = p.ori_block_table_cols;
+  f.cmp_bt_cols = p.cmp_block_table_cols;
+  f.ori_rows = p.ori_kv_rows;
+  f.cmp_rows = p.cmp_kv_rows;
+  f.ori_topk = p.ori_topk;
+  f.cmp_topk = p.cmp_topk;
+  f.ori_mode = p.ori_mask_mode;
+  f.win_l = p.ori_win_left;
+  f.win_r = p.ori_win_right;
+  f.has_cmp = p.has_cmp_kv;
+  f.max_splits = max_splits(p);
+  f.has_sinks = p.has_sinks;
+  f.fingerprint = fingerprint(p);
+  f.scale_log2 = scale * 1.4426950408889634f;
+  f.meta = meta;
+  f.q = (const uint16_t*)t->q;
+  f.ori_kv = (const char*)t->ori_kv;
+  f.ori_stride = t->ori_kv_stride;
+  f.ori_rope = (const char*)t->ori_rope;
+  f.ori_rope_stride = t->ori_rope_stride;
+  f.ori_v = (const char*)t->ori_v;
+  f.ori_v_stride = t->ori_v_stride;
+  f.cmp_kv = (const char*)t->cmp_kv;
+  f.cmp_stride = t->cmp_kv_stride;
+  f.cmp_rope = (const char*)t->cmp_rope;
+  f.cmp_rope_stride = t->cmp_rope_stride;
+  f.ori_bt = t->ori_block_table;
+  f.cmp_bt = t->cmp_block_table;
+  f.ori_idx = t->ori_sparse_indices;
+  f.cmp_idx = t->cmp_sparse_indices;
+  f.sinks = t->sinks;
+  f.out = (uint16_t*)t->attention_out;
+  f.lse = t->softmax_lse;
+  f.status = t->status;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sfmla_last_error(void) { return g_err.c_str(); }
+
+const char* sfmla_version(void) { return SFMLA_VERSION; }
+
+sfmla_status sfmla_metadata_size(const sfmla_params* params, size_t* n_ints) {
+  sfmla_status s = validate(params);
+  if (s != SFMLA_OK) return s;
+  REQUIRE(n_ints != nullptr, "n_ints is NULL");
+  *n_ints = metadata_ints(*params);
+  return ok();
+}
+
+sfmla_status sfmla_workspace_size(const sfmla_params* params, size_t* bytes) {
+  sfmla_status s = validate(params);
+  if (s != SFMLA_OK) return s;
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  *bytes = workspace_bytes(*params);
+  return ok();
+}
+
+sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len,
+                            int32_t* metadata, size_t n_ints, void* stream) {
+  sfmla_status s = validate(params);
+  if (s != SFMLA_OK) return s;
+  const sfmla_params& p = *params;
+  REQUIRE(len != nullptr, "lengths is NULL");
+  REQUIRE(metadata != nullptr, "metadata is NULL");
+  if (n_ints < metadata_ints(p))
+    return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "metadata holds %zu int32, needs %zu", n_ints,
+                metadata_ints(p));
+  REQUIRE((p.layout_q == SFMLA_LAYOUT_TND) == (len->cu_seqlens_q != nullptr),
+          "cu_seqlens_q is required for TND q and not accepted otherwise");
+  REQUIRE((p.layout_kv == SFMLA_LAYOUT_TND) == (len->cu_seqlens_ori_kv != nullptr),
+          "cu_seqlens_ori_kv is required for TND kv and not accepted otherwise");
+  REQUIRE((p.layout_kv == SFMLA_LAYOUT_TND && p.has_cmp_kv) == (len->cu_seqlens_cmp_kv != nullptr),
+          "cu_seqlens_cmp_kv is required for TND cmp_kv and not accepted otherwise");
+  REQUIRE((p.has_seqused_q != 0) == (len->seqused_q != nullptr), "has_seqused_q must match");
+  REQUIRE((p.has_seqused_ori_kv != 0) == (len->seqused_ori_kv != nullptr),
+          "has_seqused_ori_kv must match");
+  REQUIRE((p.has_seqused_cmp_kv != 0) == (len->seqused_cmp_kv != nullptr),
+          "has_seqused_cmp_kv must match");
+  REQUIRE((p.has_cmp_residual_kv != 0) == (len->cmp_residual_kv != nullptr),
+          "has_cmp_residual_kv must match");
+  REQUIRE(!(p.has_seqused_cmp_kv && !p.has_cmp_kv), "seqused_cmp_kv given without cmp_kv");
+  sfmla::PlanArgs a;
+  a.p = p;
+  a.len = *len;
+  a.meta = metadata;
+  a.fingerprint = fingerprint(p);
+  a.max_splits = max_splits(p);
+  hipError_t e = sfmla::launch_plan(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "plan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
+                           const int32_t* metadata, size_t n_ints, float softmax_scale,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  sfmla_status s = validate(params);
+  if (s != SFMLA_OK) return s;
+  const sfmla_params& p = *params;
+  sfmla::FwdArgs a;
+  s = fill_fwd_args(p, t, metadata, n_ints, softmax_scale, &a);
+  if (s != SFMLA_OK) return s;
+  const size_t need = workspace_bytes(p);
+  if (need) {
+    if (!workspace || ws_bytes < need)
+      return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes,
+                  need);
+    REQUIRE(((uintptr_t)workspace & 255) == 0, "workspace must be 256-byte aligned");
+    const size_t slots = (size_t)p.q_t * a.max_splits * p.num_heads_q;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = (float*)((char*)workspace + slots * 512 * sizeof(float));
+  }
+  int nw, groups;
+  choose_groups(p, &nw, &groups);
+  const int dqk = 512 + p.rope_head_dim;
+  const int vmode = p.has_separate_v ? 1 : 0;
+  hipError_t e = sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
+  if (a.max_splits > 1) {
+    sfmla::CombineArgs c;
+    std::memset(&c, 0, sizeof c);
+    c.rows = p.q_t;
+    c.heads = p.num_heads_q;
+    c.dv = 512;
+    c.meta = metadata;
+    c.o_part_stride = (int64_t)p.num_heads_q * 512;
+    c.o_row_stride = (int64_t)a.max_splits * p.num_heads_q * 512;
+    c.lse_part_stride = p.num_heads_q;
+    c.lse_row_stride = (int64_t)a.max_splits * p.num_heads_q;
+    c.part_o = a.ws_o;
+    c.part_lse = a.ws_lse;
+    c.sinks = t->sinks;
+    c.out = a.out;
+    c.lse_out = a.lse;
+    e = sfmla::launch_combine(c, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+sfmla_status sfmla_combine(int32_t n_parts, int32_t rows, int32_t heads, int32_t dv,
+                           const float* part_o, const float* part_lse, const float* sinks,
+                           void* out, float* lse_out, void* stream) {
+  REQUIRE(n_parts >= 1, "n_parts must be >= 1");
+  REQUIRE(rows >= 1 && heads >= 1, "rows and heads must be >= 1");
+  REQUIRE(dv >= 4 && dv <= 4096 && dv % 4 == 0, "dv must be a multiple of 4 in 4..4096");
+  REQUIRE(part_o && aligned16(part_o) && part_lse, "part_o (16-byte aligned) and part_lse are required");
+  REQUIRE(out && ((uintptr_t)out & 7) == 0, "out must be an 8-byte aligned device pointer");
+  REQUIRE(heads <= 65535, "heads must be <= 65535");
+  sfmla::CombineArgs c;
+  std::memset(&c, 0, sizeof c);
+  c.rows = rows;
+  c.heads = heads;
+  c.dv = dv;
+  c.n_parts = n_parts;
+  c.o_part_stride = (int64_t)rows * heads * dv;
+  c.o_row_stride = (int64_t)heads * dv;
+  c.lse_part_stride = (int64_t)rows * heads;
+  c.lse_row_stride = heads;
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.sinks = sinks;
+  c.out = (uint16_t*)out;
+  c.lse_out = lse_out;
+  hipError_t e = sfmla::launch_combine(c, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sfmla_status sfmla_debug_resolve(const sfmla_params* params, const sfmla_tensors* t,
+                                 const int32_t* metadata, size_t n_ints, int64_t* rows_out,
+                                 int32_t max_rows, int32_t* counts_out, void* stream) {
+  sfmla_status s = validate(params);
+  if (s != SFMLA_OK) return s;
+  sfmla::FwdArgs a;
+  s = fill_fwd_args(*params, t, metadata, n_ints, 1.0f, &a);
+  if (s != SFMLA_OK) return s;
+  REQUIRE(rows_out && counts_out && max_rows > 0, "rows_out, counts_out and max_rows > 0 required");
+  a.dbg_rows = rows_out;
+  a.dbg_counts = counts_out;
+  a.dbg_max_rows = max_rows;
+  hipError_t e = sfmla::launch_debug_resolve(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "resolve launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal definitions shared by the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "sfmla.h"
+
+namespace sfmla {
+
+constexpr int kTile = 32;          // KV rows staged in LDS per step
+constexpr int kSplitRows = 512;    // KV rows per split of one query row
+constexpr int kHeaderInts = 16;
+constexpr int kRecInts = 16;
+constexpr int32_t kMagic = 0x534d4c41;
+
+// Per-query-row plan record written by the planner (int32 each).
+enum RecField {
+  R_B = 0,       // batch index
+  R_I,           // index of the query row inside its batch
+  R_VALID,       // 1 if i < seqused_q (else the row attends to nothing)
+  R_P,           // original-KV position p = ori_len - q_used + i
+  R_PC,          // compressed-side position cmp_len*ratio + residual - q_used + i
+  R_ORI_LO,      // first row of the window rule
+  R_ORI_CNT,     // window row count, or TopK slot count
+  R_CMP_CNT,     // HCA visible count, or CSA slot count
+  R_ORI_BASE,    // physical row of logical position 0 (BSND / TND)
+  R_CMP_BASE,
+  R_ORI_LEN,
+  R_CMP_LEN,
+  R_NSPLIT,      // number of splits of this row's list
+  R_CHUNK,       // list positions per split
+  R_CMP_LIMIT,   // compressed rows [0, limit) are visible
+  R_NTOTAL       // list length (ori part + cmp part)
+};
+
+struct PlanArgs {
+  sfmla_params p;
+  sfmla_lengths len;
+  int32_t* meta;
+  uint32_t fingerprint;
+  int32_t max_splits;
+};
+
+struct FwdArgs {
+  int32_t qn, q_t, layout_kv, rope;
+  int32_t ori_bs, cmp_bs, ori_bt_cols, cmp_bt_cols;
+  int64_t ori_rows, cmp_rows;
+  int32_t ori_topk, cmp_topk, ori_mode, win_l, win_r, has_cmp;
+  int32_t max_splits, has_sinks;
+  uint32_t fingerprint;
+  float scale_log2;                 // softmax_scale * log2(e)
+  const int32_t* meta;
+  const uint16_t* q;
+  const char* ori_kv;   int64_t ori_stride;
+  const char* ori_rope; int64_t ori_rope_stride;
+  const char* ori_v;    int64_t ori_v_stride;
+  const char* cmp_kv;   int64_t cmp_stride;
+  const char* cmp_rope; int64_t cmp_rope_stride;
+  const int32_t* ori_bt;
+  const int32_t* cmp_bt;
+  const int32_t* ori_idx;
+  const int32_t* cmp_idx;
+  const float* sinks;
+  uint16_t* out;
+  float* lse;
+  int32_t* status;
+  float* ws_o;                      // [q_t][max_splits][qn][512]
+  float* ws_lse;                    // [q_t][max_splits][qn]
+  // debug resolve
+  int64_t* dbg_rows;
+  int32_t* dbg_counts;
+  int32_t dbg_max_rows;
+};
+
+struct CombineArgs {
+  int32_t rows, heads, dv;
+  int32_t n_parts;                  // fixed part count (exported merge) or 0
+  const int32_t* meta;              // per-row split counts (internal merge)
+  int64_t o_part_stride, o_row_stride;      // in floats
+  int64_t lse_part_stride, lse_row_stride;  // in floats
+  const float* part_o;
+  const float* part_lse;
+  const float* sinks;
+  uint16_t* out;
+  float* lse_out;
+};
+
+// Kernel launchers (defined in sfmla_kernels.hip).
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt,
+                          int groups, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_debug_resolve(const FwdArgs& a, hipStream_t s);
+size_t forward_lds_bytes(int dqk, int vmode, int fmt);
+
+}  // namespace sfmla

@@ -1,0 +1,168 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/sfmla.h declares, and rejects invalid parameters on the host before
+anything is launched (API page 约束说明 rules decidable from shapes)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+s = pytest.importorskip("sparse_shared_kv_amd")
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "sfmla.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:sfmla_status|const char\*)\s+(sfmla_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for need in ("sfmla_metadata", "sfmla_forward", "sfmla_combine", "sfmla_metadata_size",
+                 "sfmla_workspace_size", "sfmla_debug_resolve", "sfmla_last_error",
+                 "sfmla_version"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_shared_kv_amd", "libsfmla.so"))
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """Every field offset of the ctypes mirror equals the C compiler's."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "sfmla.h"', "int main(void){"]
+    for cname, cls in (("sfmla_params", s.Params), ("sfmla_lengths", s.Lengths),
+                       ("sfmla_tensors", s.Tensors)):
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in cls._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(ln.split() for ln in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                   check=True).stdout.splitlines())
+    for cname, cls in (("sfmla_params", s.Params), ("sfmla_lengths", s.Lengths),
+                       ("sfmla_tensors", s.Tensors)):
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got["%s.%s" % (cname, f)]) == getattr(cls, f).offset, (cname, f)
+
+
+def _params(**over):
+    P = synth.make_workload("swa_decode")
+    p = s.make_params(P.params, P.arrays)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+BAD = [
+    ("head_dim", 576, "head_dim"),
+    ("num_heads_kv", 2, "num_heads_kv"),
+    ("num_heads_q", 0, "num_heads_q"),
+    ("num_heads_q", 129, "num_heads_q"),
+    ("rope_head_dim", 32, "rope_head_dim"),
+    ("layout_kv", 1, "non-paged"),
+    ("q_t", 3, "q_t"),
+    ("ori_mask_mode", 2, "ori_mask_mode"),
+    ("ori_win_left", -2, "window"),
+    ("cmp_topk", 8, "cmp_topk"),
+    ("cmp_ratio", 4, "cmp_ratio"),
+    ("kv_dtype", 7, "kv_dtype"),
+    ("batch_size", 0, "batch_size"),
+]
+
+
+@pytest.mark.parametrize("field,value,msg", BAD, ids=[b[0] + "=" + str(b[1]) for b in BAD])
+def test_invalid_params_rejected_on_host(field, value, msg):
+    p = _params(**{field: value})
+    with pytest.raises(s.SfmlaError) as e:
+        s.sfmla_metadata_size(p)
+    assert e.value.status == 1 and msg in str(e.value)
+
+
+def test_paged_needs_block_table_and_seqused():
+    P = synth.make_workload("csa_decode_paged")
+    p = s.make_params(P.params, P.arrays)
+    p.has_seqused_ori_kv = 0
+    with pytest.raises(s.SfmlaError, match="seqused_ori_kv"):
+        s.sfmla_workspace_size(p)
+    p = s.make_params(P.params, P.arrays)
+    p.has_cmp_residual_kv = 0
+    with pytest.raises(s.SfmlaError, match="cmp_residual_kv"):
+        s.sfmla_workspace_size(p)
+
+
+def test_metadata_rejects_missing_lengths_without_launching():
+    P = synth.make_workload("hca_varlen")
+    p = s.make_params(P.params, P.arrays)
+    lens = s.Lengths()          # TND layouts need cu_seqlens: nothing given
+    with pytest.raises(s.SfmlaError, match="cu_seqlens_q"):
+        s._abi.check(s._abi.load().sfmla_metadata(ctypes.byref(p), ctypes.byref(lens),
+                                                   ctypes.c_void_p(16), 10 ** 6, None))
+
+
+def test_metadata_buffer_too_small():
+    p = _params()
+    lens = s.Lengths()
+    with pytest.raises(s.SfmlaError) as e:
+        s._abi.check(s._abi.load().sfmla_metadata(ctypes.byref(p), ctypes.byref(lens),
+                                                   ctypes.c_void_p(16), 4, None))
+    assert e.value.status == 3
+
+
+def test_forward_rejects_bad_tensors_without_launching():
+    p = _params()
+    t = s.Tensors()
+    lib = s._abi.load()
+    # no q pointer
+    st = lib.sfmla_forward(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(16), 10 ** 6,
+                           ctypes.c_float(0.1), None, 0, None)
+    assert st == 1 and b"q must be" in lib.sfmla_last_error()
+    t.q = 4096
+    t.ori_kv = 4096
+    t.ori_kv_stride = 1000          # shorter than a 512-value bf16 row
+    st = lib.sfmla_forward(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(16), 10 ** 6,
+                           ctypes.c_float(0.1), None, 0, None)
+    assert st == 1 and b"ori_kv_stride" in lib.sfmla_last_error()
+    t.ori_kv_stride = 1024
+    t.attention_out = 4096
+    t.softmax_lse = 8192
+    st = lib.sfmla_forward(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(16), 10 ** 6,
+                           ctypes.c_float(float("inf")), None, 0, None)
+    assert st == 1 and b"finite" in lib.sfmla_last_error()
+
+
+def test_workspace_sizes():
+    for name, expect_split in [("swa_decode", False), ("csa_decode_paged", True),
+                               ("sfa_mla_rope", True)]:
+        P = synth.make_workload(name) if name != "sfa_mla_rope" else _small_sfa()
+        p = s.make_params(P.params, P.arrays)
+        ws = s.sfmla_workspace_size(p)
+        assert (ws > 0) == expect_split, name
+
+
+def _small_sfa():
+    from synth.workloads import sfa_mla_rope
+    return sfa_mla_rope(batch=2, q_s=2, kv_len=4096, topk=2048)
+
+
+def test_combine_rejects_bad_dv():
+    lib = s._abi.load()
+    st = lib.sfmla_combine(2, 4, 8, 6, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
+                           ctypes.c_void_p(4096), None, None)
+    assert st == 1 and b"dv" in lib.sfmla_last_error()
