@@ -19,7 +19,7 @@
  *
  * Call pattern (sparse_flash_mla API page, 功能说明 typical flow): build the
  * split plan with sfmla_metadata() from the same parameters, then call
- * sfmla_forward() with that plan.  A plan built from other parameters is
+ * sfmla_forward() and sfmla_combine() with that plan.  A plan built from other parameters is
  * rejected on the device (outputs become NaN and *status is set), because the
  * host never reads device memory.
  *
@@ -205,18 +205,33 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
 sfmla_status sfmla_workspace_size(const sfmla_params* params, size_t* bytes);
 
 /*
- * Attention forward (sparse_flash_mla on the API page): writes attention_out
- * and, if requested, softmax_lse.  softmax_scale must be finite.  `workspace`
- * holds at least sfmla_workspace_size() bytes (may be NULL when that is 0).
+ * Attention forward (sparse_flash_mla on the API page).  Query rows whose
+ * plan has one split get their final attention_out (and softmax_lse); rows
+ * the plan splits (lists longer than one split) leave per-split partials in
+ * `workspace`, which sfmla_combine() merges.  softmax_scale must be finite.
+ * `workspace` holds at least sfmla_workspace_size() bytes, 256-byte aligned
+ * (may be NULL when that size is 0).
  */
 sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* tensors,
                            const int32_t* metadata, size_t n_ints, float softmax_scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * LSE merge of partial results over disjoint parts of each row set (the
- * split-KV merge; kv_quant_sparse_flash_attention blog, usage notes: the
- * max / sum outputs serve the DCP merge).  For r in [0, rows), h in [0, heads):
+ * Split-KV merge (the FLASH_DECODE split of the kv_quant_sparse_flash_attention
+ * blog's kernel structure): for every query row the plan splits, LSE-merge
+ * its partials from `workspace` into attention_out / softmax_lse, adding the
+ * sink once:  O = sum_k e^{lse_k} O_k / (sum_k e^{lse_k} + e^{sink}),
+ * LSE = log sum_k e^{lse_k}.  Call it after sfmla_forward() with the same
+ * arguments; it launches nothing when no row can be split.
+ */
+sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* tensors,
+                           const int32_t* metadata, size_t n_ints, const void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Generic LSE merge of partial results over disjoint parts of each row set
+ * (kv_quant_sparse_flash_attention blog, usage notes: the max / sum outputs
+ * serve the merge of KV-sharded (DCP) partial results).  For r in [0, rows), h in [0, heads):
  *   part_o[(k*rows + r)*heads + h][0..dv)  fp32, part k's output normalised
  *                                           without the sink
  *   part_lse[(k*rows + r)*heads + h]        fp32, part k's LSE (-inf = empty)
@@ -224,9 +239,9 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* tens
  *   lse_out fp32 (rows, heads) = log sum_k e^{lse_k}  (may be NULL)
  * sinks (heads) may be NULL (no sink).  dv must be a multiple of 4, <= 4096.
  */
-sfmla_status sfmla_combine(int32_t n_parts, int32_t rows, int32_t heads, int32_t dv,
-                           const float* part_o, const float* part_lse, const float* sinks,
-                           void* out, float* lse_out, void* stream);
+sfmla_status sfmla_merge_partials(int32_t n_parts, int32_t rows, int32_t heads, int32_t dv,
+                                  const float* part_o, const float* part_lse, const float* sinks,
+                                  void* out, float* lse_out, void* stream);
 
 /*
  * Debug view of the resolver: writes each query row's resolved physical rows

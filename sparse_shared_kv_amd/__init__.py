@@ -21,7 +21,7 @@ from . import _abi
 from ._abi import KV_DTYPES, LAYOUTS, Lengths, Params, SfmlaError, Tensors
 
 __all__ = ["sfmla_metadata_size", "sfmla_metadata", "sfmla_workspace_size", "sfmla_forward",
-           "sfmla_combine", "sfmla_debug_resolve", "sfmla_version", "Params", "Lengths",
+           "sfmla_combine", "sfmla_merge_partials", "sfmla_debug_resolve", "sfmla_version", "Params", "Lengths",
            "Tensors", "SfmlaError", "Call", "make_params", "CMP_BIT"]
 
 CMP_BIT = 1 << 62
@@ -72,12 +72,20 @@ def sfmla_forward(params: Params, tensors: Tensors, metadata: torch.Tensor, soft
                                     _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def sfmla_combine(part_o: torch.Tensor, part_lse: torch.Tensor, sinks, out: torch.Tensor,
-                  lse_out=None, stream=None):
+def sfmla_combine(params: Params, tensors: Tensors, metadata: torch.Tensor,
+                  workspace: torch.Tensor | None = None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _abi.check(_lib().sfmla_combine(ctypes.byref(params), ctypes.byref(tensors), _ptr(metadata),
+                                    metadata.numel(), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sfmla_merge_partials(part_o: torch.Tensor, part_lse: torch.Tensor, sinks, out: torch.Tensor,
+                         lse_out=None, stream=None):
     """part_o fp32 (n_parts, rows, heads, dv), part_lse fp32 (n_parts, rows, heads)."""
     n_parts, rows, heads, dv = part_o.shape
-    _abi.check(_lib().sfmla_combine(n_parts, rows, heads, dv, _ptr(part_o), _ptr(part_lse),
-                                    _ptr(sinks), _ptr(out), _ptr(lse_out), _stream(stream)))
+    _abi.check(_lib().sfmla_merge_partials(n_parts, rows, heads, dv, _ptr(part_o),
+                                           _ptr(part_lse), _ptr(sinks), _ptr(out),
+                                           _ptr(lse_out), _stream(stream)))
 
 
 def sfmla_debug_resolve(params: Params, tensors: Tensors, metadata: torch.Tensor,
@@ -213,9 +221,14 @@ class Call:
     def forward(self, stream=None):
         sfmla_forward(self.params, self.tensors, self.metadata, self.scale, self.workspace, stream)
 
+    def combine(self, stream=None):
+        sfmla_combine(self.params, self.tensors, self.metadata, self.workspace, stream)
+
     def run(self, stream=None):
+        """One pass of the whole path: plan, forward, split merge."""
         self.plan(stream)
         self.forward(stream)
+        self.combine(stream)
         return self.out, self.lse
 
     def resolve(self, max_rows, stream=None):

@@ -348,31 +348,47 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
   const int vmode = p.has_separate_v ? 1 : 0;
   hipError_t e = sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
-  if (a.max_splits > 1) {
-    sfmla::CombineArgs c;
-    std::memset(&c, 0, sizeof c);
-    c.rows = p.q_t;
-    c.heads = p.num_heads_q;
-    c.dv = 512;
-    c.meta = metadata;
-    c.o_part_stride = (int64_t)p.num_heads_q * 512;
-    c.o_row_stride = (int64_t)a.max_splits * p.num_heads_q * 512;
-    c.lse_part_stride = p.num_heads_q;
-    c.lse_row_stride = (int64_t)a.max_splits * p.num_heads_q;
-    c.part_o = a.ws_o;
-    c.part_lse = a.ws_lse;
-    c.sinks = t->sinks;
-    c.out = a.out;
-    c.lse_out = a.lse;
-    e = sfmla::launch_combine(c, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
-  }
   return ok();
 }
 
-sfmla_status sfmla_combine(int32_t n_parts, int32_t rows, int32_t heads, int32_t dv,
-                           const float* part_o, const float* part_lse, const float* sinks,
-                           void* out, float* lse_out, void* stream) {
+sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* t,
+                           const int32_t* metadata, size_t n_ints, const void* workspace,
+                           size_t ws_bytes, void* stream) {
+  sfmla_status s = validate(params);
+  if (s != SFMLA_OK) return s;
+  const sfmla_params& p = *params;
+  sfmla::FwdArgs a;
+  s = fill_fwd_args(p, t, metadata, n_ints, 1.0f, &a);
+  if (s != SFMLA_OK) return s;
+  if (a.max_splits <= 1) return ok();
+  const size_t need = workspace_bytes(p);
+  if (!workspace || ws_bytes < need)
+    return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
+  REQUIRE(((uintptr_t)workspace & 255) == 0, "workspace must be 256-byte aligned");
+  const size_t slots = (size_t)p.q_t * a.max_splits * p.num_heads_q;
+  sfmla::CombineArgs c;
+  std::memset(&c, 0, sizeof c);
+  c.rows = p.q_t;
+  c.heads = p.num_heads_q;
+  c.dv = 512;
+  c.meta = metadata;
+  c.o_part_stride = (int64_t)p.num_heads_q * 512;
+  c.o_row_stride = (int64_t)a.max_splits * p.num_heads_q * 512;
+  c.lse_part_stride = p.num_heads_q;
+  c.lse_row_stride = (int64_t)a.max_splits * p.num_heads_q;
+  c.part_o = (const float*)workspace;
+  c.part_lse = (const float*)((const char*)workspace + slots * 512 * sizeof(float));
+  c.sinks = t->sinks;
+  c.out = a.out;
+  c.lse_out = a.lse;
+  hipError_t e = sfmla::launch_combine(c, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sfmla_status sfmla_merge_partials(int32_t n_parts, int32_t rows, int32_t heads, int32_t dv,
+                                  const float* part_o, const float* part_lse, const float* sinks,
+                                  void* out, float* lse_out, void* stream) {
   REQUIRE(n_parts >= 1, "n_parts must be >= 1");
   REQUIRE(rows >= 1 && heads >= 1, "rows and heads must be >= 1");
   REQUIRE(dv >= 4 && dv <= 4096 && dv % 4 == 0, "dv must be a multiple of 4 in 4..4096");

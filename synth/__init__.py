@@ -18,6 +18,6 @@ Index ranges in the recipes are written with each workload's own numbers
 """
 
 from .problem import Problem, bf16_bits
-from .workloads import WORKLOADS, make_workload, random_tiny
+from .workloads import WORKLOADS, index_replicas, make_workload, random_tiny
 
-__all__ = ["Problem", "bf16_bits", "WORKLOADS", "make_workload", "random_tiny"]
+__all__ = ["Problem", "bf16_bits", "WORKLOADS", "index_replicas", "make_workload", "random_tiny"]

@@ -88,6 +88,12 @@ def swa_decode(seed=1):
                    "q, ori_kv ~ N(0,1) bf16; query at position 511")
 
 
+def _csa_indices(seq, B, C, K):
+    g_idx = _gen(seq)
+    idx = np.stack([g_idx.choice(C, K, replace=False) for _ in range(B)]).astype(np.int32)
+    return idx.reshape(B, 1, K)
+
+
 def csa_decode_paged(seed=2):
     """CSA decode, paged: B=4, q_n=64, d=512; context 32768, window 128;
     cmp_ratio 4 so 8192 compressed rows; TopK 512 drawn without replacement
@@ -99,8 +105,7 @@ def csa_decode_paged(seed=2):
     ori_bt = g_tab.permutation(B * L // bs).astype(np.int32).reshape(B, L // bs)
     cmp_blocks = B * L // bs // 4              # pool of 256 blocks
     cmp_bt = g_tab.permutation(cmp_blocks).astype(np.int32).reshape(B, cmp_blocks // B)
-    g_idx = _gen(s_idx)
-    idx = np.stack([g_idx.choice(C, K, replace=False) for _ in range(B)]).astype(np.int32)
+    idx = _csa_indices(s_idx, B, C, K)
     arrays = dict(
         q=normal_bf16(s_q, (B, qn, d)),
         ori_kv=banked_rows(s_ori, B * L, lambda s, n: normal_bf16(s, (n, d))),
@@ -109,7 +114,7 @@ def csa_decode_paged(seed=2):
         seqused_ori_kv=np.full(B, L, np.int32),
         seqused_cmp_kv=np.full(B, C, np.int32),
         cmp_residual_kv=np.zeros(B, np.int32),
-        cmp_sparse_indices=idx.reshape(B, 1, K),
+        cmp_sparse_indices=idx,
         sinks=_gen(s_sink).standard_normal(qn, dtype=np.float32),
     )
     params = _base_params(
@@ -154,6 +159,17 @@ def hca_varlen(seed=3):
                    "contexts %s" % L.tolist())
 
 
+def _sfa_indices(seq, batch, q_s, kv_len, topk):
+    g_idx = _gen(seq)
+    rows = []
+    for _b in range(batch):
+        for s in range(q_s):
+            # query s of a q_s-token step sits at position kv_len - q_s + s,
+            # so positions 0 .. kv_len - q_s + s are its causal range
+            rows.append(g_idx.choice(kv_len - q_s + s + 1, topk, replace=False))
+    return np.stack(rows).astype(np.int32).reshape(batch * q_s, 1, topk)
+
+
 def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64):
     """Token-wise sparse MLA-absorb with rope: B=32, q_s=2, q_n=128, Q_D=576,
     separate K (576) and V (512) bf16 pools, PA block 64, kv length 65536,
@@ -163,14 +179,7 @@ def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64):
     nblk = batch * kv_len // bs
     g_tab = _gen(s_tab)
     bt = g_tab.permutation(nblk).astype(np.int32).reshape(batch, kv_len // bs)
-    g_idx = _gen(s_idx)
-    rows = []
-    for _b in range(batch):
-        for s in range(q_s):
-            # query s of a q_s-token step sits at position kv_len - q_s + s,
-            # so positions 0 .. kv_len - q_s + s are its causal range
-            rows.append(g_idx.choice(kv_len - q_s + s + 1, topk, replace=False))
-    idx = np.stack(rows).astype(np.int32).reshape(batch * q_s, 1, topk)
+    idx = _sfa_indices(s_idx, batch, q_s, kv_len, topk)
     arrays = dict(
         q=normal_bf16(s_q, (batch * q_s, qn, dq)),
         ori_kv=banked_rows(s_k, nblk * bs, lambda s, n: normal_bf16(s, (n, dq))),
@@ -189,6 +198,12 @@ def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64):
                    "q, K, V ~ N(0,1) bf16; %d of the causal positions" % topk)
 
 
+def _c8_indices(seq, L, topk):
+    g_idx = _gen(seq)
+    idx = np.stack([g_idx.choice(int(n), topk, replace=False) for n in L]).astype(np.int32)
+    return idx.reshape(len(L), 1, topk)
+
+
 def c8_packed(seed=5, fmt="int8", topk=2048):
     """Quantised packed KV: the HCA-varlen shapes (TND, B=8, q_n=128, the same
     context lengths) with Q_D=576 and 656-byte packed rows (512 INT8 or
@@ -197,14 +212,13 @@ def c8_packed(seed=5, fmt="int8", topk=2048):
     s_q, s_kv, s_idx = _seqs(seed, 3)
     B, qn, dq = 8, 128, 576
     L = _varlen_lengths(3)
-    g_idx = _gen(s_idx)
-    idx = np.stack([g_idx.choice(int(n), topk, replace=False) for n in L]).astype(np.int32)
+    idx = _c8_indices(s_idx, L, topk)
     arrays = dict(
         q=normal_bf16(s_q, (B, qn, dq), std=0.5),
         ori_kv=banked_rows(s_kv, int(L.sum()), lambda s, n: packed_rows(s, n, 64, fmt)),
         cu_seqlens_q=np.arange(B + 1, dtype=np.int32),
         cu_seqlens_ori_kv=_prefix(L),
-        ori_sparse_indices=idx.reshape(B, 1, topk),
+        ori_sparse_indices=idx,
     )
     params = _base_params(
         num_heads_q=qn, rope_head_dim=64, batch_size=B, layout_q="TND",
@@ -230,6 +244,29 @@ WORKLOADS = {
 def make_workload(name, seed=None, **kw):
     fn = WORKLOADS[name]
     return fn(**kw) if seed is None else fn(seed=seed, **kw)
+
+
+def index_replicas(P: Problem, n: int):
+    """n further TopK index sets drawn by the workload's own index recipe
+    (fresh child streams), for rotating through distinct row sets between
+    timed calls.  Returns a list of (array name, array)."""
+    out = []
+    for r in range(n):
+        seq = np.random.SeedSequence([P.seed, 7919, r])
+        if P.name == "sfa_mla_rope":
+            p = P.params
+            out.append(("ori_sparse_indices", _sfa_indices(
+                seq, p["batch_size"], p["q_s"], p["max_seqlen_ori_kv"], p["ori_topk"])))
+        elif P.name.startswith("c8_packed"):
+            cu = P.arrays["cu_seqlens_ori_kv"]
+            out.append(("ori_sparse_indices", _c8_indices(seq, np.diff(cu), P.params["ori_topk"])))
+        elif P.name == "csa_decode_paged":
+            p = P.params
+            out.append(("cmp_sparse_indices", _csa_indices(
+                seq, p["batch_size"], p["max_seqlen_cmp_kv"], p["cmp_topk"])))
+        else:
+            return []
+    return out
 
 
 # ---------------------------------------------------------------------------

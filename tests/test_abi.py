@@ -23,7 +23,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for need in ("sfmla_metadata", "sfmla_forward", "sfmla_combine", "sfmla_metadata_size",
+    for need in ("sfmla_metadata", "sfmla_forward", "sfmla_combine", "sfmla_merge_partials",
+                 "sfmla_metadata_size",
                  "sfmla_workspace_size", "sfmla_debug_resolve", "sfmla_last_error",
                  "sfmla_version"):
         assert need in names
@@ -163,6 +164,6 @@ def _small_sfa():
 
 def test_combine_rejects_bad_dv():
     lib = s._abi.load()
-    st = lib.sfmla_combine(2, 4, 8, 6, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
+    st = lib.sfmla_merge_partials(2, 4, 8, 6, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
                            ctypes.c_void_p(4096), None, None)
     assert st == 1 and b"dv" in lib.sfmla_last_error()

@@ -159,12 +159,13 @@ def test_metadata_from_other_params_is_rejected():
     call.metadata.copy_(call_b.metadata)       # plan of different parameters
     call.status.zero_()
     call.forward()
+    call.combine()
     torch.cuda.synchronize()
     assert torch.isnan(call.out.float()).all()
     assert int(call.status.item()) & 1
 
 
-def test_combine_entry_point_matches_oracle_merge():
+def test_merge_partials_entry_point_matches_oracle_merge():
     import sparse_shared_kv_amd as s
     g = np.random.default_rng(3)
     n_parts, rows, heads, dv = 5, 7, 12, 512
@@ -176,8 +177,8 @@ def test_combine_entry_point_matches_oracle_merge():
     dev = torch.device("cuda")
     out = torch.empty((rows, heads, dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((rows, heads), dtype=torch.float32, device=dev)
-    s.sfmla_combine(torch.from_numpy(part_o).to(dev), torch.from_numpy(part_lse).to(dev),
-                    torch.from_numpy(sinks).to(dev), out, lse)
+    s.sfmla_merge_partials(torch.from_numpy(part_o).to(dev), torch.from_numpy(part_lse).to(dev),
+                           torch.from_numpy(sinks).to(dev), out, lse)
     torch.cuda.synchronize()
     for r in range(rows):
         O, L = oracle.combine(part_o[:, r], part_lse[:, r], sinks)
