@@ -63,6 +63,7 @@ typedef enum sfmla_status {
 /* device status word bits (sfmla_tensors.status) */
 #define SFMLA_STATUS_METADATA_MISMATCH 1
 #define SFMLA_STATUS_ROW_OUT_OF_RANGE 2
+#define SFMLA_STATUS_LIST_TOO_LONG 4   /* a row's list exceeds what max_seqlen_* / topk allow */
 
 /* layouts (API page 参数说明 layout_q / layout_kv; PA_BBND, PA_ND and PA_BSND
  * on the different pages name the same paged layout) */

@@ -11,7 +11,7 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsfmla.so")
+LIB_PATH = os.environ.get("SFMLA_LIB") or os.path.join(HERE, "libsfmla.so")
 
 LAYOUTS = {"BSND": 0, "TND": 1, "PA_BSND": 2, "PA_BBND": 2, "PA_ND": 2}
 KV_DTYPES = {"bf16": 0, "int8_packed": 1, "fp8_e4m3_packed": 2}

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -156,14 +157,34 @@ size_t workspace_bytes(const sfmla_params& p) {
   return slots * 512 * sizeof(float) + ((slots * sizeof(float) + 255) / 256) * 256;
 }
 
-// Waves per workgroup (16 heads each) and head groups: as many heads per
-// workgroup as possible while the grid still has about one workgroup per CU.
-void choose_groups(const sfmla_params& p, int* nw, int* groups) {
+// Workgroup shape: nw waves of 16 heads each (hb = 1 block per wave), in
+// `groups` head groups.  All heads of a query row share one workgroup (the
+// KV rows are gathered once) unless the grid would have fewer than about one
+// workgroup per CU; then the heads are spread over more, smaller workgroups.
+void choose_groups(const sfmla_params& p, int* nw, int* hb, int* groups) {
   const int64_t units = (int64_t)p.q_t * max_splits(p);
-  int w = std::min(8, (p.num_heads_q + 15) / 16);
-  while (w > 1 && units * ((p.num_heads_q + 16 * w - 1) / (16 * w)) < 256) w /= 2;
+  const int blocks = (p.num_heads_q + 15) / 16;        // 16-head blocks
+  const bool bf16 = p.kv_dtype == SFMLA_KV_BF16;
+  // SFMLA_SHAPE="waves,blocks_per_wave" overrides the shape (tuning aid)
+  if (const char* env = getenv("SFMLA_SHAPE")) {
+    int w = 0, b = 0;
+    if (sscanf(env, "%d,%d", &w, &b) == 2 && b == 1 &&
+        (w == 1 || w == 2 || w == 4 || w == 8)) {
+      *nw = w;
+      *hb = b;
+      *groups = (blocks + w * b - 1) / (w * b);
+      return;
+    }
+  }
+  int b = 1;
+  const int wmax = 8;
+  int per = std::min(wmax * b, blocks);                // blocks per workgroup
+  while (per > 1 && units * ((blocks + per - 1) / per) < 256) per = (per + 1) / 2;
+  if (per == 1) b = 1;
+  const int w = (per + b - 1) / b;
+  *hb = b;
   *nw = w;
-  *groups = (p.num_heads_q + 16 * w - 1) / (16 * w);
+  *groups = (blocks + w * b - 1) / (w * b);
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
@@ -342,11 +363,12 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
     a.ws_o = (float*)workspace;
     a.ws_lse = (float*)((char*)workspace + slots * 512 * sizeof(float));
   }
-  int nw, groups;
-  choose_groups(p, &nw, &groups);
+  int nw, hb, groups;
+  choose_groups(p, &nw, &hb, &groups);
   const int dqk = 512 + p.rope_head_dim;
   const int vmode = p.has_separate_v ? 1 : 0;
-  hipError_t e = sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream);
+  hipError_t e =
+      sfmla::launch_forward(a, nw, hb, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -48,6 +48,7 @@ struct FwdArgs {
   int64_t ori_rows, cmp_rows;
   int32_t ori_topk, cmp_topk, ori_mode, win_l, win_r, has_cmp;
   int32_t max_splits, has_sinks;
+  int32_t groups;                   // head groups of the launch
   uint32_t fingerprint;
   float scale_log2;                 // softmax_scale * log2(e)
   const int32_t* meta;
@@ -88,7 +89,7 @@ struct CombineArgs {
 
 // Kernel launchers (defined in sfmla_kernels.hip).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt,
+hipError_t launch_forward(const FwdArgs& a, int nw, int hb, int dqk, int vmode, int fmt,
                           int groups, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_debug_resolve(const FwdArgs& a, hipStream_t s);

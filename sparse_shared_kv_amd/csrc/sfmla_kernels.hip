@@ -499,6 +499,439 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// forward, bf16 KV: pipelined gather with direct global -> LDS loads
+// ---------------------------------------------------------------------------
+//
+// The split's list positions are resolved once into LDS.  KV tiles of 32 rows
+// are then double-buffered: while tile t is multiplied, tile t+1 streams in
+// through global_load_lds_dwordx4 (each wave instruction moves 1 KB straight
+// into LDS, lane i landing at byte 16*i of the destination).  Every stage
+// lives in its own LDS array so that the compiler can tell the in-flight
+// loads apart from the reads of the other stage and keeps the explicit
+// partial vmcnt waits; the block barrier is a bare s_barrier for the same
+// reason.  Empty / masked slots load a zero row so no stale LDS bytes (which
+// could hold NaN patterns) ever meet a zero probability.
+
+__device__ __align__(16) const uint4 g_zero_row[72] = {};
+
+// Wait until at most N vector-memory ops of this wave are outstanding (the
+// counter has 6 bits: larger N waits for slightly more than needed).
+template <int N0>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int N = N0 > 63 ? 63 : N0;
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One global_load_lds_dwordx4: every lane moves 16 bytes from `g` to LDS at
+// lds_wave_base + 16 * lane.  Issued through inline asm so that the
+// compiler's wait insertion neither tracks these loads (it cannot tell the
+// in-flight stage apart from the stage being read and would wait for all of
+// them) nor reorders LDS reads across them ("memory" clobber).  Every wait on
+// this data is explicit (wait_vmcnt + block_barrier).  Untracked vector-memory
+// ops only make the compiler's own in-order vmcnt waits stricter, never
+// insufficient.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// After an explicit full vmcnt wait: make an empty asm the last writer of
+// the loaded registers, so the compiler's wait tracking cannot attribute a
+// pending memory load to them inside the tile loop.
+template <int A, int B>
+__device__ __forceinline__ void settle(bf16x8 (&r)[A][B]) {
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int j = 0; j < B; ++j) asm volatile("" : "+v"(r[i][j]));
+}
+
+// LDS byte address of a __shared__ object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)p;
+}
+
+template <int NW, int DQK, int VMODE>
+struct Pipe {
+  static constexpr int T = kTile;
+  static constexpr int RSTR = 1024 + 32;      // LDS row stride: conflict-free K and V^T reads
+  static constexpr bool ROPE = DQK == 576;
+  static constexpr int NR = T / NW;           // rows each wave gathers per tile
+  static constexpr int ROPE_INSTR = ROPE ? (NR >= 8 ? NR / 8 : 1) : 0;
+  static constexpr int NK = NR + ROPE_INSTR;  // K-side loads per wave per tile
+  static constexpr int NV = VMODE ? NR : 0;   // V-side loads per wave per tile
+  static constexpr int KBYTES = T * RSTR + (ROPE ? T * 128 : 0);
+};
+
+// K side of one tile: 512 nope values per row (1 KB per wave instruction) and,
+// with rope, 8 rows of 64 rope values per instruction (row r's 16-byte chunk c
+// lands at position c ^ ((r >> 1) & 7) of its 128-byte LDS row, which keeps
+// the 16-row reads conflict-free).
+template <int NW, int DQK, int VMODE>
+__device__ __forceinline__ void issue_k(const uint64_t* sAK, const uint64_t* sAR, int tbase,
+                                        uint32_t ldsK, int w, int l) {
+  using C = Pipe<NW, DQK, VMODE>;
+  const uint32_t wk = __builtin_amdgcn_readfirstlane(ldsK + w * C::NR * C::RSTR);
+#pragma unroll
+  for (int j = 0; j < C::NR; ++j) {
+    const int r = w * C::NR + j;
+    dma16((const char*)sAK[tbase + r] + l * 16, wk + j * C::RSTR);
+  }
+  if constexpr (C::ROPE) {
+    const uint32_t wr = __builtin_amdgcn_readfirstlane(ldsK + kTile * C::RSTR + w * C::NR * 128);
+#pragma unroll
+    for (int q = 0; q < C::ROPE_INSTR; ++q) {
+      const int rr = w * C::NR + 8 * q + (l >> 3);
+      if (C::NR >= 8 || (l >> 3) < C::NR) {
+        const int chunk = (l & 7) ^ ((rr >> 1) & 7);
+        dma16((const char*)sAR[tbase + rr] + chunk * 16, wr + q * 1024);
+      }
+    }
+  }
+}
+
+template <int NW, int DQK, int VMODE>
+__device__ __forceinline__ void issue_v(const uint64_t* sAV, int tbase, uint32_t ldsV, int w,
+                                        int l) {
+  using C = Pipe<NW, DQK, VMODE>;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(ldsV + w * C::NR * C::RSTR);
+#pragma unroll
+  for (int j = 0; j < C::NR; ++j) {
+    const int r = w * C::NR + j;
+    dma16((const char*)sAV[tbase + r] + l * 16, wv + j * C::RSTR);
+  }
+}
+
+// Running-max growth (log2 units) below which the accumulators are not
+// rescaled: probabilities then stay below 2^8 and the normaliser uses the
+// same (stale) max, so the result is unchanged while the accumulators are
+// touched only when the max jumps.
+constexpr float kRescaleThreshold = 8.0f;
+
+// HB head blocks of 16 heads per wave.
+template <int NW, int HB, int DQK, int VMODE>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+  using C = Pipe<NW, DQK, VMODE>;
+  constexpr int T = C::T;
+  constexpr int NKS = DQK / 32;
+  constexpr int NTHR = NW * 64;
+  constexpr int HPW = 16 * HB;                     // heads per wave
+  constexpr int RS = C::RSTR;
+  // separate V: two K stages and two V stages; aliased V: three K stages
+  __shared__ __align__(16) char sK0[C::KBYTES];
+  __shared__ __align__(16) char sK1[C::KBYTES];
+  __shared__ __align__(16) char sK2[VMODE ? 16 : C::KBYTES];
+  __shared__ __align__(16) char sV0[VMODE ? T * RS : 16];
+  __shared__ __align__(16) char sV1[VMODE ? T * RS : 16];
+  __shared__ uint64_t sAK[kSplitRows + T];
+  __shared__ uint64_t sAR[C::ROPE ? kSplitRows + T : 1];
+  __shared__ uint64_t sAV[VMODE ? kSplitRows + T : 1];
+  __shared__ uint8_t sValid[kSplitRows + T];
+
+  // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so ids
+  // 8G*q + 8*hg + r (r < 8) put every head group of unit 8q + r on one XCD,
+  // dispatched together: the second gather of a row hits that XCD's L2.
+  const int G = a.groups;
+  const int bid = blockIdx.x;
+  const int unit = (bid / (8 * G)) * 8 + (bid & 7);
+  const int hg = (bid / 8) % G;
+  if (unit >= a.q_t * a.max_splits) return;
+  const int row = unit / a.max_splits, split = unit - row * a.max_splits;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, t = l & 15;
+  const int h0 = (hg * NW + w) * HPW;              // first head of this wave
+  const bool wave_on = h0 < a.qn;
+
+  if (!plan_matches(a)) {
+    if (split == 0) {
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const int h = h0 + 16 * hb + t;
+        if (h >= a.qn) continue;
+        uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
+        for (int c = g; c < 512; c += 4) op[c] = f2bf(nan);
+        if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = nan;
+      }
+      if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_METADATA_MISMATCH);
+    }
+    return;
+  }
+  const int32_t* rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
+  const int nsplit = rec[R_NSPLIT];
+  if (split >= nsplit) return;
+  const int n = rec[R_NTOTAL];
+  const int chunk = rec[R_CHUNK];
+  if (chunk > kSplitRows) {
+    // a list longer than the parameters' maxima allow: refuse the row
+    if (split == 0) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const int h = h0 + 16 * hb + t;
+        if (h >= a.qn) continue;
+        uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
+        for (int c = g; c < 512; c += 4) op[c] = f2bf(__builtin_nanf(""));
+        if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = __builtin_nanf("");
+      }
+      if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_LIST_TOO_LONG);
+    }
+    return;
+  }
+  const int k0 = split * chunk;
+  const int k1 = min(n, k0 + chunk);
+  const int nt = (k1 - k0 + T - 1) / T;
+
+  // ---- resolve every list position of this split once, into row addresses
+  //      (empty or masked slots read a zero row)
+  {
+    const char* zero = (const char*)g_zero_row;
+    for (int i = tid; i < nt * T; i += NTHR) {
+      const int k = k0 + i;
+      int side = 0;
+      int64_t phys = -1;
+      if (k < k1) phys = resolve_pos(a, rec, row, k, &side);
+      const char* ka = zero;
+      const char* va = zero;
+      const char* ra = zero;
+      if (phys >= 0) {
+        ka = side ? a.cmp_kv + phys * a.cmp_stride : a.ori_kv + phys * a.ori_stride;
+        va = (side || !a.ori_v) ? ka : a.ori_v + phys * a.ori_v_stride;
+        const char* rp = side ? a.cmp_rope : a.ori_rope;
+        ra = rp ? rp + phys * (side ? a.cmp_rope_stride : a.ori_rope_stride) : ka + 1024;
+      }
+      sAK[i] = (uint64_t)ka;
+      if constexpr (C::ROPE) sAR[i] = (uint64_t)ra;
+      if constexpr (VMODE) sAV[i] = (uint64_t)va;
+      sValid[i] = phys >= 0;
+    }
+  }
+  // Q slices (B operand: k = d, n = head), loaded before the first gathers so
+  // that waiting for them never waits for KV tiles
+  bf16x8 qreg[HB][NKS];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = h0 + 16 * hb + t;
+    const bool on = h < a.qn;
+    const uint16_t* qp = a.q + ((int64_t)row * a.qn + (on ? h : 0)) * DQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 v = on ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+      qreg[hb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  wait_lgkm0();
+  block_barrier();
+
+  f32x4 o[HB][32];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) o[hb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[HB], l_run[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) { m_run[hb] = kNegInf; l_run[hb] = 0.f; }
+  bf16x8 pb[HB];
+
+  // ---- S^T = K Q^T, online softmax -> pb (M = 16 rows, N = 16 heads per MFMA).
+  // The operands of the next PF k-steps are in flight while step ks
+  // multiplies; sched_barrier fences pin that order.
+  auto qk_softmax = [&](const char* sK, int tbase) {
+    const char* sR = sK + T * RS;
+    bool valid[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      valid[i] = sValid[tbase + 4 * g + i];
+      valid[4 + i] = sValid[tbase + 16 + 4 * g + i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s[HB][2];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* kp0 = sK + t * RS + 16 * g;
+    const char* kp1 = kp0 + 16 * RS;
+    auto kload = [&](int ks, bf16x8& k0v, bf16x8& k1v) {
+      if (!C::ROPE || ks < 16) {
+        k0v = *(const bf16x8*)(kp0 + 64 * ks);
+        k1v = *(const bf16x8*)(kp1 + 64 * ks);
+      } else {
+        const int c = 4 * (ks - 16) + g;
+        k0v = *(const bf16x8*)(sR + t * 128 + 16 * (c ^ ((t >> 1) & 7)));
+        k1v = *(const bf16x8*)(sR + (16 + t) * 128 + 16 * (c ^ (((16 + t) >> 1) & 7)));
+      }
+    };
+    constexpr int PF = NW * HB >= 8 ? (C::ROPE ? 1 : 2) : 4;   // 2 waves/SIMD: fewer registers
+    bf16x8 kb[PF][2];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kload(i, kb[i][0], kb[i][1]);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 k0v = kb[ks % PF][0], k1v = kb[ks % PF][1];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qreg[hb][ks], s[hb][0], 0, 0, 0);
+        s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qreg[hb][ks], s[hb][1], 0, 0, 0);
+      }
+      if (ks + PF < NKS) kload(ks + PF, kb[ks % PF][0], kb[ks % PF][1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // lane holds head t of each block and rows {4g+i, 16+4g+i}
+    bool any_grow = false;
+    float alpha[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      float x[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = valid[j] ? s[hb][j >> 2][j & 3] * a.scale_log2 : kNegInf;
+        x[j] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool grow = mx > m_run[hb] + kRescaleThreshold;
+      alpha[hb] = grow ? __builtin_amdgcn_exp2f(m_run[hb] - mx) : 1.f;
+      if (grow) m_run[hb] = mx;
+      any_grow |= grow;
+      const float m_use = m_run[hb] == kNegInf ? 0.f : m_run[hb];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pj = __builtin_amdgcn_exp2f(x[j] - m_use);
+        psum += pj;
+        pb[hb][j] = (__bf16)pj;
+      }
+      l_run[hb] = l_run[hb] * alpha[hb] + psum;
+    }
+    if (__any(any_grow)) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int mb = 0; mb < 32; ++mb) o[hb][mb] *= alpha[hb];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- O^T += V^T P^T (M = 16 value columns, N = 16 heads, K = 32 rows with
+  //      k = 8g+i <-> row (i < 4 ? 4g+i : 16+4g+i-4), the S^T lane layout)
+  auto pv = [&](const char* sV) {
+    const char* vp = sV + (4 * g + (t >> 2)) * RS + 8 * (t & 3);
+    constexpr int PV = NW * HB >= 8 ? 2 : 4;
+    s16x4 vb[PV][2];
+    auto vload = [&](int mb, s16x4& lo, s16x4& hi) {
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * mb));
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * RS + 32 * mb));
+    };
+#pragma unroll
+    for (int i = 0; i < PV; ++i) vload(i, vb[i][0], vb[i][1]);
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(vb[mb % PV][0], vb[mb % PV][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+        o[hb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hb], o[hb][mb], 0, 0, 0);
+      if (mb + PV < 32) vload(mb + PV, vb[mb % PV][0], vb[mb % PV][1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if constexpr (VMODE) {
+    // K(t+2) streams in from the end of QK(t); V(t+1) from the start of QK(t).
+    auto step = [&](int tt, char* sKc, char* sVc, char* sVn) {
+      if (tt + 1 < nt) wait_vmcnt<C::NV + C::NK>(); else wait_vmcnt<C::NV>();   // K(tt) landed
+      wait_lgkm0();
+      block_barrier();                                    // ... and V(tt-1) reads are done
+      if (tt + 1 < nt) issue_v<NW, DQK, VMODE>(sAV, (tt + 1) * T, lds_addr(sVn), w, l);
+      if (wave_on) qk_softmax(sKc, tt * T);
+      if (tt + 1 < nt) wait_vmcnt<C::NK + C::NV>(); else wait_vmcnt<0>();        // V(tt) landed
+      wait_lgkm0();
+      block_barrier();                                    // ... and K(tt) reads are done
+      if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(sAK, sAR, (tt + 2) * T, lds_addr(sKc), w, l);
+      if (wave_on) pv(sVc);
+    };
+    // K(0) and the Q slices land first; the explicit full wait also tells
+    // the compiler the Q loads are done, so no wait for them remains inside
+    // the loop (where it would wait for every gather in flight).
+    if (nt > 0) issue_k<NW, DQK, VMODE>(sAK, sAR, 0, lds_addr(sK0), w, l);
+    wait_vmcnt<0>();
+    settle(qreg);
+    if (nt > 0) {
+      issue_v<NW, DQK, VMODE>(sAV, 0, lds_addr(sV0), w, l);
+      if (nt > 1) issue_k<NW, DQK, VMODE>(sAK, sAR, T, lds_addr(sK1), w, l);
+    }
+    for (int tt = 0; tt < nt; tt += 2) {
+      step(tt, sK0, sV0, sV1);
+      if (tt + 1 < nt) step(tt + 1, sK1, sV1, sV0);
+    }
+  } else {
+    // V aliases K: a ring of three K stages, two tiles in flight.
+    auto step = [&](int tt, char* sKc, char* sKn2) {
+      if (tt + 1 < nt) wait_vmcnt<C::NK>(); else wait_vmcnt<0>();   // K(tt) landed
+      wait_lgkm0();
+      block_barrier();                                    // ... and tile tt-1 is consumed
+      if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(sAK, sAR, (tt + 2) * T, lds_addr(sKn2), w, l);
+      if (wave_on) {
+        qk_softmax(sKc, tt * T);
+        pv(sKc);
+      }
+    };
+    if (nt > 0) issue_k<NW, DQK, VMODE>(sAK, sAR, 0, lds_addr(sK0), w, l);
+    wait_vmcnt<0>();                                      // K(0) and the Q slices
+    settle(qreg);
+    if (nt > 1) issue_k<NW, DQK, VMODE>(sAK, sAR, T, lds_addr(sK1), w, l);
+    for (int tt = 0; tt < nt; tt += 3) {
+      step(tt, sK0, sK2);
+      if (tt + 1 < nt) step(tt + 1, sK1, sK0);
+      if (tt + 2 < nt) step(tt + 2, sK2, sK1);
+    }
+  }
+
+  if (!wave_on) return;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    float lt = l_run[hb] + __shfl_xor(l_run[hb], 16);
+    lt += __shfl_xor(lt, 32);
+    const int h = h0 + 16 * hb + t;
+    if (h >= a.qn) continue;
+    const float mr = m_run[hb];
+    const float lse2 = lt > 0.f ? mr + __builtin_log2f(lt) : kNegInf;
+    if (nsplit == 1) {
+      float den = lt;
+      if (a.has_sinks && lt > 0.f) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mr);
+      const float inv = lt > 0.f ? 1.f / den : 0.f;
+      uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512 + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 32; ++mb) {
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(o[hb][mb][0] * inv) | ((uint32_t)f2bf(o[hb][mb][1] * inv) << 16);
+        pk.y = (uint32_t)f2bf(o[hb][mb][2] * inv) | ((uint32_t)f2bf(o[hb][mb][3] * inv) << 16);
+        *(uint2*)(op + 16 * mb) = pk;
+      }
+      if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = lt > 0.f ? lse2 * kLn2 : kNegInf;
+    } else {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int64_t slot = ((int64_t)row * a.max_splits + split) * a.qn + h;
+      float* wp = a.ws_o + slot * 512 + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 32; ++mb)
+        *(float4*)(wp + 16 * mb) = make_float4(o[hb][mb][0] * inv, o[hb][mb][1] * inv,
+                                               o[hb][mb][2] * inv, o[hb][mb][3] * inv);
+      if (g == 0) a.ws_lse[slot] = lt > 0.f ? lse2 * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // merge of split partials
 // ---------------------------------------------------------------------------
 
@@ -614,15 +1047,29 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NW, int HB, int DQK, int VMODE>
+static hipError_t launch_bf16_t(const FwdArgs& a, int groups, hipStream_t s) {
+  FwdArgs b = a;
+  b.groups = groups;
+  const int64_t units = (int64_t)a.q_t * a.max_splits;
+  const int64_t blocks = (units + 7) / 8 * 8 * groups;
+  hipLaunchKernelGGL((fwd_bf16_kernel<NW, HB, DQK, VMODE>), dim3((unsigned)blocks), dim3(NW * 64),
+                     0, s, b);
+  return hipGetLastError();
+}
+
+template <int NW, int HB>
+static hipError_t launch_bf16_nw(const FwdArgs& a, int dqk, int vmode, int groups,
+                                 hipStream_t s) {
+  if (dqk == 512) return vmode ? launch_bf16_t<NW, HB, 512, 1>(a, groups, s)
+                               : launch_bf16_t<NW, HB, 512, 0>(a, groups, s);
+  return vmode ? launch_bf16_t<NW, HB, 576, 1>(a, groups, s)
+               : launch_bf16_t<NW, HB, 576, 0>(a, groups, s);
+}
+
 template <int NW>
 static hipError_t launch_fwd_nw(const FwdArgs& a, int dqk, int vmode, int fmt, int groups,
                                 hipStream_t s) {
-  if (fmt == SFMLA_KV_BF16) {
-    if (dqk == 512) return vmode ? launch_fwd_t<NW, 512, 1, 0>(a, groups, s)
-                                 : launch_fwd_t<NW, 512, 0, 0>(a, groups, s);
-    return vmode ? launch_fwd_t<NW, 576, 1, 0>(a, groups, s)
-                 : launch_fwd_t<NW, 576, 0, 0>(a, groups, s);
-  }
   if (fmt == SFMLA_KV_INT8_PACKED)
     return dqk == 512 ? launch_fwd_t<NW, 512, 0, 1>(a, groups, s)
                       : launch_fwd_t<NW, 576, 0, 1>(a, groups, s);
@@ -630,8 +1077,17 @@ static hipError_t launch_fwd_nw(const FwdArgs& a, int dqk, int vmode, int fmt, i
                     : launch_fwd_t<NW, 576, 0, 2>(a, groups, s);
 }
 
-hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
-                          hipStream_t s) {
+hipError_t launch_forward(const FwdArgs& a, int nw, int hb, int dqk, int vmode, int fmt,
+                          int groups, hipStream_t s) {
+  if (fmt == SFMLA_KV_BF16) {
+    (void)hb;   // one 16-head block per wave (two would not fit the register file)
+    switch (nw) {
+      case 1: return launch_bf16_nw<1, 1>(a, dqk, vmode, groups, s);
+      case 2: return launch_bf16_nw<2, 1>(a, dqk, vmode, groups, s);
+      case 4: return launch_bf16_nw<4, 1>(a, dqk, vmode, groups, s);
+      default: return launch_bf16_nw<8, 1>(a, dqk, vmode, groups, s);
+    }
+  }
   switch (nw) {
     case 1: return launch_fwd_nw<1>(a, dqk, vmode, fmt, groups, s);
     case 2: return launch_fwd_nw<2>(a, dqk, vmode, fmt, groups, s);
