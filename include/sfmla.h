@@ -206,15 +206,18 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
 sfmla_status sfmla_workspace_size(const sfmla_params* params, size_t* bytes);
 
 /*
- * Attention forward (sparse_flash_mla on the API page).  Query rows whose
- * plan has one split get their final attention_out (and softmax_lse); rows
- * the plan splits (lists longer than one split) leave per-split partials in
- * `workspace`, which sfmla_combine() merges.  softmax_scale must be finite.
- * `workspace` holds at least sfmla_workspace_size() bytes, 256-byte aligned
- * (may be NULL when that size is 0).
+ * Attention forward (sparse_flash_mla on the API page): writes attention_out
+ * (and softmax_lse).  softmax_scale must be finite.  `workspace` holds at
+ * least sfmla_workspace_size() bytes, 256-byte aligned (NULL when that size
+ * is 0).  Rows whose list the plan splits are merged inside this call for
+ * bf16 KV (the last split of a row to finish merges the others' partials);
+ * for packed KV their partials stay in `workspace` until sfmla_combine().
+ * The plan buffer doubles as the arrival counters of that in-call merge: the
+ * call leaves them as it found them (zero), so the same plan serves any
+ * number of calls, but two calls that share one plan must not overlap.
  */
 sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* tensors,
-                           const int32_t* metadata, size_t n_ints, float softmax_scale,
+                           int32_t* metadata, size_t n_ints, float softmax_scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -223,7 +226,8 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* tens
  * its partials from `workspace` into attention_out / softmax_lse, adding the
  * sink once:  O = sum_k e^{lse_k} O_k / (sum_k e^{lse_k} + e^{sink}),
  * LSE = log sum_k e^{lse_k}.  Call it after sfmla_forward() with the same
- * arguments; it launches nothing when no row can be split.
+ * arguments; it launches nothing when no row can be split or when the
+ * forward merged them itself (bf16 KV).
  */
 sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* tensors,
                            const int32_t* metadata, size_t n_ints, const void* workspace,

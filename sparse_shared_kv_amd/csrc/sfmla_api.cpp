@@ -147,15 +147,37 @@ int max_splits(const sfmla_params& p) {
 }
 
 size_t metadata_ints(const sfmla_params& p) {
-  return (size_t)sfmla::kHeaderInts + (size_t)sfmla::kRecInts * (size_t)p.q_t;
+  return (size_t)sfmla::kHeaderInts +
+         (size_t)(sfmla::kRecInts + sfmla::kCounterInts) * (size_t)p.q_t;
 }
 
-size_t workspace_bytes(const sfmla_params& p) {
+void choose_groups(const sfmla_params& p, int* nw, int* hb, int* groups);
+
+// Split partials.  bf16 KV: partial O in bf16 for every (row, split, padded
+// head) then the LSEs; packed KV: fp32 partial O then the LSEs.
+struct WsLayout {
+  size_t o_bytes, lse_bytes, total;
+  int heads;   // heads per row as laid out (padded for bf16)
+};
+
+WsLayout workspace_layout(const sfmla_params& p) {
+  WsLayout L{0, 0, 0, p.num_heads_q};
   const int s = max_splits(p);
-  if (s <= 1) return 0;
-  const size_t slots = (size_t)p.q_t * s * p.num_heads_q;
-  return slots * 512 * sizeof(float) + ((slots * sizeof(float) + 255) / 256) * 256;
+  if (s <= 1) return L;
+  const bool bf16 = p.kv_dtype == SFMLA_KV_BF16;
+  if (bf16) {
+    int nw, hb, groups;
+    choose_groups(p, &nw, &hb, &groups);
+    L.heads = groups * nw * hb * 16;
+  }
+  const size_t slots = (size_t)p.q_t * s * L.heads;
+  L.o_bytes = ((slots * 512 * (bf16 ? 2 : 4)) + 255) / 256 * 256;
+  L.lse_bytes = (slots * sizeof(float) + 255) / 256 * 256;
+  L.total = L.o_bytes + L.lse_bytes;
+  return L;
 }
+
+size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total; }
 
 // Workgroup shape: nw waves of 16 heads each (hb = 1 block per wave), in
 // `groups` head groups.  All heads of a query row share one workgroup (the
@@ -345,7 +367,7 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
 }
 
 sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
-                           const int32_t* metadata, size_t n_ints, float softmax_scale,
+                           int32_t* metadata, size_t n_ints, float softmax_scale,
                            void* workspace, size_t ws_bytes, void* stream) {
   sfmla_status s = validate(params);
   if (s != SFMLA_OK) return s;
@@ -359,10 +381,12 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
       return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes,
                   need);
     REQUIRE(((uintptr_t)workspace & 255) == 0, "workspace must be 256-byte aligned");
-    const size_t slots = (size_t)p.q_t * a.max_splits * p.num_heads_q;
+    const WsLayout L = workspace_layout(p);
     a.ws_o = (float*)workspace;
-    a.ws_lse = (float*)((char*)workspace + slots * 512 * sizeof(float));
+    a.ws_ob = (uint16_t*)workspace;
+    a.ws_lse = (float*)((char*)workspace + L.o_bytes);
   }
+  a.counters = metadata + sfmla::kHeaderInts + (size_t)sfmla::kRecInts * p.q_t;
   int nw, hb, groups;
   choose_groups(p, &nw, &hb, &groups);
   const int dqk = 512 + p.rope_head_dim;
@@ -382,12 +406,13 @@ sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* t,
   sfmla::FwdArgs a;
   s = fill_fwd_args(p, t, metadata, n_ints, 1.0f, &a);
   if (s != SFMLA_OK) return s;
-  if (a.max_splits <= 1) return ok();
+  // bf16 KV: the forward kernel merges split rows itself
+  if (a.max_splits <= 1 || p.kv_dtype == SFMLA_KV_BF16) return ok();
   const size_t need = workspace_bytes(p);
   if (!workspace || ws_bytes < need)
     return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
   REQUIRE(((uintptr_t)workspace & 255) == 0, "workspace must be 256-byte aligned");
-  const size_t slots = (size_t)p.q_t * a.max_splits * p.num_heads_q;
+  const WsLayout L = workspace_layout(p);
   sfmla::CombineArgs c;
   std::memset(&c, 0, sizeof c);
   c.rows = p.q_t;
@@ -399,7 +424,7 @@ sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* t,
   c.lse_part_stride = p.num_heads_q;
   c.lse_row_stride = (int64_t)a.max_splits * p.num_heads_q;
   c.part_o = (const float*)workspace;
-  c.part_lse = (const float*)((const char*)workspace + slots * 512 * sizeof(float));
+  c.part_lse = (const float*)((const char*)workspace + L.o_bytes);
   c.sinks = t->sinks;
   c.out = a.out;
   c.lse_out = a.lse;

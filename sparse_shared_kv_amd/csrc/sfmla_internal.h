@@ -12,6 +12,7 @@ constexpr int kTile = 32;          // KV rows staged in LDS per step
 constexpr int kSplitRows = 512;    // KV rows per split of one query row
 constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
+constexpr int kCounterInts = 8;    // arrival counters per query row (one per head group)
 constexpr int32_t kMagic = 0x534d4c41;
 
 // Per-query-row plan record written by the planner (int32 each).
@@ -66,8 +67,10 @@ struct FwdArgs {
   uint16_t* out;
   float* lse;
   int32_t* status;
-  float* ws_o;                      // [q_t][max_splits][qn][512]
-  float* ws_lse;                    // [q_t][max_splits][qn]
+  float* ws_o;                      // packed path: fp32 [q_t][max_splits][qn][512]
+  float* ws_lse;                    // [q_t][max_splits][heads] (bf16 path: log2 units)
+  uint16_t* ws_ob;                  // bf16 path: partial O, per-wave fragment order
+  int32_t* counters;                // bf16 path: [q_t][kCounterInts] arrival counters
   // debug resolve
   int64_t* dbg_rows;
   int32_t* dbg_counts;

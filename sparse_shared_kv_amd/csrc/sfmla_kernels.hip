@@ -189,6 +189,8 @@ __global__ void plan_kernel(PlanArgs a) {
   r[R_ORI_BASE] = ori_base; r[R_CMP_BASE] = cmp_base; r[R_ORI_LEN] = ori_len;
   r[R_CMP_LEN] = cmp_len; r[R_NSPLIT] = nsplit; r[R_CHUNK] = chunk;
   r[R_CMP_LIMIT] = cmp_limit; r[R_NTOTAL] = n;
+  int32_t* cnt = a.meta + kHeaderInts + (int64_t)p.q_t * kRecInts + (int64_t)row * kCounterInts;
+  for (int i = 0; i < kCounterInts; ++i) cnt[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -552,6 +554,33 @@ __device__ __forceinline__ void settle(bf16x8 (&r)[A][B]) {
     for (int j = 0; j < B; ++j) asm volatile("" : "+v"(r[i][j]));
 }
 
+// Cross-workgroup exchange of split partials.  The partials and their LSEs
+// are written and read with relaxed agent-scope atomic accesses, which the
+// gfx950 memory model makes coherent per location across all XCDs (sc1 cache
+// policy) without the whole-L2 write-back / invalidate that an agent-scope
+// fence costs.  Ordering against the arrival counter comes from waiting for
+// every store of the wave to complete (vmcnt 0) before the counter update;
+// the merging workgroup issues its loads only after it has read the counter.
+__device__ __forceinline__ void st_agent(uint16_t* p, uint4 v) {
+  uint64_t* q = (uint64_t*)p;
+  __hip_atomic_store(q, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint4 ld_agent(const uint16_t* p) {
+  uint64_t* q = (uint64_t*)p;
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load((float*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every vector-memory op of this wave (stores included) has completed
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // LDS byte address of a __shared__ object.
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr(T* p) {
@@ -614,6 +643,7 @@ __device__ __forceinline__ void issue_v(const uint64_t* sAV, int tbase, uint32_t
 // same (stale) max, so the result is unchanged while the accumulators are
 // touched only when the max jumps.
 constexpr float kRescaleThreshold = 8.0f;
+constexpr int kMergeSplits = 4;       // splits whose partials one merge round loads
 
 // HB head blocks of 16 heads per wave.
 template <int NW, int HB, int DQK, int VMODE>
@@ -896,38 +926,165 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  if (!wave_on) return;
+  float lt[HB], lse2[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
-    float lt = l_run[hb] + __shfl_xor(l_run[hb], 16);
-    lt += __shfl_xor(lt, 32);
+    float v = l_run[hb] + __shfl_xor(l_run[hb], 16);
+    lt[hb] = v + __shfl_xor(v, 32);
+    lse2[hb] = lt[hb] > 0.f ? m_run[hb] + __builtin_log2f(lt[hb]) : kNegInf;   // log2 units
+  }
+
+  // final output of head block hb from accumulators o (scaled by `scale`)
+  // with total weight `den` and log2-domain LSE `l2`
+  auto write_final = [&](int hb, float scale, float den, float l2) {
     const int h = h0 + 16 * hb + t;
-    if (h >= a.qn) continue;
-    const float mr = m_run[hb];
-    const float lse2 = lt > 0.f ? mr + __builtin_log2f(lt) : kNegInf;
-    if (nsplit == 1) {
-      float den = lt;
-      if (a.has_sinks && lt > 0.f) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mr);
-      const float inv = lt > 0.f ? 1.f / den : 0.f;
-      uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512 + 4 * g;
+    if (h >= a.qn) return;
+    const float inv = den > 0.f ? scale / den : 0.f;
+    uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512 + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 32; ++mb) {
-        uint2 pk;
-        pk.x = (uint32_t)f2bf(o[hb][mb][0] * inv) | ((uint32_t)f2bf(o[hb][mb][1] * inv) << 16);
-        pk.y = (uint32_t)f2bf(o[hb][mb][2] * inv) | ((uint32_t)f2bf(o[hb][mb][3] * inv) << 16);
-        *(uint2*)(op + 16 * mb) = pk;
-      }
-      if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = lt > 0.f ? lse2 * kLn2 : kNegInf;
-    } else {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int64_t slot = ((int64_t)row * a.max_splits + split) * a.qn + h;
-      float* wp = a.ws_o + slot * 512 + 4 * g;
-#pragma unroll
-      for (int mb = 0; mb < 32; ++mb)
-        *(float4*)(wp + 16 * mb) = make_float4(o[hb][mb][0] * inv, o[hb][mb][1] * inv,
-                                               o[hb][mb][2] * inv, o[hb][mb][3] * inv);
-      if (g == 0) a.ws_lse[slot] = lt > 0.f ? lse2 * kLn2 : kNegInf;
+    for (int mb = 0; mb < 32; ++mb) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(o[hb][mb][0] * inv) | ((uint32_t)f2bf(o[hb][mb][1] * inv) << 16);
+      pk.y = (uint32_t)f2bf(o[hb][mb][2] * inv) | ((uint32_t)f2bf(o[hb][mb][3] * inv) << 16);
+      *(uint2*)(op + 16 * mb) = pk;
     }
+    if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = den > 0.f ? l2 * kLn2 : kNegInf;
+  };
+
+  if (nsplit == 1) {
+    if (!wave_on) return;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = h0 + 16 * hb + t;
+      float den = lt[hb];
+      if (a.has_sinks && lt[hb] > 0.f && h < a.qn)
+        den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - m_run[hb]);
+      write_final(hb, 1.f, lt[hb] > 0.f ? den : 0.f, lse2[hb]);
+    }
+    return;
+  }
+
+  // ---- split rows: every split stores its normalised partial (bf16, in the
+  // lanes' fragment order: instruction j of a wave writes 1 KB contiguously),
+  // then counts itself in; the last one to arrive merges all of them.
+  const int HP = a.groups * NW * HPW;              // heads per row, padded
+  const int64_t wave_slot = (((int64_t)row * a.max_splits + split) * a.groups + hg) * NW + w;
+  uint16_t* pw = a.ws_ob + wave_slot * (HB * 16 * 64 * 8);
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint4 pk;
+      pk.x = (uint32_t)f2bf(o[hb][2 * j][0] * inv) | ((uint32_t)f2bf(o[hb][2 * j][1] * inv) << 16);
+      pk.y = (uint32_t)f2bf(o[hb][2 * j][2] * inv) | ((uint32_t)f2bf(o[hb][2 * j][3] * inv) << 16);
+      pk.z = (uint32_t)f2bf(o[hb][2 * j + 1][0] * inv) |
+             ((uint32_t)f2bf(o[hb][2 * j + 1][1] * inv) << 16);
+      pk.w = (uint32_t)f2bf(o[hb][2 * j + 1][2] * inv) |
+             ((uint32_t)f2bf(o[hb][2 * j + 1][3] * inv) << 16);
+      st_agent(pw + ((hb * 16 + j) * 64 + l) * 8, pk);
+    }
+    if (g == 0) st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
+  }
+  drain_vmem();                                     // this wave's partial is stored
+  __shared__ int sLast;
+  __syncthreads();
+  if (tid == 0)
+    sLast = __hip_atomic_fetch_add(&a.counters[(int64_t)row * kCounterInts + hg], 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  __syncthreads();
+  if (!sLast) return;
+  if (tid == 0)                                     // ready for the next call
+    __hip_atomic_store(&a.counters[(int64_t)row * kCounterInts + hg], 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  if (!wave_on) return;
+  // merge from the stored partials (this split's own included).  Loads are
+  // issued in rounds of kMergeSplits splits x JB column blocks so that each
+  // wave keeps 16 independent 16-B loads in flight.
+  constexpr int MS = kMergeSplits, JB = 4;
+  const int64_t split_stride = (int64_t)a.groups * NW * (HB * 16 * 64 * 8);
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = h0 + 16 * hb + t;
+    const float* lp = a.ws_lse + (int64_t)row * a.max_splits * HP + h;
+    float M = kNegInf;
+#pragma unroll 1
+    for (int s0 = 0; s0 < nsplit; s0 += MS) {
+      float v[MS];
+#pragma unroll
+      for (int q = 0; q < MS; ++q) v[q] = ld_agent(lp + (int64_t)min(s0 + q, nsplit - 1) * HP);
+#pragma unroll
+      for (int q = 0; q < MS; ++q) M = fmaxf(M, v[q]);
+    }
+    const float Mu = M == kNegInf ? 0.f : M;
+    float tot = 0.f;
+#pragma unroll 1
+    for (int s0 = 0; s0 < nsplit; s0 += MS) {
+      float v[MS];
+#pragma unroll
+      for (int q = 0; q < MS; ++q) v[q] = ld_agent(lp + (int64_t)min(s0 + q, nsplit - 1) * HP);
+#pragma unroll
+      for (int q = 0; q < MS; ++q)
+        if (s0 + q < nsplit) tot += __builtin_amdgcn_exp2f(v[q] - Mu);
+    }
+    float den = tot;
+    if (a.has_sinks && h < a.qn && tot > 0.f)
+      den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - Mu);
+    const float inv = tot > 0.f ? 1.f / den : 0.f;
+    const bool on = h < a.qn;
+    uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g;
+    const uint16_t* pr0 = a.ws_ob + ((((int64_t)row * a.max_splits) * a.groups + hg) * NW + w) *
+                                        (HB * 16 * 64 * 8) +
+                          ((hb * 16) * 64 + l) * 8;
+#pragma unroll 1
+    for (int jh = 0; jh < 16 / JB; ++jh) {
+      float acc[JB][8];
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+#pragma unroll 1
+      for (int s0 = 0; s0 < nsplit; s0 += MS) {
+        uint4 v[MS][JB];
+        float wl[MS];
+#pragma unroll
+        for (int q = 0; q < MS; ++q) {
+          const int s2 = min(s0 + q, nsplit - 1);
+          wl[q] = ld_agent(lp + (int64_t)s2 * HP);
+#pragma unroll
+          for (int j = 0; j < JB; ++j)
+            v[q][j] = ld_agent(pr0 + s2 * split_stride + (jh * JB + j) * 64 * 8);
+        }
+#pragma unroll
+        for (int q = 0; q < MS; ++q) {
+          const float ws = s0 + q < nsplit ? __builtin_amdgcn_exp2f(wl[q] - Mu) : 0.f;
+#pragma unroll
+          for (int j = 0; j < JB; ++j) {
+            const uint32_t u[4] = {v[q][j].x, v[q][j].y, v[q][j].z, v[q][j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[j][2 * e] += ws * __builtin_bit_cast(float, u[e] << 16);
+              acc[j][2 * e + 1] += ws * __builtin_bit_cast(float, u[e] & 0xffff0000u);
+            }
+          }
+        }
+      }
+      if (on) {
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          const int jj = jh * JB + j;
+          uint2 p0, p1;
+          p0.x = (uint32_t)f2bf(acc[j][0] * inv) | ((uint32_t)f2bf(acc[j][1] * inv) << 16);
+          p0.y = (uint32_t)f2bf(acc[j][2] * inv) | ((uint32_t)f2bf(acc[j][3] * inv) << 16);
+          p1.x = (uint32_t)f2bf(acc[j][4] * inv) | ((uint32_t)f2bf(acc[j][5] * inv) << 16);
+          p1.y = (uint32_t)f2bf(acc[j][6] * inv) | ((uint32_t)f2bf(acc[j][7] * inv) << 16);
+          *(uint2*)(op + 16 * (2 * jj)) = p0;
+          *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
+        }
+      }
+    }
+    if (on && a.lse && g == 0)
+      a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;
   }
 }
 
