@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "sparse_shared_kv_amd", "csrc", "sfmla_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_kernel_%s.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_%s_%s.txt")      # (kernel, workload)
 
 DESCR = {
     "sfa_mla_rope": "token-wise sparse MLA-absorb decode with rope: B=32, q_s=2, q_n=128, "
@@ -65,10 +66,15 @@ def row_bytes(P) -> tuple:
     return b, 2 * (d_qk + 512)
 
 
-def read_traffic(workload: str):
+def kernel_name(P) -> str:
+    """The forward kernel that runs for this workload's KV format."""
+    return "fwd_bf16_kernel" if P.params["kv_dtype"] == "bf16" else "fwd_kernel"
+
+
+def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source (else None)."""
-    path = TRAFFIC_FILE % workload
+    path = TRAFFIC_FILE % (kernel, workload)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -107,6 +113,94 @@ def cpu_baseline(P, flops_per_row, bytes_per_row, budget_s=10.0):
                       "%.3f GB/s gathered KV" % (len(done), len(rows), dt, by / dt / 1e9)}
 
 
+COPY_PROBE_MB = 256
+
+
+def profile_commands(outdir: str, workload: str) -> list:
+    """The rocprofv3 runs whose summaries are kept under profiles/: one
+    kernel trace with statistics, then one counter pass each for FETCH_SIZE
+    and WRITE_SIZE (with a plain device copy of known size for calibration)."""
+    b = "python3 bench.py --workload %s --no-cpu-baseline" % workload
+    return [
+        "rocprofv3 --kernel-trace --stats --output-format csv -d %s/trace -o trace -- %s"
+        % (outdir, b),
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s/fetch -o fetch -- %s --steps 5 "
+        "--warmup 2 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s/write -o write -- %s --steps 5 "
+        "--warmup 2 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
+    ]
+
+
+def write_profiles(outdir: str, workload: str) -> None:
+    """Summarise the runs of profile_commands() into profiles/ (text)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    cmds = profile_commands(outdir, workload)
+    kern = "fwd_kernel" if workload.startswith("c8_packed") else "fwd_bf16_kernel"
+    src = kernel_source_hash()
+
+    # kernel trace statistics
+    stats = glob.glob(os.path.join(outdir, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    assert stats, "no kernel_stats.csv under %s/trace" % outdir
+    rows = list(csv.DictReader(open(stats[0])))
+    lines = ["# rocprofv3 kernel trace, workload %s" % workload,
+             "# command (from the repository root):", "#   " + cmds[0],
+             "# kernel_source_sha256_16 = %s" % src, "",
+             "%-62s %6s %11s %11s %11s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
+    for r in rows:
+        lines.append("%-62s %6d %11.3f %11.3f %11.3f %7.2f" % (
+            r["Name"][:62], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    path = os.path.join(PROFILES, "%s_%s.txt" % (kern, workload))
+    open(path, "w").write("\n".join(lines) + "\n")
+    log("[profiles] wrote", path)
+
+    # HBM traffic from FETCH_SIZE / WRITE_SIZE, calibrated on the copy probe
+    def counters(sub, name):
+        f = glob.glob(os.path.join(outdir, sub, "**", "*counter_collection.csv"), recursive=True)
+        assert f, "no counter_collection.csv under %s/%s" % (outdir, sub)
+        per = defaultdict(list)
+        copy = []
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != name:
+                continue
+            v = float(r["Counter_Value"])
+            if kern + "<" in r["Kernel_Name"] or ("::" + kern + "(") in r["Kernel_Name"]:
+                per["k"].append(v)
+            if "copyBuffer" in r["Kernel_Name"]:
+                copy.append((int(r["Grid_Size"]), v))
+        assert per["k"] and copy, "kernel or copy probe missing in %s" % f[0]
+        return sum(per["k"]) / len(per["k"]), max(copy)[1], len(per["k"])
+
+    fk, fc, nf = counters("fetch", "FETCH_SIZE")
+    wk, wc, nw = counters("write", "WRITE_SIZE")
+    probe = COPY_PROBE_MB * (1 << 20)
+    ff, wf = probe / (fc * 1024.0), probe / (wc * 1024.0)
+    hbm = fk * 1024.0 * ff + wk * 1024.0 * wf
+    lines = ["# HBM traffic of %s, workload %s (rocprofv3 counters, KiB per dispatch)" % (kern, workload),
+             "# commands (from the repository root):", "#   " + cmds[1], "#   " + cmds[2],
+             "# calibration: the %d MiB device copy (reads and writes %d bytes each) reads"
+             % (COPY_PROBE_MB, probe),
+             "#   FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB: scale factors %.4f and %.4f" % (fc, wc, ff, wf),
+             "kernel = %s" % kern,
+             "workload = %s" % workload,
+             "kernel_source_sha256_16 = %s" % src,
+             "dispatches_fetch = %d" % nf,
+             "dispatches_write = %d" % nw,
+             "fetch_kib_per_dispatch = %.1f" % fk,
+             "write_kib_per_dispatch = %.1f" % wk,
+             "fetch_scale = %.4f" % ff,
+             "write_scale = %.4f" % wf,
+             "hbm_read_bytes_per_launch = %.0f" % (fk * 1024.0 * ff),
+             "hbm_write_bytes_per_launch = %.0f" % (wk * 1024.0 * wf),
+             "hbm_bytes_per_launch = %.0f" % hbm]
+    path = TRAFFIC_FILE % (kern, workload)
+    open(path, "w").write("\n".join(lines) + "\n")
+    log("[profiles] wrote", path)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,7 +212,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
+    ap.add_argument("--profile-commands", metavar="OUTDIR",
+                    help="print the rocprofv3 commands whose summaries go to profiles/, and exit")
+    ap.add_argument("--write-profiles", metavar="OUTDIR",
+                    help="summarise the output of those commands into profiles/, and exit")
     args = ap.parse_args()
+
+    if args.profile_commands:
+        print("\n".join(profile_commands(args.profile_commands, args.workload)))
+        return
+    if args.write_profiles:
+        write_profiles(args.write_profiles, args.workload)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -144,6 +249,7 @@ def main():
         name = reps[0][0]
         idx_sets = [call.d[name]] + [torch.from_numpy(a).to(dev) for _, a in reps]
     log("[bench] index replicas:", len(idx_sets) or 1)
+    idx_ptrs = [t.data_ptr() for t in idx_sets]
 
     # algorithmic work: resolved rows per query row (from the library's resolver)
     rb, fl_row = row_bytes(P)
@@ -151,7 +257,7 @@ def main():
     counts_all = []
     for k in range(max(1, len(idx_sets))):
         if idx_sets:
-            setattr(call.tensors, reps[0][0], idx_sets[k].data_ptr())
+            setattr(call.tensors, reps[0][0], idx_ptrs[k])
         call.plan()
         _, counts = call.resolve(1)
         counts_all.append(counts.cpu().numpy().astype(np.int64))
@@ -159,43 +265,55 @@ def main():
     rows_per_step = [int(c.sum()) for c in counts_all]
     flops_step = [n * fl_row * qn for n in rows_per_step]
     bytes_step = [n * rb for n in rows_per_step]
+    nrep = max(1, len(idx_sets))
 
     stream = torch.cuda.current_stream()
 
-    def step(k):
+    def select(k):
         if idx_sets:
-            setattr(call.tensors, reps[0][0], idx_sets[k % len(idx_sets)].data_ptr())
-        call.plan()
-        call.forward()
-        call.combine()
+            setattr(call.tensors, reps[0][0], idx_ptrs[k % nrep])
 
     for k in range(args.warmup):
-        step(k)
+        select(k)
+        call.plan(stream)
+        call.forward(stream)
+        call.combine(stream)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: K whole steps; HIP events on the launch stream bracket
+    # every forward launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        if idx_sets:
-            setattr(call.tensors, reps[0][0], idx_sets[k % len(idx_sets)].data_ptr())
-        e = ev[k]
-        e[0].record(stream)
-        call.plan()
-        e[1].record(stream)
-        call.forward()
-        e[2].record(stream)
-        call.combine()
-        e[3].record(stream)
+        select(k)
+        call.plan(stream)
+        ev[k][0].record(stream)
+        call.forward(stream)
+        ev[k][1].record(stream)
+        call.combine(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert int(call.status.item()) == 0, "device status %d" % int(call.status.item())
+    fwd_ms = [a.elapsed_time(b) for a, b in ev]
 
-    plan_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    fwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    # untimed: plan and combine durations for the report
+    pe = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
+    for k, e in enumerate(pe):
+        select(k)
+        e[0].record(stream)
+        call.plan(stream)
+        e[1].record(stream)
+        call.forward(stream)
+        e[2].record(stream)
+        call.combine(stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    plan_ms = [e[0].elapsed_time(e[1]) for e in pe]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in pe]
+
     ms_per_step = wall * 1e3 / args.steps
-    nrep = max(1, len(idx_sets))
     tot_flops = sum(flops_step[k % nrep] for k in range(args.steps))
     tot_bytes = sum(bytes_step[k % nrep] for k in range(args.steps))
     tflops = tot_flops / wall / 1e12
@@ -209,7 +327,8 @@ def main():
         achieved, peak, unit = fwd_bytes / fwd_avg_s / 1e9, HBM_PEAK_GBPS, "GB/s"
     else:
         achieved, peak, unit = fwd_flops / fwd_avg_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    traffic = read_traffic(args.workload)
+    kern = kernel_name(P)
+    traffic = read_traffic(kern, args.workload)
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 4
@@ -243,7 +362,7 @@ def main():
         "kernel_ms": {"plan": round(float(np.mean(plan_ms)), 5),
                       "forward": round(float(np.mean(fwd_ms)), 5),
                       "combine": round(float(np.mean(comb_ms)), 5)},
-        "roofline": {"kernel": "sfmla::fwd_kernel",
+        "roofline": {"kernel": "sfmla::" + kern,
                      "bound": "hbm" if hbm_bound else "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),

@@ -555,22 +555,20 @@ __device__ __forceinline__ void settle(bf16x8 (&r)[A][B]) {
 }
 
 // Cross-workgroup exchange of split partials.  The partials and their LSEs
-// are written and read with relaxed agent-scope atomic accesses, which the
-// gfx950 memory model makes coherent per location across all XCDs (sc1 cache
-// policy) without the whole-L2 write-back / invalidate that an agent-scope
-// fence costs.  Ordering against the arrival counter comes from waiting for
-// every store of the wave to complete (vmcnt 0) before the counter update;
-// the merging workgroup issues its loads only after it has read the counter.
-__device__ __forceinline__ void st_agent(uint16_t* p, uint4 v) {
-  uint64_t* q = (uint64_t*)p;
-  __hip_atomic_store(q, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint4 ld_agent(const uint16_t* p) {
-  uint64_t* q = (uint64_t*)p;
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+// are written and read with agent-scope accesses (sc1 cache policy: the code
+// the gfx950 memory model uses for relaxed agent-scope atomic loads and
+// stores, coherent per location across all XCDs) without the whole-L2
+// write-back / invalidate that an agent-scope fence costs.  Ordering against
+// the arrival counter comes from waiting for every store of the wave to
+// complete (vmcnt 0) before the counter update; the merging workgroup issues
+// its loads only after it has read the counter.  Partials move as 16-byte
+// buffer accesses (one full 16-byte chunk per lane), so no line is written
+// or fetched twice.
+constexpr int kSc1 = 16;                 // cache-policy bit sc1 of buffer ops
+constexpr int kBufWord3 = 0x00020000;    // raw buffer descriptor, 32-bit data format
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufWord3);
 }
 __device__ __forceinline__ void st_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -968,8 +966,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   // lanes' fragment order: instruction j of a wave writes 1 KB contiguously),
   // then counts itself in; the last one to arrive merges all of them.
   const int HP = a.groups * NW * HPW;              // heads per row, padded
-  const int64_t wave_slot = (((int64_t)row * a.max_splits + split) * a.groups + hg) * NW + w;
-  uint16_t* pw = a.ws_ob + wave_slot * (HB * 16 * 64 * 8);
+  constexpr int WAVE_BYTES = HB * 16 * 64 * 16;    // one wave's partial
+  // every split, head group and wave of this query row (< 2^31 bytes: at
+  // most 4096 splits x 128 heads x 1 KB)
+  const int64_t row_bytes = (int64_t)a.max_splits * a.groups * NW * WAVE_BYTES;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc((char*)a.ws_ob + row * row_bytes, row_bytes);
+  const int wave_off = ((split * a.groups + hg) * NW + w) * WAVE_BYTES;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
@@ -982,7 +984,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
              ((uint32_t)f2bf(o[hb][2 * j + 1][1] * inv) << 16);
       pk.w = (uint32_t)f2bf(o[hb][2 * j + 1][2] * inv) |
              ((uint32_t)f2bf(o[hb][2 * j + 1][3] * inv) << 16);
-      st_agent(pw + ((hb * 16 + j) * 64 + l) * 8, pk);
+      const u32x4 d = {pk.x, pk.y, pk.z, pk.w};
+      __builtin_amdgcn_raw_buffer_store_b128(d, rs, wave_off + ((hb * 16 + j) * 64 + l) * 16, 0, kSc1);
     }
     if (g == 0) st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
   }
@@ -1002,7 +1005,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   // issued in rounds of kMergeSplits splits x JB column blocks so that each
   // wave keeps 16 independent 16-B loads in flight.
   constexpr int MS = kMergeSplits, JB = 4;
-  const int64_t split_stride = (int64_t)a.groups * NW * (HB * 16 * 64 * 8);
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int h = h0 + 16 * hb + t;
@@ -1033,9 +1035,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const float inv = tot > 0.f ? 1.f / den : 0.f;
     const bool on = h < a.qn;
     uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g;
-    const uint16_t* pr0 = a.ws_ob + ((((int64_t)row * a.max_splits) * a.groups + hg) * NW + w) *
-                                        (HB * 16 * 64 * 8) +
-                          ((hb * 16) * 64 + l) * 8;
+    const int off0 = (hg * NW + w) * WAVE_BYTES + ((hb * 16) * 64 + l) * 16;   // split 0
+    const int split_bytes = a.groups * NW * WAVE_BYTES;
 #pragma unroll 1
     for (int jh = 0; jh < 16 / JB; ++jh) {
       float acc[JB][8];
@@ -1045,7 +1046,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
 #pragma unroll 1
       for (int s0 = 0; s0 < nsplit; s0 += MS) {
-        uint4 v[MS][JB];
+        u32x4 v[MS][JB];
         float wl[MS];
 #pragma unroll
         for (int q = 0; q < MS; ++q) {
@@ -1053,7 +1054,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
           wl[q] = ld_agent(lp + (int64_t)s2 * HP);
 #pragma unroll
           for (int j = 0; j < JB; ++j)
-            v[q][j] = ld_agent(pr0 + s2 * split_stride + (jh * JB + j) * 64 * 8);
+            v[q][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, off0 + s2 * split_bytes + (jh * JB + j) * 64 * 16, 0, kSc1);
         }
 #pragma unroll
         for (int q = 0; q < MS; ++q) {
