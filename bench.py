@@ -67,8 +67,8 @@ def row_bytes(P) -> tuple:
 
 
 def kernel_name(P) -> str:
-    """The forward kernel that runs for this workload's KV format."""
-    return "fwd_bf16_kernel" if P.params["kv_dtype"] == "bf16" else "fwd_kernel"
+    """The forward kernel (one template for every KV format)."""
+    return "fwd_kernel"
 
 
 def read_traffic(kernel: str, workload: str):
@@ -138,7 +138,7 @@ def write_profiles(outdir: str, workload: str) -> None:
     from collections import defaultdict
 
     cmds = profile_commands(outdir, workload)
-    kern = "fwd_kernel" if workload.startswith("c8_packed") else "fwd_bf16_kernel"
+    kern = "fwd_kernel"
     src = kernel_source_hash()
 
     # kernel trace statistics

@@ -209,10 +209,10 @@ sfmla_status sfmla_workspace_size(const sfmla_params* params, size_t* bytes);
  * Attention forward (sparse_flash_mla on the API page): writes attention_out
  * (and softmax_lse).  softmax_scale must be finite.  `workspace` holds at
  * least sfmla_workspace_size() bytes, 256-byte aligned (NULL when that size
- * is 0).  Rows whose list the plan splits are merged inside this call for
- * bf16 KV (the last split of a row to finish merges the others' partials);
- * for packed KV their partials stay in `workspace` until sfmla_combine().
- * The plan buffer doubles as the arrival counters of that in-call merge: the
+ * is 0).  Rows whose list the plan splits are merged inside this call (the
+ * last split of a row to finish merges the others' partials, which pass
+ * through `workspace` as bf16), so attention_out and softmax_lse are final
+ * when the call's work completes.  The plan buffer doubles as the arrival counters of that in-call merge: the
  * call leaves them as it found them (zero), so the same plan serves any
  * number of calls, but two calls that share one plan must not overlap.
  */
@@ -221,13 +221,12 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* tens
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Split-KV merge (the FLASH_DECODE split of the kv_quant_sparse_flash_attention
- * blog's kernel structure): for every query row the plan splits, LSE-merge
- * its partials from `workspace` into attention_out / softmax_lse, adding the
- * sink once:  O = sum_k e^{lse_k} O_k / (sum_k e^{lse_k} + e^{sink}),
- * LSE = log sum_k e^{lse_k}.  Call it after sfmla_forward() with the same
- * arguments; it launches nothing when no row can be split or when the
- * forward merged them itself (bf16 KV).
+ * Split-KV merge step (the FLASH_DECODE split of the kv_quant_sparse_flash_attention
+ * blog's kernel structure): O = sum_k e^{lse_k} O_k / (sum_k e^{lse_k} + e^{sink}),
+ * LSE = log sum_k e^{lse_k}, the sink added once.  sfmla_forward() performs
+ * this merge itself for every split row, so this call validates its
+ * arguments like sfmla_forward() and launches nothing; it is kept so that a
+ * caller's plan / forward / combine sequence stays valid.
  */
 sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* tensors,
                            const int32_t* metadata, size_t n_ints, const void* workspace,

@@ -151,27 +151,26 @@ size_t metadata_ints(const sfmla_params& p) {
          (size_t)(sfmla::kRecInts + sfmla::kCounterInts) * (size_t)p.q_t;
 }
 
-void choose_groups(const sfmla_params& p, int* nw, int* hb, int* groups);
+// Workgroups below which a launch spreads a row's heads over several groups.
+constexpr int64_t kMinGroups = 256;
+void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg);
 
-// Split partials.  bf16 KV: partial O in bf16 for every (row, split, padded
-// head) then the LSEs; packed KV: fp32 partial O then the LSEs.
+// Split partials: normalised bf16 partial O for every (row, split, padded
+// head), laid out per wave in MFMA fragment order, then the log2-domain LSEs.
 struct WsLayout {
   size_t o_bytes, lse_bytes, total;
-  int heads;   // heads per row as laid out (padded for bf16)
+  int heads;   // heads per row as laid out (padded to whole waves)
 };
 
 WsLayout workspace_layout(const sfmla_params& p) {
   WsLayout L{0, 0, 0, p.num_heads_q};
   const int s = max_splits(p);
   if (s <= 1) return L;
-  const bool bf16 = p.kv_dtype == SFMLA_KV_BF16;
-  if (bf16) {
-    int nw, hb, groups;
-    choose_groups(p, &nw, &hb, &groups);
-    L.heads = groups * nw * hb * 16;
-  }
+  int nw, groups, bpg;
+  choose_groups(p, &nw, &groups, &bpg);
+  L.heads = groups * nw * 16;
   const size_t slots = (size_t)p.q_t * s * L.heads;
-  L.o_bytes = ((slots * 512 * (bf16 ? 2 : 4)) + 255) / 256 * 256;
+  L.o_bytes = (slots * 512 * 2 + 255) / 256 * 256;
   L.lse_bytes = (slots * sizeof(float) + 255) / 256 * 256;
   L.total = L.o_bytes + L.lse_bytes;
   return L;
@@ -179,34 +178,32 @@ WsLayout workspace_layout(const sfmla_params& p) {
 
 size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total; }
 
-// Workgroup shape: nw waves of 16 heads each (hb = 1 block per wave), in
-// `groups` head groups.  All heads of a query row share one workgroup (the
-// KV rows are gathered once) unless the grid would have fewer than about one
-// workgroup per CU; then the heads are spread over more, smaller workgroups.
-void choose_groups(const sfmla_params& p, int* nw, int* hb, int* groups) {
+// Workgroup shape: nw waves; the heads of a query row are cut into `groups`
+// head groups of bpg 16-head blocks (bpg <= nw), one block per wave, and the
+// waves past bpg only help gather.  All heads of a query row share one
+// workgroup (the KV rows are gathered once) unless the grid would have too
+// few workgroups to spread over the chip; then the heads are spread over
+// more groups, each re-gathering the row's KV (mostly from L2).  The shape
+// never changes a result: every head is computed the same way in any group.
+void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
   const int64_t units = (int64_t)p.q_t * max_splits(p);
   const int blocks = (p.num_heads_q + 15) / 16;        // 16-head blocks
-  const bool bf16 = p.kv_dtype == SFMLA_KV_BF16;
-  // SFMLA_SHAPE="waves,blocks_per_wave" overrides the shape (tuning aid)
-  if (const char* env = getenv("SFMLA_SHAPE")) {
-    int w = 0, b = 0;
-    if (sscanf(env, "%d,%d", &w, &b) == 2 && b == 1 &&
-        (w == 1 || w == 2 || w == 4 || w == 8)) {
-      *nw = w;
-      *hb = b;
-      *groups = (blocks + w * b - 1) / (w * b);
+  const int wmax = p.kv_dtype == SFMLA_KV_BF16 ? 8 : 4;  // packed rows: more registers per wave
+  *nw = wmax;
+  // SFMLA_BPG=<blocks per group> overrides the split of the heads (tuning aid)
+  if (const char* env = getenv("SFMLA_BPG")) {
+    const int b = atoi(env);
+    if (b == 1 || b == 2 || b == 4 || b == 8) {
+      *bpg = std::min(b, wmax);
+      *groups = (blocks + *bpg - 1) / *bpg;
       return;
     }
   }
-  int b = 1;
-  const int wmax = 8;
-  int per = std::min(wmax * b, blocks);                // blocks per workgroup
-  while (per > 1 && units * ((blocks + per - 1) / per) < 256) per = (per + 1) / 2;
-  if (per == 1) b = 1;
-  const int w = (per + b - 1) / b;
-  *hb = b;
-  *nw = w;
-  *groups = (blocks + w * b - 1) / (w * b);
+  int per = 1;                                         // blocks per group: 1, 2, 4 or 8
+  while (per < wmax && per < blocks) per *= 2;
+  while (per > 1 && units * ((blocks + per - 1) / per) < kMinGroups) per /= 2;
+  *bpg = per;
+  *groups = (blocks + per - 1) / per;
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
@@ -382,17 +379,17 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
                   need);
     REQUIRE(((uintptr_t)workspace & 255) == 0, "workspace must be 256-byte aligned");
     const WsLayout L = workspace_layout(p);
-    a.ws_o = (float*)workspace;
     a.ws_ob = (uint16_t*)workspace;
     a.ws_lse = (float*)((char*)workspace + L.o_bytes);
   }
   a.counters = metadata + sfmla::kHeaderInts + (size_t)sfmla::kRecInts * p.q_t;
-  int nw, hb, groups;
-  choose_groups(p, &nw, &hb, &groups);
+  int nw, groups, bpg;
+  choose_groups(p, &nw, &groups, &bpg);
+  a.bpg = bpg;
   const int dqk = 512 + p.rope_head_dim;
   const int vmode = p.has_separate_v ? 1 : 0;
   hipError_t e =
-      sfmla::launch_forward(a, nw, hb, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream);
+      sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -406,30 +403,11 @@ sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* t,
   sfmla::FwdArgs a;
   s = fill_fwd_args(p, t, metadata, n_ints, 1.0f, &a);
   if (s != SFMLA_OK) return s;
-  // bf16 KV: the forward kernel merges split rows itself
-  if (a.max_splits <= 1 || p.kv_dtype == SFMLA_KV_BF16) return ok();
-  const size_t need = workspace_bytes(p);
-  if (!workspace || ws_bytes < need)
-    return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
-  REQUIRE(((uintptr_t)workspace & 255) == 0, "workspace must be 256-byte aligned");
-  const WsLayout L = workspace_layout(p);
-  sfmla::CombineArgs c;
-  std::memset(&c, 0, sizeof c);
-  c.rows = p.q_t;
-  c.heads = p.num_heads_q;
-  c.dv = 512;
-  c.meta = metadata;
-  c.o_part_stride = (int64_t)p.num_heads_q * 512;
-  c.o_row_stride = (int64_t)a.max_splits * p.num_heads_q * 512;
-  c.lse_part_stride = p.num_heads_q;
-  c.lse_row_stride = (int64_t)a.max_splits * p.num_heads_q;
-  c.part_o = (const float*)workspace;
-  c.part_lse = (const float*)((const char*)workspace + L.o_bytes);
-  c.sinks = t->sinks;
-  c.out = a.out;
-  c.lse_out = a.lse;
-  hipError_t e = sfmla::launch_combine(c, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
+  // the forward kernel merges split rows itself (the last split of a row to
+  // finish merges them), so there is nothing left to launch
+  (void)workspace;
+  (void)ws_bytes;
+  (void)stream;
   return ok();
 }
 

@@ -50,6 +50,7 @@ struct FwdArgs {
   int32_t ori_topk, cmp_topk, ori_mode, win_l, win_r, has_cmp;
   int32_t max_splits, has_sinks;
   int32_t groups;                   // head groups of the launch
+  int32_t bpg;                      // 16-head blocks per head group (<= waves; spare waves only load)
   uint32_t fingerprint;
   float scale_log2;                 // softmax_scale * log2(e)
   const int32_t* meta;
@@ -67,7 +68,6 @@ struct FwdArgs {
   uint16_t* out;
   float* lse;
   int32_t* status;
-  float* ws_o;                      // packed path: fp32 [q_t][max_splits][qn][512]
   float* ws_lse;                    // [q_t][max_splits][heads] (bf16 path: log2 units)
   uint16_t* ws_ob;                  // bf16 path: partial O, per-wave fragment order
   int32_t* counters;                // bf16 path: [q_t][kCounterInts] arrival counters
@@ -92,10 +92,9 @@ struct CombineArgs {
 
 // Kernel launchers (defined in sfmla_kernels.hip).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_forward(const FwdArgs& a, int nw, int hb, int dqk, int vmode, int fmt,
-                          int groups, hipStream_t s);
+hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
+                          hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_debug_resolve(const FwdArgs& a, hipStream_t s);
-size_t forward_lds_bytes(int dqk, int vmode, int fmt);
 
 }  // namespace sfmla

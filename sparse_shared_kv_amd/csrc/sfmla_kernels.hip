@@ -5,10 +5,12 @@
 //                      step of the sparse_flash_mla API page).
 //   fwd_kernel         one workgroup per (split, query row, head group):
 //                      resolve the split's list positions to physical rows,
-//                      gather them into LDS, S^T = K Q^T on bf16 MFMA,
+//                      gather them into LDS (packed INT8 / FP8 rows are then
+//                      decoded exactly to bf16), S^T = K Q^T on bf16 MFMA,
 //                      online softmax, O^T += V^T P^T on bf16 MFMA, then the
-//                      final output or a partial for the merge.
-//   combine_kernel     LSE merge of split partials with the sink applied once.
+//                      final output, or a partial that the last split of the
+//                      row to finish merges.
+//   combine_kernel     generic LSE merge of fp32 partials, sink applied once.
 //   resolve_kernel     debug dump of the resolved rows in canonical order.
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l holds A[m = l%16][k = 8(l/16)+i],
@@ -36,63 +38,98 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-__device__ __forceinline__ int64_t map_row(int layout, int64_t base, int bs, int bt_cols,
-                                           const int32_t* bt, int b, int j, int64_t pool_rows,
-                                           int32_t* status) {
-  int64_t phys;
-  if (layout == SFMLA_LAYOUT_PA_BSND) {
-    int blk = j / bs;
-    if (blk >= bt_cols) {
-      if (status) atomicOr(status, SFMLA_STATUS_ROW_OUT_OF_RANGE);
+// The resolution of one list position is split into its memory steps so
+// that a workgroup can issue every position's index load, then every
+// position's block-table load, with the loads of all positions in flight.
+// The row's plan record is read once, into uniform registers.
+struct RowInfo {
+  int b, p, ori_lo, ori_cnt, ori_len, cmp_limit, ori_base, cmp_base;
+};
+
+__device__ __forceinline__ RowInfo row_info(const int32_t* rec) {
+  RowInfo r;
+  r.b = __builtin_amdgcn_readfirstlane(rec[R_B]);
+  r.p = __builtin_amdgcn_readfirstlane(rec[R_P]);
+  r.ori_lo = __builtin_amdgcn_readfirstlane(rec[R_ORI_LO]);
+  r.ori_cnt = __builtin_amdgcn_readfirstlane(rec[R_ORI_CNT]);
+  r.ori_len = __builtin_amdgcn_readfirstlane(rec[R_ORI_LEN]);
+  r.cmp_limit = __builtin_amdgcn_readfirstlane(rec[R_CMP_LIMIT]);
+  r.ori_base = __builtin_amdgcn_readfirstlane(rec[R_ORI_BASE]);
+  r.cmp_base = __builtin_amdgcn_readfirstlane(rec[R_CMP_BASE]);
+  return r;
+}
+
+// List position k of query row `row` -> the index-list entry it reads, or
+// nullptr where the position follows a window or all-visible rule.
+__device__ __forceinline__ const int32_t* slot_entry(const FwdArgs& a, const RowInfo& ri, int row,
+                                                     int k) {
+  if (k < ri.ori_cnt) return a.ori_topk > 0 ? a.ori_idx + (int64_t)row * a.ori_topk + k : nullptr;
+  return a.cmp_topk > 0 ? a.cmp_idx + (int64_t)row * a.cmp_topk + (k - ri.ori_cnt) : nullptr;
+}
+
+// List position k (entry value v where it has one) -> logical row j of its
+// KV (-1: empty or masked slot); *is_cmp tells which KV.
+__device__ __forceinline__ int slot_row(const FwdArgs& a, const RowInfo& ri, int k, int v,
+                                        int* is_cmp) {
+  if (k < ri.ori_cnt) {
+    *is_cmp = 0;
+    if (a.ori_topk <= 0) return ri.ori_lo + k;
+    if (v < 0 || v >= ri.ori_len) return -1;
+    if (a.ori_mode == SFMLA_MASK_CAUSAL && v > ri.p) return -1;
+    if (a.ori_mode == SFMLA_MASK_BAND &&
+        ((a.win_l >= 0 && v < ri.p - a.win_l) || (a.win_r >= 0 && v > ri.p + a.win_r)))
       return -1;
-    }
-    phys = (int64_t)bt[(int64_t)b * bt_cols + blk] * bs + (j - blk * bs);
-  } else {
-    phys = base + j;
+    return v;
   }
-  if (phys < 0 || phys >= pool_rows) {
-    if (status) atomicOr(status, SFMLA_STATUS_ROW_OUT_OF_RANGE);
+  *is_cmp = 1;
+  if (a.cmp_topk <= 0) return k - ri.ori_cnt;
+  if (v < 0 || v >= ri.cmp_limit) return -1;
+  return v;
+}
+
+// PA layout: the block-table entry logical row j lies in (nullptr when the
+// layout is not paged, j < 0, or j is past the table: the last is reported).
+__device__ __forceinline__ const int32_t* table_entry(const FwdArgs& a, const RowInfo& ri, int j,
+                                                      int is_cmp) {
+  if (a.layout_kv != SFMLA_LAYOUT_PA_BSND || j < 0) return nullptr;
+  const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
+  const int cols = is_cmp ? a.cmp_bt_cols : a.ori_bt_cols;
+  const int blk = j / bs;
+  if (blk >= cols) {
+    if (a.status) atomicOr(a.status, SFMLA_STATUS_ROW_OUT_OF_RANGE);
+    return nullptr;
+  }
+  return (is_cmp ? a.cmp_bt : a.ori_bt) + (int64_t)ri.b * cols + blk;
+}
+
+// Logical row j (table entry value e for PA) -> physical row, or -1 when the
+// slot is empty or the row lies outside its pool (reported).
+__device__ __forceinline__ int64_t phys_row(const FwdArgs& a, const RowInfo& ri, int j, int is_cmp,
+                                            bool has_entry, int e) {
+  if (j < 0) return -1;
+  int64_t phys;
+  if (a.layout_kv == SFMLA_LAYOUT_PA_BSND) {
+    if (!has_entry) return -1;                                   // past the table
+    const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
+    phys = (int64_t)e * bs + (j - (j / bs) * bs);
+  } else {
+    phys = (int64_t)(is_cmp ? ri.cmp_base : ri.ori_base) + j;
+  }
+  if (phys < 0 || phys >= (is_cmp ? a.cmp_rows : a.ori_rows)) {
+    if (a.status) atomicOr(a.status, SFMLA_STATUS_ROW_OUT_OF_RANGE);
     return -1;
   }
   return phys;
 }
 
-// List position k of query row `row` -> physical row (or -1 if the slot is
-// empty / masked).  *is_cmp tells which KV the row lives in.
+// One list position, all steps in order (debug dump).
 __device__ __forceinline__ int64_t resolve_pos(const FwdArgs& a, const int32_t* rec, int row,
                                                int k, int* is_cmp) {
-  const int ori_cnt = rec[R_ORI_CNT];
-  const int b = rec[R_B];
-  if (k < ori_cnt) {
-    *is_cmp = 0;
-    int j;
-    if (a.ori_topk > 0) {
-      const int v = a.ori_idx[(int64_t)row * a.ori_topk + k];
-      if (v < 0 || v >= rec[R_ORI_LEN]) return -1;
-      const int p = rec[R_P];
-      if (a.ori_mode == SFMLA_MASK_CAUSAL && v > p) return -1;
-      if (a.ori_mode == SFMLA_MASK_BAND &&
-          ((a.win_l >= 0 && v < p - a.win_l) || (a.win_r >= 0 && v > p + a.win_r)))
-        return -1;
-      j = v;
-    } else {
-      j = rec[R_ORI_LO] + k;
-    }
-    return map_row(a.layout_kv, rec[R_ORI_BASE], a.ori_bs, a.ori_bt_cols, a.ori_bt, b, j,
-                   a.ori_rows, a.status);
-  }
-  *is_cmp = 1;
-  k -= ori_cnt;
-  int j;
-  if (a.cmp_topk > 0) {
-    const int v = a.cmp_idx[(int64_t)row * a.cmp_topk + k];
-    if (v < 0 || v >= rec[R_CMP_LIMIT]) return -1;
-    j = v;
-  } else {
-    j = k;
-  }
-  return map_row(a.layout_kv, rec[R_CMP_BASE], a.cmp_bs, a.cmp_bt_cols, a.cmp_bt, b, j,
-                 a.cmp_rows, a.status);
+  const RowInfo ri = row_info(rec);
+  const int32_t* ep = slot_entry(a, ri, row, k);
+  const int j = slot_row(a, ri, k, ep ? *ep : 0, is_cmp);
+  const int32_t* tp = table_entry(a, ri, j, *is_cmp);
+  return phys_row(a, ri, j, *is_cmp, tp != nullptr, tp ? *tp : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -232,276 +269,8 @@ __device__ __forceinline__ void codes_to_bf16(uint4 c, uint4& lo, uint4& hi) {
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <int DQK, int VMODE, int FMT>
-struct Lds {
-  static constexpr int KSTR = DQK * 2 + 16;   // padded K row (bytes)
-  static constexpr int VSTR = 512 * 2 + 16;   // padded V row (bytes)
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + kTile * KSTR;
-  static constexpr int SC_OFF = V_OFF + (VMODE ? kTile * VSTR : 0);
-  static constexpr int PHYS_OFF = SC_OFF + kTile * 16;
-  static constexpr int SIDE_OFF = PHYS_OFF + kTile * 8;
-  static constexpr int BYTES = SIDE_OFF + kTile * 4;
-};
-
-template <int NW, int DQK, int VMODE, int FMT>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
-  using L = Lds<DQK, VMODE, FMT>;
-  constexpr int NKS = DQK / 32;                 // k-steps of the QK product
-  constexpr int NTHR = NW * 64;
-  extern __shared__ __align__(16) char smem[];
-  char* sK = smem + L::K_OFF;
-  char* sV = VMODE ? smem + L::V_OFF : sK;
-  constexpr int VS = VMODE ? L::VSTR : L::KSTR;
-  float* sScale = (float*)(smem + L::SC_OFF);
-  int64_t* sPhys = (int64_t*)(smem + L::PHYS_OFF);
-  int32_t* sSide = (int32_t*)(smem + L::SIDE_OFF);
-
-  const int row = blockIdx.x, split = blockIdx.y, hg = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int g = l >> 4, t = l & 15;
-  const int h0 = (hg * NW + w) * 16;
-  const int h = h0 + t;
-  const bool wave_on = h0 < a.qn;
-  const bool head_on = h < a.qn;
-
-  if (!plan_matches(a)) {
-    if (split == 0 && head_on && row < a.q_t) {
-      const float nan = __builtin_nanf("");
-      uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
-      for (int c = g; c < 512; c += 4) op[c] = f2bf(nan);
-      if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = nan;
-      if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_METADATA_MISMATCH);
-    }
-    return;
-  }
-  const int32_t* rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
-  const int nsplit = rec[R_NSPLIT];
-  if (split >= nsplit) return;
-  const int n = rec[R_NTOTAL];
-  const int chunk = rec[R_CHUNK];
-  const int k0 = split * chunk;
-  const int k1 = min(n, k0 + chunk);
-
-  // this lane's slice of Q: B operand (k = d, n = head)
-  bf16x8 qreg[NKS];
-  {
-    const uint16_t* qp = a.q + ((int64_t)row * a.qn + (head_on ? h : 0)) * DQK + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 v = head_on ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
-      qreg[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  f32x4 o[32];
-#pragma unroll
-  for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;
-  float l_run = 0.f;
-
-  for (int t0 = k0; t0 < k1; t0 += kTile) {
-    // ---- resolve this tile's list positions
-    if (tid < kTile) {
-      const int k = t0 + tid;
-      int side = 0;
-      int64_t phys = -1;
-      if (k < k1) phys = resolve_pos(a, rec, row, k, &side);
-      sPhys[tid] = phys;
-      sSide[tid] = side;
-    }
-    __syncthreads();
-
-    // ---- gather the rows into LDS (16 bytes per thread per step)
-    if constexpr (FMT == SFMLA_KV_BF16) {
-      constexpr int CK = 64 + (DQK - 512) / 8;          // K chunks per row
-      constexpr int CH = CK + (VMODE ? 64 : 0);
-      for (int c = tid; c < kTile * CH; c += NTHR) {
-        const int r = c / CH, cc = c - r * CH;
-        const int64_t phys = sPhys[r];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        char* dst;
-        if (cc < 64) dst = sK + r * L::KSTR + cc * 16;
-        else if (cc < CK) dst = sK + r * L::KSTR + 1024 + (cc - 64) * 16;
-        else dst = sV + r * L::VSTR + (cc - CK) * 16;
-        if (phys >= 0) {
-          const int side = sSide[r];
-          const char* kbase = side ? a.cmp_kv + phys * a.cmp_stride : a.ori_kv + phys * a.ori_stride;
-          const char* src;
-          if (cc < 64) {
-            src = kbase + cc * 16;
-          } else if (cc < CK) {
-            const char* rp = side ? a.cmp_rope : a.ori_rope;
-            const int64_t rs = side ? a.cmp_rope_stride : a.ori_rope_stride;
-            src = (rp ? rp + phys * rs : kbase + 1024) + (cc - 64) * 16;
-          } else {
-            src = (side || !a.ori_v ? kbase : a.ori_v + phys * a.ori_v_stride) + (cc - CK) * 16;
-          }
-          v = *(const uint4*)src;
-        }
-        *(uint4*)dst = v;
-      }
-    } else {
-      constexpr int CR = (DQK - 512) / 8;               // rope chunks
-      constexpr int CH = 32 + CR + 1;
-      for (int c = tid; c < kTile * CH; c += NTHR) {
-        const int r = c / CH, cc = c - r * CH;
-        const int64_t phys = sPhys[r];
-        const char* rowp = nullptr;
-        if (phys >= 0)
-          rowp = sSide[r] ? a.cmp_kv + phys * a.cmp_stride : a.ori_kv + phys * a.ori_stride;
-        if (cc < 32) {
-          uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-          if (rowp) codes_to_bf16<FMT>(*(const uint4*)(rowp + cc * 16), lo, hi);
-          *(uint4*)(sK + r * L::KSTR + cc * 32) = lo;
-          *(uint4*)(sK + r * L::KSTR + cc * 32 + 16) = hi;
-        } else if (cc < 32 + CR) {
-          uint4 v = rowp ? *(const uint4*)(rowp + 512 + (cc - 32) * 16) : make_uint4(0, 0, 0, 0);
-          *(uint4*)(sK + r * L::KSTR + 1024 + (cc - 32) * 16) = v;
-        } else {
-          uint4 v = rowp ? *(const uint4*)(rowp + 512 + 2 * (DQK - 512)) : make_uint4(0, 0, 0, 0);
-          *(uint4*)(sScale + r * 4) = v;
-        }
-      }
-    }
-    __syncthreads();
-
-    if (wave_on) {
-      // ---- S^T = K Q^T : two 16-row blocks, M = rows, N = heads, K = d
-      f32x4 s[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const char* kp = sK + (rb * 16 + t) * L::KSTR + 16 * g;
-        if constexpr (FMT == SFMLA_KV_BF16) {
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            bf16x8 kv = *(const bf16x8*)(kp + 64 * ks);
-            s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qreg[ks], s[rb], 0, 0, 0);
-          }
-        } else {
-          // per-128-dim tile partial sums, scaled by that tile's fp32 scale
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              bf16x8 kv = *(const bf16x8*)(kp + 64 * (4 * t4 + kk));
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qreg[4 * t4 + kk], acc, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              s[rb][i] += acc[i] * sScale[(rb * 16 + 4 * g + i) * 4 + t4];
-          }
-#pragma unroll
-          for (int ks = 16; ks < NKS; ++ks) {
-            bf16x8 kv = *(const bf16x8*)(kp + 64 * ks);
-            s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qreg[ks], s[rb], 0, 0, 0);
-          }
-        }
-      }
-
-      // ---- online softmax (log2 domain); lane holds head t, rows
-      //      {4g+i, 16+4g+i}, i < 4
-      float x[8];
-      float mx = kNegInf;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = sPhys[rb * 16 + 4 * g + i] >= 0;
-          const float v = ok ? s[rb][i] * a.scale_log2 : kNegInf;
-          x[rb * 4 + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float p[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
-        psum += p[j];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int mb = 0; mb < 32; ++mb) o[mb] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T : M = 16 value columns per block, N = heads,
-      //      K = 32 rows with k = 8g+i <-> row (i<4 ? 4g+i : 16+4g+i-4)
-      const char* vp = sV + (4 * g + (t >> 2)) * VS + 8 * (t & 3);
-      if constexpr (FMT == SFMLA_KV_BF16) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-#pragma unroll
-        for (int mb = 0; mb < 32; ++mb) {
-          s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * mb));
-          s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * VS + 32 * mb));
-          bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[mb], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          bf16x8 pb;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int rr = (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4);
-            pb[j] = (__bf16)(p[j] * sScale[rr * 4 + t4]);
-          }
-#pragma unroll
-          for (int mb = 8 * t4; mb < 8 * t4 + 8; ++mb) {
-            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * mb));
-            s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * VS + 32 * mb));
-            bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[mb], 0, 0, 0);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  if (!wave_on) return;
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt += __shfl_xor(lt, 32);
-  if (!head_on) return;
-  const float lse2 = lt > 0.f ? m_run + __builtin_log2f(lt) : kNegInf;  // log2 units
-  if (nsplit == 1) {
-    float den = lt;
-    if (a.has_sinks && lt > 0.f) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - m_run);
-    const float inv = lt > 0.f ? 1.f / den : 0.f;
-    uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512 + 4 * g;
-#pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
-      uint2 pk;
-      pk.x = (uint32_t)f2bf(o[mb][0] * inv) | ((uint32_t)f2bf(o[mb][1] * inv) << 16);
-      pk.y = (uint32_t)f2bf(o[mb][2] * inv) | ((uint32_t)f2bf(o[mb][3] * inv) << 16);
-      *(uint2*)(op + 16 * mb) = pk;
-    }
-    if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = lt > 0.f ? lse2 * kLn2 : kNegInf;
-  } else {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int64_t slot = ((int64_t)row * a.max_splits + split) * a.qn + h;
-    float* wp = a.ws_o + slot * 512 + 4 * g;
-#pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
-      float4 v = make_float4(o[mb][0] * inv, o[mb][1] * inv, o[mb][2] * inv, o[mb][3] * inv);
-      *(float4*)(wp + 16 * mb) = v;
-    }
-    if (g == 0) a.ws_lse[slot] = lt > 0.f ? lse2 * kLn2 : kNegInf;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// forward, bf16 KV: pipelined gather with direct global -> LDS loads
+// forward: pipelined gather with direct global -> LDS loads
 // ---------------------------------------------------------------------------
 //
 // The split's list positions are resolved once into LDS.  KV tiles of 32 rows
@@ -541,6 +310,23 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
                :
                : "v"(g), "s"(lds_addr)
                : "memory", "m0");
+}
+
+// The same with a uniform row address in an SGPR pair (lane offset in a
+// VGPR).  s_nop 4 gives the five wait states a VMEM instruction needs after a
+// VALU write (v_readlane) of an SGPR it reads, which also covers the M0 write.
+__device__ __forceinline__ void dma16_s(uint64_t base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// 64-bit value held by lane j, as a uniform (SGPR) value.
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int j) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, j);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), j);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // After an explicit full vmcnt wait: make an empty asm the last writer of
@@ -600,27 +386,32 @@ struct Pipe {
 // K side of one tile: 512 nope values per row (1 KB per wave instruction) and,
 // with rope, 8 rows of 64 rope values per instruction (row r's 16-byte chunk c
 // lands at position c ^ ((r >> 1) & 7) of its 128-byte LDS row, which keeps
-// the 16-row reads conflict-free).
+// the 16-row reads conflict-free).  All row addresses of the wave's share are
+// read from LDS before the first load is issued (the loads' "memory" clobber
+// would otherwise serialise one LDS round trip per load): nope rows with one
+// read (lane j holds row j, handed out with v_readlane), rope rows per lane.
 template <int NW, int DQK, int VMODE>
 __device__ __forceinline__ void issue_k(const uint64_t* sAK, const uint64_t* sAR, int tbase,
                                         uint32_t ldsK, int w, int l) {
   using C = Pipe<NW, DQK, VMODE>;
   const uint32_t wk = __builtin_amdgcn_readfirstlane(ldsK + w * C::NR * C::RSTR);
+  const uint64_t mine = sAK[tbase + w * C::NR + (l < C::NR ? l : 0)];
+  const char* rsrc[C::ROPE ? C::ROPE_INSTR : 1];
+  if constexpr (C::ROPE) {
 #pragma unroll
-  for (int j = 0; j < C::NR; ++j) {
-    const int r = w * C::NR + j;
-    dma16((const char*)sAK[tbase + r] + l * 16, wk + j * C::RSTR);
+    for (int q = 0; q < C::ROPE_INSTR; ++q) {
+      const int rr = w * C::NR + 8 * q + ((l >> 3) < C::NR ? (l >> 3) : 0);
+      const int chunk = (l & 7) ^ ((rr >> 1) & 7);
+      rsrc[q] = (const char*)sAR[tbase + rr] + chunk * 16;
+    }
   }
+#pragma unroll
+  for (int j = 0; j < C::NR; ++j) dma16_s(readlane64(mine, j), l * 16, wk + j * C::RSTR);
   if constexpr (C::ROPE) {
     const uint32_t wr = __builtin_amdgcn_readfirstlane(ldsK + kTile * C::RSTR + w * C::NR * 128);
 #pragma unroll
-    for (int q = 0; q < C::ROPE_INSTR; ++q) {
-      const int rr = w * C::NR + 8 * q + (l >> 3);
-      if (C::NR >= 8 || (l >> 3) < C::NR) {
-        const int chunk = (l & 7) ^ ((rr >> 1) & 7);
-        dma16((const char*)sAR[tbase + rr] + chunk * 16, wr + q * 1024);
-      }
-    }
+    for (int q = 0; q < C::ROPE_INSTR; ++q)
+      if (C::NR >= 8 || (l >> 3) < C::NR) dma16(rsrc[q], wr + q * 1024);
   }
 }
 
@@ -629,10 +420,89 @@ __device__ __forceinline__ void issue_v(const uint64_t* sAV, int tbase, uint32_t
                                         int l) {
   using C = Pipe<NW, DQK, VMODE>;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(ldsV + w * C::NR * C::RSTR);
+  const uint64_t mine = sAV[tbase + w * C::NR + (l < C::NR ? l : 0)];
 #pragma unroll
-  for (int j = 0; j < C::NR; ++j) {
-    const int r = w * C::NR + j;
-    dma16((const char*)sAV[tbase + r] + l * 16, wv + j * C::RSTR);
+  for (int j = 0; j < C::NR; ++j) dma16_s(readlane64(mine, j), l * 16, wv + j * C::RSTR);
+}
+
+// Packed rows (512 INT8 / FP8-E4M3 codes, the bf16 rope, four fp32 scales of
+// 128 columns each) are gathered as raw bytes: tile rows lie back to back in
+// the LDS stage (row stride = the packed row size), each wave instruction
+// moving 64 consecutive 16-byte chunks, which may span several rows.  Padding
+// lanes (past the tile) read the zero row into the stage's tail so that every
+// wave issues the same number of loads.
+template <int NW, int DQK>
+struct PackedPipe {
+  static constexpr int ROPE = DQK - 512;                     // rope values per row
+  static constexpr int CPR = (512 + 2 * ROPE + 16) / 16;      // 16-byte chunks per row
+  static constexpr int NI = (kTile * CPR + 63) / 64;          // instructions per tile
+  static constexpr int PER = (NI + NW - 1) / NW;              // per wave
+  static constexpr int RAWB = PER * NW * 1024;                // LDS bytes per stage
+};
+
+template <int NW, int DQK>
+__device__ __forceinline__ void issue_raw(const uint64_t* sAK, int tbase, uint32_t ldsRaw, int w,
+                                          int l) {
+  using P = PackedPipe<NW, DQK>;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(ldsRaw + w * P::PER * 1024);
+  constexpr int B = 8;                                        // addresses read per batch
+#pragma unroll
+  for (int q0 = 0; q0 < P::PER; q0 += B) {
+    const char* src[B];
+#pragma unroll
+    for (int q = q0; q < q0 + B && q < P::PER; ++q) {
+      const int c = (w * P::PER + q) * 64 + l;                // chunk index in the tile
+      const int r = c < kTile * P::CPR ? c / P::CPR : 0;
+      const char* rowp = (const char*)sAK[tbase + r];
+      src[q - q0] = c < kTile * P::CPR ? rowp + 16 * (c - r * P::CPR) : (const char*)g_zero_row;
+    }
+#pragma unroll
+    for (int q = q0; q < q0 + B && q < P::PER; ++q) dma16(src[q - q0], base + q * 1024);
+  }
+}
+
+// Raw packed tile -> the bf16 K tile the MFMA path reads (codes decoded
+// exactly; rope copied into its swizzled region) and the tile's scales,
+// stored scale-tile major: sScale[32 * j + row] for columns [128 j, 128 j + 128).
+template <int NW, int DQK, int FMT>
+__device__ __forceinline__ void decode_tile(const char* raw, char* kbf, float* sScale, int tid) {
+  using P = PackedPipe<NW, DQK>;
+  constexpr int NTHR = NW * 64;
+  constexpr int RB = P::CPR * 16;
+  constexpr int RS = 1024 + 32;
+  constexpr int NIT = kTile * 32 / NTHR;          // 16-code chunks per thread
+  constexpr int U = NIT < 4 ? NIT : 4;            // chunks read before any is converted
+  static_assert(kTile * 32 % NTHR == 0 && NIT % U == 0, "decode split");
+#pragma unroll
+  for (int i0 = 0; i0 < NIT; i0 += U) {
+    uint4 c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = tid + (i0 + u) * NTHR;
+      c[u] = *(const uint4*)(raw + (i >> 5) * RB + 16 * (i & 31));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = tid + (i0 + u) * NTHR;
+      uint4 lo, hi;
+      codes_to_bf16<FMT>(c[u], lo, hi);
+      *(uint4*)(kbf + (i >> 5) * RS + 32 * (i & 31)) = lo;
+      *(uint4*)(kbf + (i >> 5) * RS + 32 * (i & 31) + 16) = hi;
+    }
+  }
+  if constexpr (P::ROPE > 0) {
+    for (int i = tid; i < kTile * 8; i += NTHR) {
+      const int r = i >> 3, c = i & 7;
+      *(uint4*)(kbf + kTile * RS + r * 128 + 16 * (c ^ ((r >> 1) & 7))) =
+          *(const uint4*)(raw + r * RB + 512 + 16 * c);
+    }
+  }
+  for (int i = tid; i < kTile; i += NTHR) {
+    const float4 sc = *(const float4*)(raw + i * RB + 512 + 2 * P::ROPE);
+    sScale[i] = sc.x;
+    sScale[kTile + i] = sc.y;
+    sScale[2 * kTile + i] = sc.z;
+    sScale[3 * kTile + i] = sc.w;
   }
 }
 
@@ -643,23 +513,32 @@ __device__ __forceinline__ void issue_v(const uint64_t* sAV, int tbase, uint32_t
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kMergeSplits = 4;       // splits whose partials one merge round loads
 
-// HB head blocks of 16 heads per wave.
-template <int NW, int HB, int DQK, int VMODE>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+// HB head blocks of 16 heads per wave; FMT is the KV storage format.
+template <int NW, int HB, int DQK, int VMODE, int FMT>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   using C = Pipe<NW, DQK, VMODE>;
+  using PP = PackedPipe<NW, DQK>;
+  constexpr bool PK = FMT != SFMLA_KV_BF16;       // packed rows (V = decoded nope)
+  static_assert(!PK || VMODE == 0, "packed KV has no separate V");
+  constexpr bool BROPE = C::ROPE && !PK;          // rope gathered from its own address
   constexpr int T = C::T;
   constexpr int NKS = DQK / 32;
   constexpr int NTHR = NW * 64;
   constexpr int HPW = 16 * HB;                     // heads per wave
   constexpr int RS = C::RSTR;
-  // separate V: two K stages and two V stages; aliased V: three K stages
+  // bf16, separate V: two K stages and two V stages; bf16, aliased V: three K
+  // stages; packed: three raw stages and one decoded K tile (sK0)
   __shared__ __align__(16) char sK0[C::KBYTES];
-  __shared__ __align__(16) char sK1[C::KBYTES];
-  __shared__ __align__(16) char sK2[VMODE ? 16 : C::KBYTES];
+  __shared__ __align__(16) char sK1[PK ? 16 : C::KBYTES];
+  __shared__ __align__(16) char sK2[(VMODE || PK) ? 16 : C::KBYTES];
   __shared__ __align__(16) char sV0[VMODE ? T * RS : 16];
   __shared__ __align__(16) char sV1[VMODE ? T * RS : 16];
+  __shared__ __align__(16) char sW0[PK ? PP::RAWB : 16];
+  __shared__ __align__(16) char sW1[PK ? PP::RAWB : 16];
+  __shared__ __align__(16) char sW2[PK ? PP::RAWB : 16];
+  __shared__ __align__(16) float sScale[PK ? 4 * T : 4];
   __shared__ uint64_t sAK[kSplitRows + T];
-  __shared__ uint64_t sAR[C::ROPE ? kSplitRows + T : 1];
+  __shared__ uint64_t sAR[BROPE ? kSplitRows + T : 1];
   __shared__ uint64_t sAV[VMODE ? kSplitRows + T : 1];
   __shared__ uint8_t sValid[kSplitRows + T];
 
@@ -674,8 +553,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   const int row = unit / a.max_splits, split = unit - row * a.max_splits;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g = l >> 4, t = l & 15;
-  const int h0 = (hg * NW + w) * HPW;              // first head of this wave
-  const bool wave_on = h0 < a.qn;
+  // a head group holds a.bpg 16-head blocks; waves past them only gather
+  const int h0 = (hg * a.bpg + w) * HPW;           // first head of this wave
+  const bool wave_on = w < a.bpg && h0 < a.qn;
 
   if (!plan_matches(a)) {
     if (split == 0) {
@@ -683,7 +563,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         const int h = h0 + 16 * hb + t;
-        if (h >= a.qn) continue;
+        if (!wave_on || h >= a.qn) continue;
         uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
         for (int c = g; c < 512; c += 4) op[c] = f2bf(nan);
         if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = nan;
@@ -703,7 +583,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         const int h = h0 + 16 * hb + t;
-        if (h >= a.qn) continue;
+        if (!wave_on || h >= a.qn) continue;
         uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
         for (int c = g; c < 512; c += 4) op[c] = f2bf(__builtin_nanf(""));
         if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = __builtin_nanf("");
@@ -716,15 +596,57 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   const int k1 = min(n, k0 + chunk);
   const int nt = (k1 - k0 + T - 1) / T;
 
+  // Q slices (B operand: k = d, n = head), loaded first: they travel while
+  // the list positions resolve, and waiting for them never waits for KV tiles
+  bf16x8 qreg[HB][NKS];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = h0 + 16 * hb + t;
+    const bool on = wave_on && h < a.qn;
+    const uint16_t* qp = a.q + ((int64_t)row * a.qn + (on ? h : 0)) * DQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 v = on ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+      qreg[hb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
   // ---- resolve every list position of this split once, into row addresses
-  //      (empty or masked slots read a zero row)
+  //      (empty or masked slots read a zero row).  Each thread takes up to
+  //      PPT positions; the index loads of all of them, then the table loads
+  //      of all of them, are in flight together.
   {
+    constexpr int PPT = (kSplitRows + T + NTHR - 1) / NTHR;
     const char* zero = (const char*)g_zero_row;
-    for (int i = tid; i < nt * T; i += NTHR) {
-      const int k = k0 + i;
-      int side = 0;
-      int64_t phys = -1;
-      if (k < k1) phys = resolve_pos(a, rec, row, k, &side);
+    const RowInfo ri = row_info(rec);
+    const int ntT = nt * T;
+    int vv[PPT], jj[PPT], sd[PPT], ee[PPT];
+    bool he[PPT];
+    // loads are unconditional (a position without an entry reads its own
+    // plan record) so that no branch join waits for one before the next issues
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int k = k0 + tid + u * NTHR;
+      const int32_t* ep = (tid + u * NTHR < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
+      vv[u] = *(ep ? ep : rec);
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int k = k0 + tid + u * NTHR;
+      sd[u] = 0;
+      jj[u] = (tid + u * NTHR < ntT && k < k1) ? slot_row(a, ri, k, vv[u], &sd[u]) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int32_t* tp = table_entry(a, ri, jj[u], sd[u]);
+      he[u] = tp != nullptr;
+      ee[u] = *(tp ? tp : rec);
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = tid + u * NTHR;
+      if (i >= ntT) break;
+      const int side = sd[u];
+      const int64_t phys = phys_row(a, ri, jj[u], side, he[u], ee[u]);
       const char* ka = zero;
       const char* va = zero;
       const char* ra = zero;
@@ -735,23 +657,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         ra = rp ? rp + phys * (side ? a.cmp_rope_stride : a.ori_rope_stride) : ka + 1024;
       }
       sAK[i] = (uint64_t)ka;
-      if constexpr (C::ROPE) sAR[i] = (uint64_t)ra;
+      if constexpr (BROPE) sAR[i] = (uint64_t)ra;
       if constexpr (VMODE) sAV[i] = (uint64_t)va;
       sValid[i] = phys >= 0;
-    }
-  }
-  // Q slices (B operand: k = d, n = head), loaded before the first gathers so
-  // that waiting for them never waits for KV tiles
-  bf16x8 qreg[HB][NKS];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int h = h0 + 16 * hb + t;
-    const bool on = h < a.qn;
-    const uint16_t* qp = a.q + ((int64_t)row * a.qn + (on ? h : 0)) * DQK + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 v = on ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
-      qreg[hb][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
   wait_lgkm0();
@@ -766,6 +674,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) { m_run[hb] = kNegInf; l_run[hb] = 0.f; }
   bf16x8 pb[HB];
+  bf16x8 pbt[PK ? 4 : 1][HB];     // packed: P times the rows' scales, per 128 value columns
 
   // ---- S^T = K Q^T, online softmax -> pb (M = 16 rows, N = 16 heads per MFMA).
   // The operands of the next PF k-steps are in flight while step ks
@@ -778,8 +687,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       valid[i] = sValid[tbase + 4 * g + i];
       valid[4 + i] = sValid[tbase + 16 + 4 * g + i];
     }
+    // packed: the scales of this lane's rows (4g+i and 16+4g+i), per tile
+    f32x4 sc[PK ? 4 : 1][2];
+    if constexpr (PK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sc[j][0] = *(const f32x4*)(sScale + j * T + 4 * g);
+        sc[j][1] = *(const f32x4*)(sScale + j * T + 16 + 4 * g);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 s[HB][2];
+    f32x4 s[HB][2], sp[HB][2];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const char* kp0 = sK + t * RS + 16 * g;
@@ -804,8 +722,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       const bf16x8 k0v = kb[ks % PF][0], k1v = kb[ks % PF][1];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qreg[hb][ks], s[hb][0], 0, 0, 0);
-        s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qreg[hb][ks], s[hb][1], 0, 0, 0);
+        if (PK && ks < 16) {
+          // exact scaling: one partial product per 128-column scale tile
+          const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+          sp[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qreg[hb][ks],
+                                                              ks % 4 ? sp[hb][0] : z, 0, 0, 0);
+          sp[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qreg[hb][ks],
+                                                              ks % 4 ? sp[hb][1] : z, 0, 0, 0);
+          if (ks % 4 == 3) {
+            s[hb][0] += sp[hb][0] * sc[PK ? ks / 4 : 0][0];
+            s[hb][1] += sp[hb][1] * sc[PK ? ks / 4 : 0][1];
+          }
+        } else {
+          s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qreg[hb][ks], s[hb][0], 0, 0, 0);
+          s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qreg[hb][ks], s[hb][1], 0, 0, 0);
+        }
       }
       if (ks + PF < NKS) kload(ks + PF, kb[ks % PF][0], kb[ks % PF][1]);
     }
@@ -835,7 +766,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       for (int j = 0; j < 8; ++j) {
         const float pj = __builtin_amdgcn_exp2f(x[j] - m_use);
         psum += pj;
-        pb[hb][j] = (__bf16)pj;
+        if constexpr (PK) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pbt[u][hb][j] = (__bf16)(pj * sc[PK ? u : 0][j >> 2][j & 3]);
+        } else {
+          pb[hb][j] = (__bf16)pj;
+        }
       }
       l_run[hb] = l_run[hb] * alpha[hb] + psum;
     }
@@ -867,13 +803,38 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
           bf16x8, __builtin_shufflevector(vb[mb % PV][0], vb[mb % PV][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
-        o[hb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hb], o[hb][mb], 0, 0, 0);
+        o[hb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, PK ? pbt[PK ? mb >> 3 : 0][hb] : pb[hb],
+                                                            o[hb][mb], 0, 0, 0);
       if (mb + PV < 32) vload(mb + PV, vb[mb % PV][0], vb[mb % PV][1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if constexpr (VMODE) {
+  if constexpr (PK) {
+    // raw stages W0..W2 (two tiles in flight); the decoded tile lives in sK0
+    auto step = [&](int tt, char* sWc, char* sWn2) {
+      if (tt + 1 < nt) wait_vmcnt<PP::PER>(); else wait_vmcnt<0>();   // raw(tt) landed
+      wait_lgkm0();
+      block_barrier();                          // ... and tile tt-1 is consumed
+      if (tt + 2 < nt) issue_raw<NW, DQK>(sAK, (tt + 2) * T, lds_addr(sWn2), w, l);
+      decode_tile<NW, DQK, FMT>(sWc, sK0, sScale, tid);
+      wait_lgkm0();
+      block_barrier();                          // decoded tile complete
+      if (wave_on) {
+        qk_softmax(sK0, tt * T);
+        pv(sK0);
+      }
+    };
+    if (nt > 0) issue_raw<NW, DQK>(sAK, 0, lds_addr(sW0), w, l);
+    wait_vmcnt<0>();                            // raw(0) and the Q slices
+    settle(qreg);
+    if (nt > 1) issue_raw<NW, DQK>(sAK, T, lds_addr(sW1), w, l);
+    for (int tt = 0; tt < nt; tt += 3) {
+      step(tt, sW0, sW2);
+      if (tt + 1 < nt) step(tt + 1, sW1, sW0);
+      if (tt + 2 < nt) step(tt + 2, sW2, sW1);
+    }
+  } else if constexpr (VMODE) {
     // K(t+2) streams in from the end of QK(t); V(t+1) from the start of QK(t).
     auto step = [&](int tt, char* sKc, char* sVc, char* sVn) {
       if (tt + 1 < nt) wait_vmcnt<C::NV + C::NK>(); else wait_vmcnt<C::NV>();   // K(tt) landed
@@ -973,7 +934,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc((char*)a.ws_ob + row * row_bytes, row_bytes);
   const int wave_off = ((split * a.groups + hg) * NW + w) * WAVE_BYTES;
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
+  for (int hb = 0; hb < HB && wave_on; ++hb) {       // loader-only waves have no partial
     const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -987,7 +948,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       const u32x4 d = {pk.x, pk.y, pk.z, pk.w};
       __builtin_amdgcn_raw_buffer_store_b128(d, rs, wave_off + ((hb * 16 + j) * 64 + l) * 16, 0, kSc1);
     }
-    if (g == 0) st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
+    if (g == 0)
+      st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
   }
   drain_vmem();                                     // this wave's partial is stored
   __shared__ int sLast;
@@ -1186,72 +1148,37 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t forward_lds_bytes(int dqk, int vmode, int /*fmt*/) {
-  if (dqk == 512) return vmode ? Lds<512, 1, 0>::BYTES : Lds<512, 0, 0>::BYTES;
-  return vmode ? Lds<576, 1, 0>::BYTES : Lds<576, 0, 0>::BYTES;
-}
-
 template <int NW, int DQK, int VMODE, int FMT>
 static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s) {
-  const size_t lds = Lds<DQK, VMODE, FMT>::BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_kernel<NW, DQK, VMODE, FMT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((fwd_kernel<NW, DQK, VMODE, FMT>), dim3(a.q_t, a.max_splits, groups),
-                     dim3(NW * 64), lds, s, a);
-  return hipGetLastError();
-}
-
-template <int NW, int HB, int DQK, int VMODE>
-static hipError_t launch_bf16_t(const FwdArgs& a, int groups, hipStream_t s) {
   FwdArgs b = a;
   b.groups = groups;
+  if (b.bpg < 1 || b.bpg > NW) return hipErrorInvalidConfiguration;
   const int64_t units = (int64_t)a.q_t * a.max_splits;
   const int64_t blocks = (units + 7) / 8 * 8 * groups;
-  hipLaunchKernelGGL((fwd_bf16_kernel<NW, HB, DQK, VMODE>), dim3((unsigned)blocks), dim3(NW * 64),
-                     0, s, b);
+  hipLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                     s, b);
   return hipGetLastError();
 }
 
-template <int NW, int HB>
-static hipError_t launch_bf16_nw(const FwdArgs& a, int dqk, int vmode, int groups,
-                                 hipStream_t s) {
-  if (dqk == 512) return vmode ? launch_bf16_t<NW, HB, 512, 1>(a, groups, s)
-                               : launch_bf16_t<NW, HB, 512, 0>(a, groups, s);
-  return vmode ? launch_bf16_t<NW, HB, 576, 1>(a, groups, s)
-               : launch_bf16_t<NW, HB, 576, 0>(a, groups, s);
-}
-
-template <int NW>
-static hipError_t launch_fwd_nw(const FwdArgs& a, int dqk, int vmode, int fmt, int groups,
-                                hipStream_t s) {
-  if (fmt == SFMLA_KV_INT8_PACKED)
-    return dqk == 512 ? launch_fwd_t<NW, 512, 0, 1>(a, groups, s)
-                      : launch_fwd_t<NW, 576, 0, 1>(a, groups, s);
-  return dqk == 512 ? launch_fwd_t<NW, 512, 0, 2>(a, groups, s)
-                    : launch_fwd_t<NW, 576, 0, 2>(a, groups, s);
-}
-
-hipError_t launch_forward(const FwdArgs& a, int nw, int hb, int dqk, int vmode, int fmt,
-                          int groups, hipStream_t s) {
-  if (fmt == SFMLA_KV_BF16) {
-    (void)hb;   // one 16-head block per wave (two would not fit the register file)
-    switch (nw) {
-      case 1: return launch_bf16_nw<1, 1>(a, dqk, vmode, groups, s);
-      case 2: return launch_bf16_nw<2, 1>(a, dqk, vmode, groups, s);
-      case 4: return launch_bf16_nw<4, 1>(a, dqk, vmode, groups, s);
-      default: return launch_bf16_nw<8, 1>(a, dqk, vmode, groups, s);
-    }
-  }
-  switch (nw) {
-    case 1: return launch_fwd_nw<1>(a, dqk, vmode, fmt, groups, s);
-    case 2: return launch_fwd_nw<2>(a, dqk, vmode, fmt, groups, s);
-    case 4: return launch_fwd_nw<4>(a, dqk, vmode, fmt, groups, s);
-    default: return launch_fwd_nw<8>(a, dqk, vmode, fmt, groups, s);
+// Eight waves per workgroup for bf16 rows; four for packed rows, whose
+// decode needs more registers per wave.
+hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
+                          hipStream_t s) {
+  switch (fmt) {
+    case SFMLA_KV_INT8_PACKED:
+      if (nw != 4) return hipErrorInvalidConfiguration;
+      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_INT8_PACKED>(a, groups, s)
+                        : launch_fwd_t<4, 576, 0, SFMLA_KV_INT8_PACKED>(a, groups, s);
+    case SFMLA_KV_FP8_E4M3_PACKED:
+      if (nw != 4) return hipErrorInvalidConfiguration;
+      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s)
+                        : launch_fwd_t<4, 576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s);
+    default:
+      if (nw != 8) return hipErrorInvalidConfiguration;
+      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, 0>(a, groups, s)
+                                   : launch_fwd_t<8, 512, 0, 0>(a, groups, s);
+      return vmode ? launch_fwd_t<8, 576, 1, 0>(a, groups, s)
+                   : launch_fwd_t<8, 576, 0, 0>(a, groups, s);
   }
 }
 
