@@ -963,33 +963,54 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     __hip_atomic_store(&a.counters[(int64_t)row * kCounterInts + hg], 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   if (!wave_on) return;
-  // merge from the stored partials (this split's own included).  Loads are
-  // issued in rounds of kMergeSplits splits x JB column blocks so that each
-  // wave keeps 16 independent 16-B loads in flight.
-  constexpr int MS = kMergeSplits, JB = 4;
+  // merge from the stored partials (this split's own included).  Round r
+  // loads column blocks [JB*(r / ns4), +JB) of kMergeSplits splits (16 loads
+  // of 16 bytes per lane in flight); the first round travels together with
+  // the loads of the LSEs, which give the max and the normaliser in one pass.
+  constexpr int MS = kMergeSplits, JB = 4, NJ = 16 / JB;
+  const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
+  const int R = NJ * ns4;                               // load rounds
+  const int split_bytes = a.groups * NW * WAVE_BYTES;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int h = h0 + 16 * hb + t;
     const float* lp = a.ws_lse + (int64_t)row * a.max_splits * HP + h;
-    float M = kNegInf;
+    const int off0 = (hg * NW + w) * WAVE_BYTES + ((hb * 16) * 64 + l) * 16;   // split 0
+    u32x4 v[MS][JB];
+    float wl[MS];
+    auto issue = [&](int r) {
+      const int jr = r / ns4, s0 = (r - jr * ns4) * MS;
+#pragma unroll
+      for (int q = 0; q < MS; ++q) {
+        const int s2 = min(s0 + q, nsplit - 1);
+        wl[q] = ld_agent(lp + (int64_t)s2 * HP);
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+          v[q][j] = __builtin_amdgcn_raw_buffer_load_b128(
+              rs, off0 + s2 * split_bytes + (jr * JB + j) * 64 * 16, 0, kSc1);
+      }
+    };
+    issue(0);
+    // max and normaliser over every split's LSE (the first chunk is wl)
+    float M = kNegInf, tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < MS; ++q)
+      if (q < nsplit) M = fmaxf(M, wl[q]);
 #pragma unroll 1
-    for (int s0 = 0; s0 < nsplit; s0 += MS) {
-      float v[MS];
-#pragma unroll
-      for (int q = 0; q < MS; ++q) v[q] = ld_agent(lp + (int64_t)min(s0 + q, nsplit - 1) * HP);
-#pragma unroll
-      for (int q = 0; q < MS; ++q) M = fmaxf(M, v[q]);
-    }
-    const float Mu = M == kNegInf ? 0.f : M;
-    float tot = 0.f;
-#pragma unroll 1
-    for (int s0 = 0; s0 < nsplit; s0 += MS) {
-      float v[MS];
-#pragma unroll
-      for (int q = 0; q < MS; ++q) v[q] = ld_agent(lp + (int64_t)min(s0 + q, nsplit - 1) * HP);
+    for (int s0 = MS; s0 < nsplit; s0 += MS) {
 #pragma unroll
       for (int q = 0; q < MS; ++q)
-        if (s0 + q < nsplit) tot += __builtin_amdgcn_exp2f(v[q] - Mu);
+        if (s0 + q < nsplit) M = fmaxf(M, ld_agent(lp + (int64_t)(s0 + q) * HP));
+    }
+    const float Mu = M == kNegInf ? 0.f : M;
+#pragma unroll
+    for (int q = 0; q < MS; ++q)
+      if (q < nsplit) tot += __builtin_amdgcn_exp2f(wl[q] - Mu);
+#pragma unroll 1
+    for (int s0 = MS; s0 < nsplit; s0 += MS) {
+#pragma unroll
+      for (int q = 0; q < MS; ++q)
+        if (s0 + q < nsplit) tot += __builtin_amdgcn_exp2f(ld_agent(lp + (int64_t)(s0 + q) * HP) - Mu);
     }
     float den = tot;
     if (a.has_sinks && h < a.qn && tot > 0.f)
@@ -997,46 +1018,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     const float inv = tot > 0.f ? 1.f / den : 0.f;
     const bool on = h < a.qn;
     uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g;
-    const int off0 = (hg * NW + w) * WAVE_BYTES + ((hb * 16) * 64 + l) * 16;   // split 0
-    const int split_bytes = a.groups * NW * WAVE_BYTES;
+    float acc[JB][8];
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
 #pragma unroll 1
-    for (int jh = 0; jh < 16 / JB; ++jh) {
-      float acc[JB][8];
+    for (int r = 0; r < R; ++r) {
+      if (r > 0) issue(r);
+      const int jr = r / ns4, s0 = (r - jr * ns4) * MS;
 #pragma unroll
-      for (int j = 0; j < JB; ++j)
+      for (int q = 0; q < MS; ++q) {
+        const float ws = s0 + q < nsplit ? __builtin_amdgcn_exp2f(wl[q] - Mu) : 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-#pragma unroll 1
-      for (int s0 = 0; s0 < nsplit; s0 += MS) {
-        u32x4 v[MS][JB];
-        float wl[MS];
+        for (int j = 0; j < JB; ++j) {
+          const uint32_t u[4] = {v[q][j].x, v[q][j].y, v[q][j].z, v[q][j].w};
 #pragma unroll
-        for (int q = 0; q < MS; ++q) {
-          const int s2 = min(s0 + q, nsplit - 1);
-          wl[q] = ld_agent(lp + (int64_t)s2 * HP);
-#pragma unroll
-          for (int j = 0; j < JB; ++j)
-            v[q][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, off0 + s2 * split_bytes + (jh * JB + j) * 64 * 16, 0, kSc1);
-        }
-#pragma unroll
-        for (int q = 0; q < MS; ++q) {
-          const float ws = s0 + q < nsplit ? __builtin_amdgcn_exp2f(wl[q] - Mu) : 0.f;
-#pragma unroll
-          for (int j = 0; j < JB; ++j) {
-            const uint32_t u[4] = {v[q][j].x, v[q][j].y, v[q][j].z, v[q][j].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc[j][2 * e] += ws * __builtin_bit_cast(float, u[e] << 16);
-              acc[j][2 * e + 1] += ws * __builtin_bit_cast(float, u[e] & 0xffff0000u);
-            }
+          for (int e = 0; e < 4; ++e) {
+            acc[j][2 * e] += ws * __builtin_bit_cast(float, u[e] << 16);
+            acc[j][2 * e + 1] += ws * __builtin_bit_cast(float, u[e] & 0xffff0000u);
           }
         }
       }
+      if (s0 + MS < nsplit) continue;                    // more splits for these columns
       if (on) {
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
-          const int jj = jh * JB + j;
+          const int jj = jr * JB + j;
           uint2 p0, p1;
           p0.x = (uint32_t)f2bf(acc[j][0] * inv) | ((uint32_t)f2bf(acc[j][1] * inv) << 16);
           p0.y = (uint32_t)f2bf(acc[j][2] * inv) | ((uint32_t)f2bf(acc[j][3] * inv) << 16);
@@ -1046,6 +1054,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
         }
       }
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
     }
     if (on && a.lse && g == 0)
       a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;

@@ -121,6 +121,31 @@ def test_deterministic_bitwise():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "int8_packed"])
+def test_head_grouping_invariance_bitwise(fmt, monkeypatch):
+    """Spreading a row's heads over 1, 2, 4 or 8 head groups (the rest of the
+    workgroup's waves only gathering) leaves every output bit unchanged."""
+    import sparse_shared_kv_amd as s
+    kw = dict(family="sfa", max_kv=2500, topk=1100, num_heads_q=128)
+    if fmt != "bf16":
+        kw.update(kv_dtype=fmt, rope_head_dim=64)
+    P = synth.random_tiny(503, **kw)
+    outs, status = [], 0
+    for bpg in ("1", "2", "4", "8"):
+        monkeypatch.setenv("SFMLA_BPG", bpg)
+        call = s.Call(P.params, P.arrays)            # workspace sized for this grouping
+        outs.append([None if t is None else t.clone() for t in call.run()])
+        torch.cuda.synchronize()
+        status |= int(call.status.item())
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0])
+        assert (o[1] is None and outs[0][1] is None) or torch.equal(o[1], outs[0][1])
+    ref = oracle.forward(P, rows=[0, 1])
+    res = dict(O=outs[0][0].float().cpu().numpy(), status=status,
+               lse=None if outs[0][1] is None else outs[0][1].cpu().numpy())
+    check_outputs(P, res, ref, [0, 1])
+
+
 def test_batch_invariance_bitwise():
     """A sequence alone and inside a batch gives bit-identical rows."""
     L = logical(21, q_lens=[2, 3, 1, 2], ori_lens=[900, 1400, 300, 2000], qn=32, ratio=4,
