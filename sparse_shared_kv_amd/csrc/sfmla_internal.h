@@ -12,7 +12,7 @@ constexpr int kTile = 32;          // KV rows staged in LDS per step
 constexpr int kSplitRows = 512;    // KV rows per split of one query row
 constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
-constexpr int kCounterInts = 8;    // arrival counters per query row (one per head group)
+constexpr int kCounterInts = 64;   // arrival counters per query row (one per head group x wave)
 constexpr int32_t kMagic = 0x534d4c41;
 
 // Per-query-row plan record written by the planner (int32 each).
@@ -70,7 +70,7 @@ struct FwdArgs {
   int32_t* status;
   float* ws_lse;                    // [q_t][max_splits][heads] (bf16 path: log2 units)
   uint16_t* ws_ob;                  // bf16 path: partial O, per-wave fragment order
-  int32_t* counters;                // bf16 path: [q_t][kCounterInts] arrival counters
+  int32_t* counters;                // [q_t][kCounterInts] arrival counters of split partials
   // debug resolve
   int64_t* dbg_rows;
   int32_t* dbg_counts;

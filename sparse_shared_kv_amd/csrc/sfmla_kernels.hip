@@ -542,15 +542,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   __shared__ uint64_t sAV[VMODE ? kSplitRows + T : 1];
   __shared__ uint8_t sValid[kSplitRows + T];
 
-  // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so ids
-  // 8G*q + 8*hg + r (r < 8) put every head group of unit 8q + r on one XCD,
-  // dispatched together: the second gather of a row hits that XCD's L2.
+  // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so XCD x = bid
+  // mod 8 takes the query rows 8k + x, and within it slot bid / 8 runs over
+  // (k, split, head group): every split and head group of a row is on one
+  // XCD, dispatched together; the groups' repeated gathers and the merger's
+  // reads of the other splits' partials stay within that XCD's L2.
   const int G = a.groups;
   const int bid = blockIdx.x;
-  const int unit = (bid / (8 * G)) * 8 + (bid & 7);
-  const int hg = (bid / 8) % G;
-  if (unit >= a.q_t * a.max_splits) return;
-  const int row = unit / a.max_splits, split = unit - row * a.max_splits;
+  const int slot = bid >> 3;
+  const int hg = slot % G;
+  const int split = (slot / G) % a.max_splits;
+  const int row = (slot / G / a.max_splits) * 8 + (bid & 7);
+  if (row >= a.q_t) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g = l >> 4, t = l & 15;
   // a head group holds a.bpg 16-head blocks; waves past them only gather
@@ -926,6 +929,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // ---- split rows: every split stores its normalised partial (bf16, in the
   // lanes' fragment order: instruction j of a wave writes 1 KB contiguously),
   // then counts itself in; the last one to arrive merges all of them.
+  // loader-only waves hold no partial (their h0 lies in another group's heads)
+  if (!wave_on) return;
+  static_assert(NW * 8 <= kCounterInts, "arrival counters per row: head groups (<= 8) x waves");
   const int HP = a.groups * NW * HPW;              // heads per row, padded
   constexpr int WAVE_BYTES = HB * 16 * 64 * 16;    // one wave's partial
   // every split, head group and wave of this query row (< 2^31 bytes: at
@@ -934,7 +940,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc((char*)a.ws_ob + row * row_bytes, row_bytes);
   const int wave_off = ((split * a.groups + hg) * NW + w) * WAVE_BYTES;
 #pragma unroll
-  for (int hb = 0; hb < HB && wave_on; ++hb) {       // loader-only waves have no partial
+  for (int hb = 0; hb < HB; ++hb) {
     const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -952,17 +958,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
   }
   drain_vmem();                                     // this wave's partial is stored
-  __shared__ int sLast;
-  __syncthreads();
-  if (tid == 0)
-    sLast = __hip_atomic_fetch_add(&a.counters[(int64_t)row * kCounterInts + hg], 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
-  __syncthreads();
-  if (!sLast) return;
-  if (tid == 0)                                     // ready for the next call
-    __hip_atomic_store(&a.counters[(int64_t)row * kCounterInts + hg], 0, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  if (!wave_on) return;
+  // Arrival is counted per (row, head group, wave): the last of the splits'
+  // waves for these 16 heads merges them, so the merges of one row spread
+  // over the splits' workgroups and no workgroup barrier is needed.
+  int32_t* ctr = a.counters + (int64_t)row * kCounterInts + hg * NW + w;
+  int last = 0;
+  if (l == 0)
+    last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  if (!__builtin_amdgcn_readfirstlane(last)) return;
+  if (l == 0)                                       // ready for the next call
+    __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // merge from the stored partials (this split's own included).  Round r
   // loads column blocks [JB*(r / ns4), +JB) of kMergeSplits splits (16 loads
   // of 16 bytes per lane in flight); the first round travels together with
@@ -1165,8 +1170,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s) {
   FwdArgs b = a;
   b.groups = groups;
   if (b.bpg < 1 || b.bpg > NW) return hipErrorInvalidConfiguration;
-  const int64_t units = (int64_t)a.q_t * a.max_splits;
-  const int64_t blocks = (units + 7) / 8 * 8 * groups;
+  const int64_t blocks = (int64_t)(a.q_t + 7) / 8 * 8 * a.max_splits * groups;
   hipLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      s, b);
   return hipGetLastError();
