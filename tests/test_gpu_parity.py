@@ -213,3 +213,65 @@ def test_merge_partials_entry_point_matches_oracle_merge():
         fin = np.isfinite(L)
         assert (np.isfinite(gl) == fin).all()
         assert np.abs(gl[fin] - L[fin]).max() <= 1e-3
+
+
+@pytest.mark.parametrize("fmt", ["int8_packed", "fp8_e4m3_packed"])
+def test_rope_free_rows_equal_zero_rope_rows_bitwise(fmt):
+    """528-byte rows (no rope) give bit-identical results to 656-byte rows
+    whose rope is zero (SparseAttnSharedkv README, 参数说明: the packed row
+    width with and without rope)."""
+    import copy
+    import sparse_shared_kv_amd as s
+    P = synth.random_tiny(601, family="sfa", kv_dtype=fmt, rope_head_dim=64, num_heads_q=64,
+                          max_kv=700, topk=600)
+    P656 = copy.deepcopy(P)
+    P656.arrays["ori_kv"] = P656.arrays["ori_kv"].copy()
+    P656.arrays["ori_kv"][:, 512:640] = 0                      # zero rope
+    P528 = copy.deepcopy(P656)
+    P528.params["rope_head_dim"] = 0
+    P528.arrays["ori_kv"] = np.ascontiguousarray(
+        np.concatenate([P656.arrays["ori_kv"][:, :512], P656.arrays["ori_kv"][:, 640:656]], axis=1))
+    P528.arrays["q"] = np.ascontiguousarray(P656.arrays["q"][..., :512])
+    # the same softmax scale on both sides (not 1/sqrt of each width)
+    P528.params["softmax_scale"] = P656.params["softmax_scale"]
+    a = run_gpu(P656)
+    b = run_gpu(P528)
+    assert a["status"] == 0 and b["status"] == 0
+    assert np.array_equal(a["O"], b["O"])
+    assert np.array_equal(a["lse"], b["lse"])
+    ref = oracle.forward(P528, rows=[0, 1])
+    check_outputs(P528, b, ref, [0, 1])
+
+
+def test_graph_replay_matches_eager():
+    """plan + forward + combine captured in one HIP graph: every replay,
+    with other eager work and synchronisations in between, reproduces the
+    eager result bit for bit."""
+    import sparse_shared_kv_amd as s
+    P = synth.random_tiny(602, family="sfa", max_kv=3000, topk=1500, num_heads_q=128)
+    other = synth.random_tiny(603, family="csa", num_heads_q=64, max_kv=900)
+    call = s.Call(P.params, P.arrays)
+    eager = [t.clone() for t in call.run() if t is not None]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call.run()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.run()
+    oc = s.Call(other.params, other.arrays)
+    for rep in range(4):
+        for t in (call.out, call.lse):
+            if t is not None:
+                t.fill_(float("nan"))                # the replay must rewrite every output
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t for t in (call.out, call.lse) if t is not None]
+        for e, x in zip(eager, got):
+            assert torch.equal(e, x), rep
+        oc.run()                                     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert int(call.status.item()) == 0

@@ -424,3 +424,27 @@ def test_inconsistent_residual_rejected():
         P.arrays["cmp_residual_kv"][:] = 1
     with pytest.raises(ValueError):
         oracle.forward(P)
+
+
+@pytest.mark.parametrize("fmt", ["int8_packed", "fp8_e4m3_packed"])
+def test_rope_free_rows_equal_zero_rope_rows(fmt):
+    """A 528-byte row (no rope) and a 656-byte row whose rope is zero are the
+    same key and value (SparseAttnSharedkv README, 参数说明: the packed row
+    holds the rope between the codes and the scales only when rope is used)."""
+    import copy
+    P = synth.random_tiny(611, family="sfa", kv_dtype=fmt, rope_head_dim=64, num_heads_q=4,
+                          max_kv=60)
+    P656 = copy.deepcopy(P)
+    P656.arrays["ori_kv"] = P656.arrays["ori_kv"].copy()
+    P656.arrays["ori_kv"][:, 512:640] = 0
+    P528 = copy.deepcopy(P656)
+    P528.params["rope_head_dim"] = 0
+    P528.arrays["ori_kv"] = np.ascontiguousarray(
+        np.concatenate([P656.arrays["ori_kv"][:, :512], P656.arrays["ori_kv"][:, 640:656]], axis=1))
+    P528.arrays["q"] = np.ascontiguousarray(P656.arrays["q"][..., :512])
+    a = oracle.forward(P656)
+    b = oracle.forward(P528)
+    assert np.array_equal(a["O"], b["O"]) and np.array_equal(a["lse"], b["lse"])
+    # and the rope does matter when it is not zero
+    c = oracle.forward(P)
+    assert not np.allclose(c["O"], a["O"])
