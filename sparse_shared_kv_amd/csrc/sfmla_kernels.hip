@@ -599,20 +599,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const int k1 = min(n, k0 + chunk);
   const int nt = (k1 - k0 + T - 1) / T;
 
-  // Q slices (B operand: k = d, n = head), loaded first: they travel while
-  // the list positions resolve, and waiting for them never waits for KV tiles
+  // Q slices (B operand: k = d, n = head).  They are loaded right after the
+  // index loads of the resolve below: loads complete in order, so the checks
+  // on the indices do not wait for Q, while Q travels during the table step.
   bf16x8 qreg[HB][NKS];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int h = h0 + 16 * hb + t;
-    const bool on = wave_on && h < a.qn;
-    const uint16_t* qp = a.q + ((int64_t)row * a.qn + (on ? h : 0)) * DQK + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 v = on ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
-      qreg[hb][ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
   // ---- resolve every list position of this split once, into row addresses
   //      (empty or masked slots read a zero row).  Each thread takes up to
   //      PPT positions; the index loads of all of them, then the table loads
@@ -632,6 +622,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       const int32_t* ep = (tid + u * NTHR < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
       vv[u] = *(ep ? ep : rec);
     }
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      // unconditional loads (a branch join would wait for them): lanes of
+      // heads past q_n read head 0; their scores stay in their own lanes and
+      // their outputs are never written
+      const int h = h0 + 16 * hb + t;
+      const uint16_t* qp = a.q + ((int64_t)row * a.qn + (h < a.qn ? h : 0)) * DQK + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
+    }
+
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int k = k0 + tid + u * NTHR;
