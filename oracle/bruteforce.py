@@ -123,7 +123,9 @@ def brute_force(P):
                 if not ok:
                     continue
                 if p["ori_topk"] > 0:
-                    w[j] = np.count_nonzero(np.asarray(a["ori_sparse_indices"])[row, 0] == j)
+                    # entries that select the block holding position j
+                    sbs = int(p.get("sparse_block_size", 1))
+                    w[j] = np.count_nonzero(np.asarray(a["ori_sparse_indices"])[row, 0] == j // sbs)
                 else:
                     w[j] = 1.0
             if n_ori:

@@ -24,6 +24,12 @@ notes):
       v <= p.
   R6  query rows past seqused_q attend to nothing (output 0, LSE -inf).
   R7  block-table entries are >= 0 block ids.
+  R18 block-wise TopK (sparse_block_size s > 1, SparseFlashAttention README
+      参数说明 sparseBlockSize; kv_quant_sparse_flash_attention blog 参数说明
+      sparse_block_size): entry v selects tokens v*s .. v*s + s - 1, which
+      share that selection; each of them still passes the side's mask
+      predicate on its own.  Entries keep slot order, tokens ascend within
+      an entry.
 """
 
 from __future__ import annotations
@@ -125,6 +131,12 @@ def cmp_visible(mode: int, j: int, p_c: int, n: int, ratio: int) -> bool:
     raise ValueError("cmp_mask_mode %d" % mode)
 
 
+def block_tokens(v: int, sbs: int) -> list:
+    """Token positions selected by TopK entry v when entries select blocks of
+    sbs consecutive tokens (R18): v*sbs .. v*sbs + sbs - 1."""
+    return [v * sbs + u for u in range(sbs)]
+
+
 def physical_row(P, side: str, b: int, j: int) -> int:
     """Logical position j of batch b -> physical row of the side's KV tensor.
 
@@ -164,9 +176,13 @@ def resolve_rows(P, row: int, b: int, i: int):
     ori = []
     if int(p["ori_topk"]) > 0:                                  # R4, R5
         idx = _arr(P, "ori_sparse_indices")[row, 0]
+        sbs = int(p.get("sparse_block_size", 1))                # R18
         for v in idx.tolist():
-            if v >= 0 and ori_visible(mode, v, pos, L["ori_len"], left, right):
-                ori.append(v)
+            if v < 0:
+                continue
+            for j in block_tokens(v, sbs):
+                if ori_visible(mode, j, pos, L["ori_len"], left, right):
+                    ori.append(j)
     else:
         for j in range(L["ori_len"]):                           # R2
             if ori_visible(mode, j, pos, L["ori_len"], left, right):

@@ -33,7 +33,7 @@ def _base_params(**kw):
         ori_topk=0, cmp_topk=0, cmp_ratio=1, ori_mask_mode=4,
         cmp_mask_mode=0, ori_win_left=-1, ori_win_right=-1, has_ori_kv=True,
         has_cmp_kv=False, kv_dtype="bf16", separate_v=False,
-        softmax_scale=1.0, return_softmax_lse=True,
+        softmax_scale=1.0, return_softmax_lse=True, sparse_block_size=1,
     )
     for k, v in kw.items():
         if k not in p:
@@ -278,7 +278,8 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
                 batch=None, max_q=4, max_kv=64, block_size=None,
                 cmp_ratio=None, sinks=None, dist="normal", topk=None,
                 separate_v=None, q_lens=None, ori_lens=None,
-                seqused_q=None, duplicates=False, win=None, masks=None):
+                seqused_q=None, duplicates=False, win=None, masks=None,
+                sparse_block_size=1):
     """A small random problem.
 
     family: "swa" (ori window only), "csa" (window + TopK compressed rows),
@@ -286,7 +287,9 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
     token-wise sparse MLA-absorb form).  Lengths, windows, mask modes,
     layouts and index tails are drawn at random unless given.  dist "p4" uses
     the SparseAttnSharedKV example's draws (q ~ U(-10,10), kv ~ U(-5,10),
-    sinks ~ U(0,1)), which give very peaked softmaxes.
+    sinks ~ U(0,1)), which give very peaked softmaxes.  sparse_block_size
+    (sfa only) > 1 makes each TopK entry select that many consecutive tokens;
+    paged block sizes are then multiples of it.
     """
     ss = np.random.SeedSequence(seed)
     s_cfg, s_q, s_ori, s_v, s_cmp, s_idx, s_tab, s_sink = ss.spawn(8)
@@ -304,6 +307,9 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
     if separate_v is None:
         separate_v = bool(family == "sfa" and not packed and g.integers(0, 2))
     bs = block_size or int(g.choice([1, 2, 16]))
+    sbs = int(sparse_block_size)
+    if sbs > 1 and bs % sbs:
+        bs = sbs * (1 + bs // sbs)
     r = cmp_ratio or (1 if family in ("swa", "sfa") else int(g.choice([1, 2, 4])))
     has_cmp = family in ("csa", "hca")
 
@@ -420,9 +426,11 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
         return out
 
     if family == "sfa":
-        K = topk or int(g.integers(1, max_kv + 1))
+        nblk = [-(-n // sbs) for n in ori_lens]              # entries index blocks
+        K = topk or int(g.integers(1, max(nblk) + 1))
         params["ori_topk"] = K
-        arrays["ori_sparse_indices"] = index_rows(ori_lens, K)
+        params["sparse_block_size"] = sbs
+        arrays["ori_sparse_indices"] = index_rows(nblk, K)
     if family == "csa":
         K = topk or int(g.integers(1, 2 * max(1, max(cmp_lens)) + 2))
         params["cmp_topk"] = K

@@ -83,6 +83,9 @@ for s in range(6):
     CASES.append(dict(seed=200 + s, dist="p4", family=["csa", "hca", "swa"][s % 3]))
 for s in range(4):
     CASES.append(dict(seed=300 + s, family=["csa", "sfa"][s % 2], duplicates=True))
+for s in range(9):                                  # block-wise TopK (R18)
+    CASES.append(dict(seed=400 + s, family="sfa", sparse_block_size=[2, 4, 16][s % 3],
+                      max_kv=90, duplicates=bool(s % 4 == 3)))
 
 
 @pytest.mark.parametrize("kw", CASES, ids=lambda k: "-".join("%s" % v for v in k.values()))
@@ -448,3 +451,30 @@ def test_rope_free_rows_equal_zero_rope_rows(fmt):
     # and the rope does matter when it is not zero
     c = oracle.forward(P)
     assert not np.allclose(c["O"], a["O"])
+
+
+
+@pytest.mark.parametrize("sbs", [2, 8])
+def test_block_topk_covering_the_prefix_equals_sdpa_causal(sbs):
+    """Block-wise TopK (R18) whose entries are every block up to the query's
+    block, under the causal mode, is dense causal attention (torch SDPA)."""
+    P = synth.random_tiny(431, family="sfa", layout_q="TND", layout_kv="TND", batch=1,
+                          q_lens=[5], ori_lens=[37], num_heads_q=3, sparse_block_size=sbs,
+                          masks=(3, 0), sinks=False, separate_v=False, rope_head_dim=0)
+    K = -(-37 // sbs)
+    idx = np.full((5, 1, K), -1, dtype=np.int32)
+    rng = np.random.default_rng(5)
+    for i in range(5):
+        blocks = rng.permutation(np.arange((37 - 5 + i) // sbs + 1))   # any slot order
+        idx[i, 0, :len(blocks)] = blocks
+    P.arrays["ori_sparse_indices"] = idx
+    P.params["ori_topk"] = K
+    r = oracle.forward(P)
+    q = torch.from_numpy(P.arrays["q"].view(np.int16)).view(torch.bfloat16).double()       # (5, h, d)
+    k = torch.from_numpy(P.arrays["ori_kv"].view(np.int16)).view(torch.bfloat16).double()  # (37, d)
+    qh = q.permute(1, 0, 2)
+    kh = k[None].expand(qh.shape[0], -1, -1).contiguous()
+    mask = torch.ones(5, 37, dtype=torch.bool).tril(diagonal=37 - 5)   # right-down causal
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qh, kh, kh, attn_mask=mask, scale=P.params["softmax_scale"])
+    assert np.abs(r["O"] - ref.permute(1, 0, 2).numpy()).max() < 1e-12

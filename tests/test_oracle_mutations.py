@@ -28,6 +28,7 @@ def _pins():
         ("sink", T.test_sink_closed_form),
         ("merge", T.test_split_merge_equals_unsplit),
         ("cp", T.test_cp_split_invariance),
+        ("block_sdpa", lambda: T.test_block_topk_covering_the_prefix_equals_sdpa_causal(8)),
     ]
     for name, fn in checks:
         try:
@@ -48,6 +49,7 @@ _orig_attend = oatt.attend
 _orig_phys = ores.physical_row
 _orig_fp8 = odec.fp8_e4m3fn_to_f64
 _orig_packed = odec.decode_packed
+_orig_block_tokens = ores.block_tokens
 
 
 def _band_exclusive(mode, j, p, n, left, right):
@@ -100,6 +102,10 @@ def _v_from_rope(q, K, V, scale, sinks=None):
     return _orig_attend(q, K, K[:, -V.shape[1]:], scale, sinks)
 
 
+def _block_offset_dropped(v, sbs):
+    return [v + u for u in range(sbs)]                  # forgets the block stride
+
+
 MUTANTS = {
     "window_left_edge_exclusive": (ores, "ori_visible", _band_exclusive),
     "cmp_causal_strict": (ores, "cmp_visible", _cmp_strict),
@@ -110,6 +116,7 @@ MUTANTS = {
     "fp8_exponent_bias_off_by_one": (odec, "fp8_e4m3fn_to_f64", _fp8_bias8),
     "packed_scale_tiles_reversed": (oatt, "decode_packed", _packed_scale_tiles_swapped),
     "value_taken_from_wrong_columns": (oatt, "attend", _v_from_rope),
+    "block_offset_dropped": (ores, "block_tokens", _block_offset_dropped),
 }
 
 
