@@ -110,6 +110,11 @@ typedef struct sfmla_params {
   int32_t max_seqlen_cmp_kv; /* longest cmp length (0 without cmp_kv)         */
   int32_t ori_topk;      /* 0: window rule; > 0: TopK list over ori_kv        */
   int32_t cmp_topk;      /* 0: all visible cmp rows (HCA); > 0: CSA list      */
+  int32_t ori_sparse_block_size; /* tokens per ori TopK entry: 1 token-wise;
+                            2..128 (power of two) block-wise, entry v selecting
+                            tokens v*s .. v*s+s-1 (SparseFlashAttention README,
+                            参数说明 sparseBlockSize); must divide ori_block_size
+                            under PA; 1 when ori_topk is 0                    */
   int32_t cmp_ratio;     /* >= 1 (1 without cmp_kv)                           */
   int32_t ori_mask_mode; /* 0, 3 or 4 (TopK lists: 0 or 3)                    */
   int32_t cmp_mask_mode; /* 0 or 3                                            */

@@ -127,6 +127,7 @@ def make_params(spec: dict, arrays: dict) -> Params:
     p.max_seqlen_cmp_kv = int(g("max_seqlen_cmp_kv", 0))
     p.ori_topk = int(g("ori_topk", 0))
     p.cmp_topk = int(g("cmp_topk", 0))
+    p.ori_sparse_block_size = int(g("sparse_block_size", 1))
     p.cmp_ratio = int(g("cmp_ratio", 1))
     p.ori_mask_mode = int(g("ori_mask_mode"))
     p.cmp_mask_mode = int(g("cmp_mask_mode", 0))

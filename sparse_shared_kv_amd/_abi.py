@@ -34,7 +34,8 @@ class Params(ctypes.Structure):
         ("ori_block_table_cols", _i32), ("cmp_block_table_cols", _i32),
         ("ori_kv_rows", _i64), ("cmp_kv_rows", _i64),
         ("max_seqlen_q", _i32), ("max_seqlen_ori_kv", _i32), ("max_seqlen_cmp_kv", _i32),
-        ("ori_topk", _i32), ("cmp_topk", _i32), ("cmp_ratio", _i32),
+        ("ori_topk", _i32), ("cmp_topk", _i32), ("ori_sparse_block_size", _i32),
+        ("cmp_ratio", _i32),
         ("ori_mask_mode", _i32), ("cmp_mask_mode", _i32), ("ori_win_left", _i32),
         ("ori_win_right", _i32), ("has_ori_kv", _i32), ("has_cmp_kv", _i32),
         ("kv_dtype", _i32), ("has_separate_v", _i32), ("has_sinks", _i32),

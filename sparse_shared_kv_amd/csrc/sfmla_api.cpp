@@ -54,7 +54,8 @@ uint32_t fingerprint(const sfmla_params& p) {
       p.num_heads_q, p.num_heads_kv, p.head_dim, p.rope_head_dim, p.batch_size, p.layout_q,
       p.layout_kv, p.q_s, p.q_t, p.ori_kv_s, p.cmp_kv_s, p.ori_block_size, p.cmp_block_size,
       p.ori_block_table_cols, p.cmp_block_table_cols, p.max_seqlen_q, p.max_seqlen_ori_kv,
-      p.max_seqlen_cmp_kv, p.ori_topk, p.cmp_topk, p.cmp_ratio, p.ori_mask_mode,
+      p.max_seqlen_cmp_kv, p.ori_topk, p.cmp_topk, p.ori_sparse_block_size, p.cmp_ratio,
+      p.ori_mask_mode,
       p.cmp_mask_mode, p.ori_win_left, p.ori_win_right, p.has_ori_kv, p.has_cmp_kv,
       p.kv_dtype, p.has_separate_v, p.has_sinks, p.return_softmax_lse, p.has_seqused_q,
       p.has_seqused_ori_kv, p.has_seqused_cmp_kv, p.has_cmp_residual_kv};
@@ -94,6 +95,15 @@ sfmla_status validate(const sfmla_params* pp) {
   REQUIRE(p.ori_kv_rows < ((int64_t)1 << 40), "ori_kv_rows too large");
   REQUIRE(p.ori_win_left >= -1 && p.ori_win_right >= -1, "window bounds must be -1 or >= 0");
   REQUIRE(p.ori_topk >= 0 && p.cmp_topk >= 0, "topk must be >= 0");
+  {
+    const int s = p.ori_sparse_block_size;
+    REQUIRE(s >= 1 && s <= 128 && (s & (s - 1)) == 0,
+            "ori_sparse_block_size must be a power of two in 1..128");
+    REQUIRE(s == 1 || p.ori_topk > 0, "ori_sparse_block_size > 1 needs an ori TopK list");
+    REQUIRE(p.layout_kv != SFMLA_LAYOUT_PA_BSND || s == 1 || p.ori_block_size % s == 0,
+            "ori_sparse_block_size must divide ori_block_size");
+    REQUIRE((int64_t)p.ori_topk * s <= ((int64_t)1 << 30), "ori_topk * ori_sparse_block_size too large");
+  }
   REQUIRE(p.ori_mask_mode == 0 || p.ori_mask_mode == 3 || p.ori_mask_mode == 4,
           "ori_mask_mode must be 0, 3 or 4");
   REQUIRE(p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_INT8_PACKED ||
@@ -130,7 +140,7 @@ sfmla_status validate(const sfmla_params* pp) {
 int64_t max_list(const sfmla_params& p) {
   int64_t n;
   if (p.ori_topk > 0) {
-    n = p.ori_topk;
+    n = (int64_t)p.ori_topk * p.ori_sparse_block_size;
   } else if (p.ori_mask_mode == 4 && p.ori_win_left >= 0 && p.ori_win_right >= 0) {
     n = std::min<int64_t>(p.max_seqlen_ori_kv, (int64_t)p.ori_win_left + p.ori_win_right + 1);
   } else {
@@ -272,6 +282,7 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
   f.ori_rows = p.ori_kv_rows;
   f.cmp_rows = p.cmp_kv_rows;
   f.ori_topk = p.ori_topk;
+  f.ori_sbs_log2 = __builtin_ctz((unsigned)p.ori_sparse_block_size);   // a power of two
   f.cmp_topk = p.cmp_topk;
   f.ori_mode = p.ori_mask_mode;
   f.win_l = p.ori_win_left;

@@ -48,6 +48,7 @@ struct FwdArgs {
   int32_t ori_bs, cmp_bs, ori_bt_cols, cmp_bt_cols;
   int64_t ori_rows, cmp_rows;
   int32_t ori_topk, cmp_topk, ori_mode, win_l, win_r, has_cmp;
+  int32_t ori_sbs_log2;             // log2 of the tokens per ori TopK entry (block-wise TopK)
   int32_t max_splits, has_sinks;
   int32_t groups;                   // head groups of the launch
   int32_t bpg;                      // 16-head blocks per head group (<= waves; spare waves only load)

@@ -63,7 +63,8 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* rec) {
 // nullptr where the position follows a window or all-visible rule.
 __device__ __forceinline__ const int32_t* slot_entry(const FwdArgs& a, const RowInfo& ri, int row,
                                                      int k) {
-  if (k < ri.ori_cnt) return a.ori_topk > 0 ? a.ori_idx + (int64_t)row * a.ori_topk + k : nullptr;
+  if (k < ri.ori_cnt)
+    return a.ori_topk > 0 ? a.ori_idx + (int64_t)row * a.ori_topk + (k >> a.ori_sbs_log2) : nullptr;
   return a.cmp_topk > 0 ? a.cmp_idx + (int64_t)row * a.cmp_topk + (k - ri.ori_cnt) : nullptr;
 }
 
@@ -74,12 +75,16 @@ __device__ __forceinline__ int slot_row(const FwdArgs& a, const RowInfo& ri, int
   if (k < ri.ori_cnt) {
     *is_cmp = 0;
     if (a.ori_topk <= 0) return ri.ori_lo + k;
-    if (v < 0 || v >= ri.ori_len) return -1;
-    if (a.ori_mode == SFMLA_MASK_CAUSAL && v > ri.p) return -1;
+    if (v < 0) return -1;
+    // block-wise entries select tokens v*s .. v*s+s-1 (s = 1: token-wise);
+    // each passes the mask on its own
+    const int64_t j = ((int64_t)v << a.ori_sbs_log2) + (k & ((1 << a.ori_sbs_log2) - 1));
+    if (j >= ri.ori_len) return -1;
+    if (a.ori_mode == SFMLA_MASK_CAUSAL && j > ri.p) return -1;
     if (a.ori_mode == SFMLA_MASK_BAND &&
-        ((a.win_l >= 0 && v < ri.p - a.win_l) || (a.win_r >= 0 && v > ri.p + a.win_r)))
+        ((a.win_l >= 0 && j < ri.p - a.win_l) || (a.win_r >= 0 && j > ri.p + a.win_r)))
       return -1;
-    return v;
+    return (int)j;
   }
   *is_cmp = 1;
   if (a.cmp_topk <= 0) return k - ri.ori_cnt;
@@ -190,7 +195,7 @@ __global__ void plan_kernel(PlanArgs a) {
 
   int ori_lo = 0, ori_cnt = 0;
   if (p.ori_topk > 0) {
-    ori_cnt = p.ori_topk;
+    ori_cnt = p.ori_topk * p.ori_sparse_block_size;   // list positions (tokens)
   } else {
     int lo = 0, hi = ori_len - 1;
     if (p.ori_mask_mode == SFMLA_MASK_CAUSAL) {

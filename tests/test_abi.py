@@ -85,6 +85,10 @@ BAD = [
     ("cmp_ratio", 4, "cmp_ratio"),
     ("kv_dtype", 7, "kv_dtype"),
     ("batch_size", 0, "batch_size"),
+    ("ori_sparse_block_size", 0, "ori_sparse_block_size"),
+    ("ori_sparse_block_size", 3, "ori_sparse_block_size"),
+    ("ori_sparse_block_size", 256, "ori_sparse_block_size"),
+    ("ori_sparse_block_size", 4, "needs an ori TopK list"),
 ]
 
 
@@ -167,3 +171,13 @@ def test_combine_rejects_bad_dv():
     st = lib.sfmla_merge_partials(2, 4, 8, 6, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
                            ctypes.c_void_p(4096), None, None)
     assert st == 1 and b"dv" in lib.sfmla_last_error()
+
+
+def test_block_wise_topk_must_divide_the_page():
+    P = synth.random_tiny(5, family="sfa", layout_kv="PA_BSND", block_size=16,
+                          sparse_block_size=16)
+    p = s.make_params(P.params, P.arrays)
+    assert s.sfmla_metadata_size(p) > 0
+    p.ori_sparse_block_size = 32                    # does not divide the 16-token page
+    with pytest.raises(s.SfmlaError, match="divide ori_block_size"):
+        s.sfmla_metadata_size(p)

@@ -73,6 +73,16 @@ TINY += [dict(seed=500, family="swa", max_kv=1500, win=(-1, -1), masks=(0, 0), n
               rope_head_dim=0, num_heads_q=64),
          dict(seed=507, family="sfa", max_kv=1700, topk=1500, separate_v=True, rope_head_dim=64,
               num_heads_q=128, layout_q="TND", layout_kv="PA_BSND", block_size=64)]
+# block-wise TopK entries (sparse_block_size > 1), every layout and format,
+# with duplicates, and lists long enough for several splits
+TINY += [dict(seed=700 + s, family="sfa", sparse_block_size=[2, 4, 16, 64][s % 4],
+              max_kv=300, num_heads_q=[16, 64, 128][s % 3],
+              kv_dtype=["bf16", "bf16", "int8_packed", "fp8_e4m3_packed"][(s // 2) % 4],
+              duplicates=bool(s % 5 == 4)) for s in range(10)]
+TINY += [dict(seed=720, family="sfa", sparse_block_size=16, max_kv=3000, topk=120,
+              num_heads_q=128, layout_q="BSND", layout_kv="PA_BSND", block_size=64),
+         dict(seed=721, family="sfa", sparse_block_size=8, max_kv=2500, topk=250,
+              kv_dtype="int8_packed", rope_head_dim=64, num_heads_q=64)]
 
 
 @pytest.mark.parametrize("kw", TINY, ids=lambda k: "-".join(str(v) for v in k.values()))
