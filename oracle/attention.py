@@ -21,7 +21,14 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import decode as _decode
 from .decode import bf16_to_f64, decode_packed
+
+
+def elem_to_f64(P):
+    """Decoder of the 16-bit q / kv elements: float16 when kv_dtype is
+    fp16 (q, kv and the output then share that type), bfloat16 otherwise."""
+    return _decode.fp16_to_f64 if P.params["kv_dtype"] == "fp16" else bf16_to_f64
 from .resolve import CMP_BIT, query_rows, resolve_rows
 
 
@@ -46,10 +53,11 @@ def _rows_kv(P, phys: np.ndarray):
             continue
         src = np.asarray(P.arrays["%s_kv" % side])
         rows = src[rid[sel]]
-        if p["kv_dtype"] == "bf16":
-            k = bf16_to_f64(rows[:, :d_qk])
+        if p["kv_dtype"] in ("bf16", "fp16"):
+            dec = elem_to_f64(P)
+            k = dec(rows[:, :d_qk])
             if side == "ori" and p.get("separate_v"):
-                v = bf16_to_f64(np.asarray(P.arrays["ori_v"])[rid[sel]][:, :512])
+                v = dec(np.asarray(P.arrays["ori_v"])[rid[sel]][:, :512])
             else:
                 v = k[:, :512]
         else:
@@ -107,7 +115,7 @@ def forward(P, rows=None):
         _, _, phys = resolve_rows(P, row, b, i)
         lists[row] = phys
         K, V = _rows_kv(P, phys)
-        q = bf16_to_f64(q_all[row])
+        q = elem_to_f64(P)(q_all[row])
         o, l1, l2 = attend(q, K, V, float(p["softmax_scale"]), sinks)
         O[row], lse[row], lse_tot[row] = o, l1, l2
     return dict(O=O, lse=lse, lse_total=lse_tot, lists=lists)

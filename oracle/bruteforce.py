@@ -25,6 +25,15 @@ import numpy as np
 import torch
 
 
+def _f16(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16).to(torch.float64).numpy()
+
+
+def _elem(P):
+    return _f16 if P.params["kv_dtype"] == "fp16" else _bf16
+
+
 def _bf16(bits):
     t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
     return t.view(torch.bfloat16).to(torch.float64).numpy()
@@ -77,10 +86,10 @@ def _decode(P, side, phys):
     p = P.params
     rope = int(p["rope_head_dim"])
     src = np.asarray(P.arrays[side + "_kv"])[phys]
-    if p["kv_dtype"] == "bf16":
-        k = _bf16(src[:, :512 + rope])
+    if p["kv_dtype"] in ("bf16", "fp16"):
+        k = _elem(P)(src[:, :512 + rope])
         if side == "ori" and p.get("separate_v"):
-            v = _bf16(np.asarray(P.arrays["ori_v"])[phys][:, :512])
+            v = _elem(P)(np.asarray(P.arrays["ori_v"])[phys][:, :512])
         else:
             v = k[:, :512]
         return k, v
@@ -155,7 +164,7 @@ def brute_force(P):
             Kall = np.concatenate(k_parts)[W > 0]
             Vall = np.concatenate(v_parts)[W > 0]
             Wv = W[W > 0]
-            q = _bf16(q_all[row])
+            q = _elem(P)(q_all[row])
             for h in range(qn):
                 s = scale * (Kall @ q[h])
                 top = s.max()

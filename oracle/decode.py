@@ -21,6 +21,23 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def fp16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE 754 binary16 bits -> float64, from the format's definition: sign,
+    5-bit exponent with bias 15, 10-bit fraction; exponent 0 is subnormal
+    (f / 2^10 * 2^-14), exponent 31 is infinity (f = 0) or NaN.  float16 is
+    the other q / kv type the pages allow (sparse_flash_mla API page and
+    SparseFlashAttention README, 参数说明 data types)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b & 0x8000, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = (1.0 + f / 1024.0) * np.exp2(e.astype(np.float64) - 15.0)
+    subnormal = (f / 1024.0) * 2.0 ** -14
+    mag = np.where(e == 0, subnormal, normal)
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
 def int8_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.asarray(codes, dtype=np.uint8).view(np.int8).astype(np.float64)
 

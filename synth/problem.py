@@ -66,11 +66,16 @@ def bf16_bits(x) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def fp16_bits(x) -> np.ndarray:
+    """Round fp32 values to float16 (nearest, ties to even); return uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def normal_bf16(seq: np.random.SeedSequence, shape, std=1.0) -> np.ndarray:
+def normal_bf16(seq: np.random.SeedSequence, shape, std=1.0, fp16=False) -> np.ndarray:
     """bf16 bits of N(0, std^2) draws, filled block-parallel.
 
     Row blocks get their own spawned child stream, so the values do not depend
@@ -90,7 +95,7 @@ def normal_bf16(seq: np.random.SeedSequence, shape, std=1.0) -> np.ndarray:
         v = g.standard_normal((r1 - r0, width), dtype=np.float32)
         if std != 1.0:
             v *= np.float32(std)
-        out[r0:r1] = bf16_bits(v)
+        out[r0:r1] = fp16_bits(v) if fp16 else bf16_bits(v)
 
     if n_blocks == 1:
         work(0)

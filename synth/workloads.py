@@ -12,7 +12,7 @@ import math
 
 import numpy as np
 
-from .problem import (Problem, banked_rows, bf16_bits, normal_bf16,
+from .problem import (Problem, banked_rows, bf16_bits, fp16_bits, normal_bf16,
                       packed_rows)
 
 
@@ -303,7 +303,9 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
     rope = rope_head_dim if rope_head_dim is not None else (
         int(g.choice([0, 64])) if family == "sfa" else 0)
     kv_dtype = kv_dtype or "bf16"
-    packed = kv_dtype != "bf16"
+    packed = kv_dtype not in ("bf16", "fp16")
+    half = kv_dtype == "fp16"                 # q, kv and output in float16
+    to_bits = fp16_bits if half else bf16_bits
     if separate_v is None:
         separate_v = bool(family == "sfa" and not packed and g.integers(0, 2))
     bs = block_size or int(g.choice([1, 2, 16]))
@@ -340,16 +342,16 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
         use_seqused_q = False
     if dist == "p4":
         qv = _gen(s_q).uniform(-10, 10, (rows, qn, d_qk)).astype(np.float32)
-        q = bf16_bits(qv)
+        q = to_bits(qv)
     else:
-        q = normal_bf16(s_q, (rows, qn, d_qk))
+        q = normal_bf16(s_q, (rows, qn, d_qk), fp16=half)
 
     def kv_rows(seq, n, width_elems):
         if packed:
             return packed_rows(seq, n, rope, "int8" if kv_dtype == "int8_packed" else "fp8")
         if dist == "p4":
-            return bf16_bits(_gen(seq).uniform(-5, 10, (n, width_elems)).astype(np.float32))
-        return normal_bf16(seq, (n, width_elems))
+            return to_bits(_gen(seq).uniform(-5, 10, (n, width_elems)).astype(np.float32))
+        return normal_bf16(seq, (n, width_elems), fp16=half)
 
     g_tab = _gen(s_tab)
     arrays = dict(q=q)

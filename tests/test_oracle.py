@@ -62,6 +62,15 @@ def test_bf16_decoder_matches_torch():
     assert np.array_equal(ours[ok], ref[ok])
 
 
+def test_fp16_decoder_matches_torch_all_codes():
+    codes = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.float16).double().numpy()
+    got = odec.fp16_to_f64(codes)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert (both_nan | (got == ref)).all()
+    assert np.array_equal(np.signbit(got[~both_nan]), np.signbit(ref[~both_nan]))
+
+
 def test_int8_decoder():
     codes = np.arange(256, dtype=np.uint8)
     assert np.array_equal(odec.int8_to_f64(codes),
@@ -83,6 +92,9 @@ for s in range(6):
     CASES.append(dict(seed=200 + s, dist="p4", family=["csa", "hca", "swa"][s % 3]))
 for s in range(4):
     CASES.append(dict(seed=300 + s, family=["csa", "sfa"][s % 2], duplicates=True))
+for s in range(8):                                  # float16 q / kv / output
+    CASES.append(dict(seed=500 + s, kv_dtype="fp16", family=["swa", "csa", "hca", "sfa"][s % 4],
+                      dist=["normal", "p4"][(s // 4) % 2]))
 for s in range(9):                                  # block-wise TopK (R18)
     CASES.append(dict(seed=400 + s, family="sfa", sparse_block_size=[2, 4, 16][s % 3],
                       max_kv=90, duplicates=bool(s % 4 == 3)))

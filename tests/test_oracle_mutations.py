@@ -23,6 +23,7 @@ def _pins():
                              T.test_uniform_attention_with_sink())),
         ("lse", T.test_lse_against_scipy_logsumexp),
         ("fp8", T.test_fp8_decoder_matches_torch_all_codes),
+        ("fp16", T.test_fp16_decoder_matches_torch_all_codes),
         ("packed", lambda: T.test_packed_equals_float_on_dequantised_values("int8_packed", 64)),
         ("layout", lambda: T.test_layout_and_block_permutation_invariance("csa")),
         ("sink", T.test_sink_closed_form),
@@ -50,6 +51,7 @@ _orig_phys = ores.physical_row
 _orig_fp8 = odec.fp8_e4m3fn_to_f64
 _orig_packed = odec.decode_packed
 _orig_block_tokens = ores.block_tokens
+_orig_fp16 = odec.fp16_to_f64
 
 
 def _band_exclusive(mode, j, p, n, left, right):
@@ -102,6 +104,10 @@ def _v_from_rope(q, K, V, scale, sinks=None):
     return _orig_attend(q, K, K[:, -V.shape[1]:], scale, sinks)
 
 
+def _fp16_bias16(bits):
+    return _orig_fp16(bits) * 0.5                       # exponent bias 16 instead of 15
+
+
 def _block_offset_dropped(v, sbs):
     return [v + u for u in range(sbs)]                  # forgets the block stride
 
@@ -117,6 +123,7 @@ MUTANTS = {
     "packed_scale_tiles_reversed": (oatt, "decode_packed", _packed_scale_tiles_swapped),
     "value_taken_from_wrong_columns": (oatt, "attend", _v_from_rope),
     "block_offset_dropped": (ores, "block_tokens", _block_offset_dropped),
+    "fp16_exponent_bias_off_by_one": (odec, "fp16_to_f64", _fp16_bias16),
 }
 
 
