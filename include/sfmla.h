@@ -75,6 +75,10 @@ typedef enum sfmla_status {
 #define SFMLA_KV_BF16 0
 #define SFMLA_KV_INT8_PACKED 1     /* 512 int8 codes, rope bf16, 4 fp32 scales */
 #define SFMLA_KV_FP8_E4M3_PACKED 2 /* 512 OCP E4M3FN codes, rope bf16, 4 scales */
+#define SFMLA_KV_FP16 3            /* IEEE float16 q, kv (and V) and attention_out:
+                                      the pages' other 16-bit type, shared by
+                                      q and kv (SparseFlashAttention README,
+                                      约束说明; API page 参数说明 ori_kv)  */
 
 /* mask modes (API page 参数说明 ori_mask_mode / cmp_mask_mode) */
 #define SFMLA_MASK_NONE 0
@@ -161,7 +165,9 @@ typedef struct sfmla_lengths {
  * consecutive physical rows, which may include padding — API page 约束说明:
  * non-contiguous rows with inter-row padding are allowed).
  *
- *   q            bf16, contiguous (q_t, num_heads_q, 512 + rope)
+ *   q            bf16 (float16 for SFMLA_KV_FP16), contiguous
+ *                (q_t, num_heads_q, 512 + rope); "bf16" below reads float16
+ *                for that format
  *   ori_kv       bf16 rows: 512 nope values, then (if rope_head_dim = 64 and
  *                ori_rope is NULL) 64 rope values; packed rows: 512 codes,
  *                2*rope bytes of bf16 rope, 16 bytes of fp32 scales

@@ -173,7 +173,8 @@ class Call:
         self.params = make_params(self.spec, self.d)
         self.scale = float(self.spec["softmax_scale"])
         qn = self.params.num_heads_q
-        self.out = torch.empty((self.params.q_t, qn, 512), dtype=torch.bfloat16, device=self.device)
+        odt = torch.float16 if self.spec.get("kv_dtype") == "fp16" else torch.bfloat16
+        self.out = torch.empty((self.params.q_t, qn, 512), dtype=odt, device=self.device)
         self.lse = (torch.empty((self.params.q_t, qn), dtype=torch.float32, device=self.device)
                     if self.params.return_softmax_lse else None)
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SFMLA_LIB") or os.path.join(HERE, "libsfmla.so")
 
 LAYOUTS = {"BSND": 0, "TND": 1, "PA_BSND": 2, "PA_BBND": 2, "PA_ND": 2}
-KV_DTYPES = {"bf16": 0, "int8_packed": 1, "fp8_e4m3_packed": 2}
+KV_DTYPES = {"bf16": 0, "int8_packed": 1, "fp8_e4m3_packed": 2, "fp16": 3}
 STATUS = {0: "SFMLA_OK", 1: "SFMLA_ERR_INVALID_ARGUMENT", 2: "SFMLA_ERR_UNSUPPORTED",
           3: "SFMLA_ERR_BUFFER_TOO_SMALL", 4: "SFMLA_ERR_LAUNCH", 5: "SFMLA_ERR_METADATA"}
 STATUS_METADATA_MISMATCH = 1

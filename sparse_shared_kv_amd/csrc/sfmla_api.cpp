@@ -106,10 +106,11 @@ sfmla_status validate(const sfmla_params* pp) {
   }
   REQUIRE(p.ori_mask_mode == 0 || p.ori_mask_mode == 3 || p.ori_mask_mode == 4,
           "ori_mask_mode must be 0, 3 or 4");
-  REQUIRE(p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_INT8_PACKED ||
+  REQUIRE(p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_FP16 ||
+              p.kv_dtype == SFMLA_KV_INT8_PACKED ||
               p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED,
           "unknown kv_dtype");
-  REQUIRE(!(p.has_separate_v && p.kv_dtype != SFMLA_KV_BF16),
+  REQUIRE(!(p.has_separate_v && p.kv_dtype != SFMLA_KV_BF16 && p.kv_dtype != SFMLA_KV_FP16),
           "a separate V is only supported for bf16 KV (packed V is the dequantised nope)");
   if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.ori_kv_s > 0, "BSND ori_kv needs ori_kv_s > 0");
   if (p.layout_kv == SFMLA_LAYOUT_PA_BSND) {
@@ -198,7 +199,8 @@ size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total
 void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
   const int64_t units = (int64_t)p.q_t * max_splits(p);
   const int blocks = (p.num_heads_q + 15) / 16;        // 16-head blocks
-  const int wmax = p.kv_dtype == SFMLA_KV_BF16 ? 8 : 4;  // packed rows: more registers per wave
+  const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
+  const int wmax = packed ? 4 : 8;                     // packed rows: more registers per wave
   *nw = wmax;
   // SFMLA_BPG=<blocks per group> overrides the split of the heads (tuning aid)
   if (const char* env = getenv("SFMLA_BPG")) {
@@ -228,7 +230,7 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
   REQUIRE(std::isfinite(scale), "softmax_scale must be finite");
   REQUIRE(t->q && aligned16(t->q), "q must be a 16-byte aligned device pointer");
   REQUIRE(t->ori_kv && aligned16(t->ori_kv), "ori_kv must be a 16-byte aligned device pointer");
-  const bool packed = p.kv_dtype != SFMLA_KV_BF16;
+  const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int64_t need_row = packed ? 512 + 2 * p.rope_head_dim + 16
                                   : (p.rope_head_dim && !t->ori_rope ? 1152 : 1024);
   REQUIRE(t->ori_kv_stride >= need_row && t->ori_kv_stride % 16 == 0,

@@ -248,6 +248,41 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// The 16-bit element type of q, bf16 / fp16 kv, P and the outputs: bfloat16,
+// or IEEE float16 when the kv format is SFMLA_KV_FP16 (q, kv and the output
+// then share that type).  Vectors of 8 elements travel as bf16x8 bit
+// patterns either way.
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+template <bool HALF>
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (HALF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+template <bool HALF>
+__device__ __forceinline__ uint16_t to16(float f) {
+  if constexpr (HALF) return __builtin_bit_cast(uint16_t, (_Float16)f);
+  else return f2bf(f);
+}
+template <bool HALF>
+__device__ __forceinline__ __bf16 elem16(float f) {
+  if constexpr (HALF) return __builtin_bit_cast(__bf16, (_Float16)f);
+  else return (__bf16)f;
+}
+// element 0 / 1 of a pair packed in 32 bits
+template <bool HALF>
+__device__ __forceinline__ float lo16(uint32_t u) {
+  if constexpr (HALF) return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+  else return __builtin_bit_cast(float, u << 16);
+}
+template <bool HALF>
+__device__ __forceinline__ float hi16(uint32_t u) {
+  if constexpr (HALF) return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+  else return __builtin_bit_cast(float, u & 0xffff0000u);
+}
+
 // 16 stored codes -> 16 bf16 values (exact: INT8 and E4M3 values fit bf16).
 template <int FMT>
 __device__ __forceinline__ void codes_to_bf16(uint4 c, uint4& lo, uint4& hi) {
@@ -523,8 +558,11 @@ template <int NW, int HB, int DQK, int VMODE, int FMT>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   using C = Pipe<NW, DQK, VMODE>;
   using PP = PackedPipe<NW, DQK>;
-  constexpr bool PK = FMT != SFMLA_KV_BF16;       // packed rows (V = decoded nope)
+  constexpr bool HALF = FMT == SFMLA_KV_FP16;     // float16 q / kv / P / output
+  constexpr bool PK = FMT != SFMLA_KV_BF16 && !HALF;   // packed rows (V = decoded nope)
   static_assert(!PK || VMODE == 0, "packed KV has no separate V");
+  static_assert(FMT == SFMLA_KV_BF16 || FMT == SFMLA_KV_INT8_PACKED ||
+                FMT == SFMLA_KV_FP8_E4M3_PACKED || FMT == SFMLA_KV_FP16, "KV format");
   constexpr bool BROPE = C::ROPE && !PK;          // rope gathered from its own address
   constexpr int T = C::T;
   constexpr int NKS = DQK / 32;
@@ -573,7 +611,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         const int h = h0 + 16 * hb + t;
         if (!wave_on || h >= a.qn) continue;
         uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
-        for (int c = g; c < 512; c += 4) op[c] = f2bf(nan);
+        for (int c = g; c < 512; c += 4) op[c] = to16<HALF>(nan);
         if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = nan;
       }
       if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_METADATA_MISMATCH);
@@ -593,7 +631,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         const int h = h0 + 16 * hb + t;
         if (!wave_on || h >= a.qn) continue;
         uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
-        for (int c = g; c < 512; c += 4) op[c] = f2bf(__builtin_nanf(""));
+        for (int c = g; c < 512; c += 4) op[c] = to16<HALF>(__builtin_nanf(""));
         if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = __builtin_nanf("");
       }
       if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_LIST_TOO_LONG);
@@ -735,17 +773,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         if (PK && ks < 16) {
           // exact scaling: one partial product per 128-column scale tile
           const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-          sp[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qreg[hb][ks],
-                                                              ks % 4 ? sp[hb][0] : z, 0, 0, 0);
-          sp[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qreg[hb][ks],
-                                                              ks % 4 ? sp[hb][1] : z, 0, 0, 0);
+          sp[hb][0] = mfma16<HALF>(k0v, qreg[hb][ks], ks % 4 ? sp[hb][0] : z);
+          sp[hb][1] = mfma16<HALF>(k1v, qreg[hb][ks], ks % 4 ? sp[hb][1] : z);
           if (ks % 4 == 3) {
             s[hb][0] += sp[hb][0] * sc[PK ? ks / 4 : 0][0];
             s[hb][1] += sp[hb][1] * sc[PK ? ks / 4 : 0][1];
           }
         } else {
-          s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qreg[hb][ks], s[hb][0], 0, 0, 0);
-          s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qreg[hb][ks], s[hb][1], 0, 0, 0);
+          s[hb][0] = mfma16<HALF>(k0v, qreg[hb][ks], s[hb][0]);
+          s[hb][1] = mfma16<HALF>(k1v, qreg[hb][ks], s[hb][1]);
         }
       }
       if (ks + PF < NKS) kload(ks + PF, kb[ks % PF][0], kb[ks % PF][1]);
@@ -778,9 +814,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         psum += pj;
         if constexpr (PK) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) pbt[u][hb][j] = (__bf16)(pj * sc[PK ? u : 0][j >> 2][j & 3]);
+          for (int u = 0; u < 4; ++u) pbt[u][hb][j] = elem16<HALF>(pj * sc[PK ? u : 0][j >> 2][j & 3]);
         } else {
-          pb[hb][j] = (__bf16)pj;
+          pb[hb][j] = elem16<HALF>(pj);
         }
       }
       l_run[hb] = l_run[hb] * alpha[hb] + psum;
@@ -813,8 +849,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           bf16x8, __builtin_shufflevector(vb[mb % PV][0], vb[mb % PV][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
-        o[hb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, PK ? pbt[PK ? mb >> 3 : 0][hb] : pb[hb],
-                                                            o[hb][mb], 0, 0, 0);
+        o[hb][mb] = mfma16<HALF>(va, PK ? pbt[PK ? mb >> 3 : 0][hb] : pb[hb], o[hb][mb]);
       if (mb + PV < 32) vload(mb + PV, vb[mb % PV][0], vb[mb % PV][1]);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -913,8 +948,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 32; ++mb) {
       uint2 pk;
-      pk.x = (uint32_t)f2bf(o[hb][mb][0] * inv) | ((uint32_t)f2bf(o[hb][mb][1] * inv) << 16);
-      pk.y = (uint32_t)f2bf(o[hb][mb][2] * inv) | ((uint32_t)f2bf(o[hb][mb][3] * inv) << 16);
+      pk.x = (uint32_t)to16<HALF>(o[hb][mb][0] * inv) | ((uint32_t)to16<HALF>(o[hb][mb][1] * inv) << 16);
+      pk.y = (uint32_t)to16<HALF>(o[hb][mb][2] * inv) | ((uint32_t)to16<HALF>(o[hb][mb][3] * inv) << 16);
       *(uint2*)(op + 16 * mb) = pk;
     }
     if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = den > 0.f ? l2 * kLn2 : kNegInf;
@@ -952,12 +987,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       uint4 pk;
-      pk.x = (uint32_t)f2bf(o[hb][2 * j][0] * inv) | ((uint32_t)f2bf(o[hb][2 * j][1] * inv) << 16);
-      pk.y = (uint32_t)f2bf(o[hb][2 * j][2] * inv) | ((uint32_t)f2bf(o[hb][2 * j][3] * inv) << 16);
-      pk.z = (uint32_t)f2bf(o[hb][2 * j + 1][0] * inv) |
-             ((uint32_t)f2bf(o[hb][2 * j + 1][1] * inv) << 16);
-      pk.w = (uint32_t)f2bf(o[hb][2 * j + 1][2] * inv) |
-             ((uint32_t)f2bf(o[hb][2 * j + 1][3] * inv) << 16);
+      pk.x = (uint32_t)to16<HALF>(o[hb][2 * j][0] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][1] * inv) << 16);
+      pk.y = (uint32_t)to16<HALF>(o[hb][2 * j][2] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][3] * inv) << 16);
+      pk.z = (uint32_t)to16<HALF>(o[hb][2 * j + 1][0] * inv) |
+             ((uint32_t)to16<HALF>(o[hb][2 * j + 1][1] * inv) << 16);
+      pk.w = (uint32_t)to16<HALF>(o[hb][2 * j + 1][2] * inv) |
+             ((uint32_t)to16<HALF>(o[hb][2 * j + 1][3] * inv) << 16);
       const u32x4 d = {pk.x, pk.y, pk.z, pk.w};
       __builtin_amdgcn_raw_buffer_store_b128(d, rs, wave_off + ((hb * 16 + j) * 64 + l) * 16, 0, kSc1);
     }
@@ -1047,8 +1082,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           const uint32_t u[4] = {v[q][j].x, v[q][j].y, v[q][j].z, v[q][j].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[j][2 * e] += ws * __builtin_bit_cast(float, u[e] << 16);
-            acc[j][2 * e + 1] += ws * __builtin_bit_cast(float, u[e] & 0xffff0000u);
+            acc[j][2 * e] += ws * lo16<HALF>(u[e]);
+            acc[j][2 * e + 1] += ws * hi16<HALF>(u[e]);
           }
         }
       }
@@ -1058,10 +1093,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         for (int j = 0; j < JB; ++j) {
           const int jj = jr * JB + j;
           uint2 p0, p1;
-          p0.x = (uint32_t)f2bf(acc[j][0] * inv) | ((uint32_t)f2bf(acc[j][1] * inv) << 16);
-          p0.y = (uint32_t)f2bf(acc[j][2] * inv) | ((uint32_t)f2bf(acc[j][3] * inv) << 16);
-          p1.x = (uint32_t)f2bf(acc[j][4] * inv) | ((uint32_t)f2bf(acc[j][5] * inv) << 16);
-          p1.y = (uint32_t)f2bf(acc[j][6] * inv) | ((uint32_t)f2bf(acc[j][7] * inv) << 16);
+          p0.x = (uint32_t)to16<HALF>(acc[j][0] * inv) | ((uint32_t)to16<HALF>(acc[j][1] * inv) << 16);
+          p0.y = (uint32_t)to16<HALF>(acc[j][2] * inv) | ((uint32_t)to16<HALF>(acc[j][3] * inv) << 16);
+          p1.x = (uint32_t)to16<HALF>(acc[j][4] * inv) | ((uint32_t)to16<HALF>(acc[j][5] * inv) << 16);
+          p1.y = (uint32_t)to16<HALF>(acc[j][6] * inv) | ((uint32_t)to16<HALF>(acc[j][7] * inv) << 16);
           *(uint2*)(op + 16 * (2 * jj)) = p0;
           *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
         }
@@ -1196,6 +1231,12 @@ hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt,
       if (nw != 4) return hipErrorInvalidConfiguration;
       return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s)
                         : launch_fwd_t<4, 576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s);
+    case SFMLA_KV_FP16:
+      if (nw != 8) return hipErrorInvalidConfiguration;
+      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, SFMLA_KV_FP16>(a, groups, s)
+                                   : launch_fwd_t<8, 512, 0, SFMLA_KV_FP16>(a, groups, s);
+      return vmode ? launch_fwd_t<8, 576, 1, SFMLA_KV_FP16>(a, groups, s)
+                   : launch_fwd_t<8, 576, 0, SFMLA_KV_FP16>(a, groups, s);
     default:
       if (nw != 8) return hipErrorInvalidConfiguration;
       if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, 0>(a, groups, s)

@@ -79,6 +79,14 @@ TINY += [dict(seed=700 + s, family="sfa", sparse_block_size=[2, 4, 16, 64][s % 4
               max_kv=300, num_heads_q=[16, 64, 128][s % 3],
               kv_dtype=["bf16", "bf16", "int8_packed", "fp8_e4m3_packed"][(s // 2) % 4],
               duplicates=bool(s % 5 == 4)) for s in range(10)]
+# float16 q / kv / output: every family, peaked softmaxes, long lists
+TINY += [dict(seed=800 + s, kv_dtype="fp16", family=["swa", "csa", "hca", "sfa"][s % 4],
+              dist=["normal", "p4"][(s // 4) % 2], num_heads_q=[16, 64, 128, 5][s % 4])
+         for s in range(8)]
+TINY += [dict(seed=810, kv_dtype="fp16", family="sfa", max_kv=2600, topk=1300, rope_head_dim=64,
+              separate_v=True, num_heads_q=128, layout_q="TND", layout_kv="PA_BSND", block_size=64),
+         dict(seed=811, kv_dtype="fp16", family="hca", max_kv=2200, cmp_ratio=1, masks=(0, 3),
+              num_heads_q=32)]
 TINY += [dict(seed=720, family="sfa", sparse_block_size=16, max_kv=3000, topk=120,
               num_heads_q=128, layout_q="BSND", layout_kv="PA_BSND", block_size=64),
          dict(seed=721, family="sfa", sparse_block_size=8, max_kv=2500, topk=250,
