@@ -34,6 +34,10 @@ DESCR = {
     "sfa_mla_rope": "token-wise sparse MLA-absorb decode with rope: B=32, q_s=2, q_n=128, "
                     "d_qk=576 (512+64 rope), separate V (512), TopK 2048 of 65536 cached tokens, "
                     "PA_BSND block 64, bf16",
+    "sfa_mla_rope_fp16": "the headline decode in float16 (q, K, V and output): B=32, q_s=2, "
+                         "q_n=128, d_qk=576, separate V, TopK 2048 of 65536 tokens, PA block 64",
+    "sfa_mla_rope_block16": "the headline decode with block-wise TopK: 128 entries of 16 "
+                            "consecutive tokens (2048 tokens) per query, bf16, PA block 64",
     "c8_packed_int8": "INT8 per-128-tile packed KV (656-B rows), TND B=8, q_n=128, d_qk=576, "
                       "TopK 2048 of 16K-131K tokens",
     "c8_packed_fp8": "FP8-E4M3 per-128-tile packed KV (656-B rows), TND B=8, q_n=128, d_qk=576, "
@@ -59,7 +63,7 @@ def row_bytes(P) -> tuple:
     """Bytes of one gathered KV row and flops per (row, head)."""
     p = P.params
     d_qk = 512 + int(p["rope_head_dim"])
-    if p["kv_dtype"] == "bf16":
+    if p["kv_dtype"] in ("bf16", "fp16"):
         b = 2 * d_qk + (1024 if p.get("separate_v") else 0)
     else:
         b = 512 + 2 * int(p["rope_head_dim"]) + 16
@@ -350,7 +354,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": P.params["kv_dtype"] if P.params["kv_dtype"] != "bf16" else "bf16",
+        "dtype": P.params["kv_dtype"],
         "data": "synthetic (seeded; %s)" % P.recipe,
         "config": {"workload": args.workload, "description": DESCR[args.workload],
                    "query_rows": int(P.query_rows), "q_n": qn,

@@ -159,31 +159,36 @@ def hca_varlen(seed=3):
                    "contexts %s" % L.tolist())
 
 
-def _sfa_indices(seq, batch, q_s, kv_len, topk):
+def _sfa_indices(seq, batch, q_s, kv_len, topk, sbs=1):
+    """Entries drawn without replacement from the causal range of each query;
+    with sbs > 1 they are blocks of sbs tokens (the blocks whose first token
+    is causal for the query)."""
     g_idx = _gen(seq)
     rows = []
     for _b in range(batch):
         for s in range(q_s):
             # query s of a q_s-token step sits at position kv_len - q_s + s,
             # so positions 0 .. kv_len - q_s + s are its causal range
-            rows.append(g_idx.choice(kv_len - q_s + s + 1, topk, replace=False))
+            rows.append(g_idx.choice((kv_len - q_s + s) // sbs + 1, topk, replace=False))
     return np.stack(rows).astype(np.int32).reshape(batch * q_s, 1, topk)
 
 
-def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64):
+def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64, fp16=False, sbs=1):
     """Token-wise sparse MLA-absorb with rope: B=32, q_s=2, q_n=128, Q_D=576,
     separate K (576) and V (512) bf16 pools, PA block 64, kv length 65536,
-    TopK 2048 drawn uniformly from the causal positions, scale 1/sqrt(576)."""
+    TopK 2048 drawn uniformly from the causal positions, scale 1/sqrt(576).
+    fp16: the same in float16; sbs > 1: topk / sbs entries of sbs-token
+    blocks (block-wise TopK, the same 2048 tokens per query)."""
     s_q, s_k, s_v, s_tab, s_idx = _seqs(seed, 5)
     qn, dq = 128, 576
     nblk = batch * kv_len // bs
     g_tab = _gen(s_tab)
     bt = g_tab.permutation(nblk).astype(np.int32).reshape(batch, kv_len // bs)
-    idx = _sfa_indices(s_idx, batch, q_s, kv_len, topk)
+    idx = _sfa_indices(s_idx, batch, q_s, kv_len, topk // sbs, sbs)
     arrays = dict(
-        q=normal_bf16(s_q, (batch * q_s, qn, dq)),
-        ori_kv=banked_rows(s_k, nblk * bs, lambda s, n: normal_bf16(s, (n, dq))),
-        ori_v=banked_rows(s_v, nblk * bs, lambda s, n: normal_bf16(s, (n, 512))),
+        q=normal_bf16(s_q, (batch * q_s, qn, dq), fp16=fp16),
+        ori_kv=banked_rows(s_k, nblk * bs, lambda s, n: normal_bf16(s, (n, dq), fp16=fp16)),
+        ori_v=banked_rows(s_v, nblk * bs, lambda s, n: normal_bf16(s, (n, 512), fp16=fp16)),
         ori_block_table=bt,
         seqused_ori_kv=np.full(batch, kv_len, np.int32),
         ori_sparse_indices=idx,
@@ -191,11 +196,14 @@ def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64):
     params = _base_params(
         num_heads_q=qn, rope_head_dim=64, batch_size=batch, layout_q="BSND",
         layout_kv="PA_BSND", q_s=q_s, q_t=batch * q_s, ori_block_size=bs,
-        max_seqlen_q=q_s, max_seqlen_ori_kv=kv_len, ori_topk=topk,
-        ori_mask_mode=3, has_cmp_kv=False, separate_v=True,
-        softmax_scale=1.0 / math.sqrt(dq))
-    return Problem("sfa_mla_rope", seed, params, arrays,
-                   "q, K, V ~ N(0,1) bf16; %d of the causal positions" % topk)
+        max_seqlen_q=q_s, max_seqlen_ori_kv=kv_len, ori_topk=topk // sbs,
+        ori_mask_mode=3, has_cmp_kv=False, separate_v=True, sparse_block_size=sbs,
+        kv_dtype="fp16" if fp16 else "bf16", softmax_scale=1.0 / math.sqrt(dq))
+    name = "sfa_mla_rope" + ("_fp16" if fp16 else "") + ("_block%d" % sbs if sbs > 1 else "")
+    what = ("%d blocks of %d causal tokens" % (topk // sbs, sbs)) if sbs > 1 else (
+        "%d of the causal positions" % topk)
+    return Problem(name, seed, params, arrays,
+                   "q, K, V ~ N(0,1) %s; %s" % ("float16" if fp16 else "bf16", what))
 
 
 def _c8_indices(seq, L, topk):
@@ -236,6 +244,8 @@ WORKLOADS = {
     "csa_decode_paged": csa_decode_paged,
     "hca_varlen": hca_varlen,
     "sfa_mla_rope": sfa_mla_rope,
+    "sfa_mla_rope_fp16": lambda seed=4: sfa_mla_rope(seed, fp16=True),
+    "sfa_mla_rope_block16": lambda seed=4: sfa_mla_rope(seed, sbs=16),
     "c8_packed_int8": lambda seed=5: c8_packed(seed, "int8"),
     "c8_packed_fp8": lambda seed=5: c8_packed(seed, "fp8"),
 }
@@ -253,10 +263,11 @@ def index_replicas(P: Problem, n: int):
     out = []
     for r in range(n):
         seq = np.random.SeedSequence([P.seed, 7919, r])
-        if P.name == "sfa_mla_rope":
+        if P.name.startswith("sfa_mla_rope"):
             p = P.params
             out.append(("ori_sparse_indices", _sfa_indices(
-                seq, p["batch_size"], p["q_s"], p["max_seqlen_ori_kv"], p["ori_topk"])))
+                seq, p["batch_size"], p["q_s"], p["max_seqlen_ori_kv"], p["ori_topk"],
+                p["sparse_block_size"])))
         elif P.name.startswith("c8_packed"):
             cu = P.arrays["cu_seqlens_ori_kv"]
             out.append(("ori_sparse_indices", _c8_indices(seq, np.diff(cu), P.params["ori_topk"])))
