@@ -47,6 +47,9 @@ DESCR = {
     "csa_decode_paged": "CSA paged decode: B=4, q_n=64, window 128 + TopK 512 of 8192 "
                         "compressed rows (ratio 4), PA block 128, sinks",
     "swa_decode": "SWA decode: B=2, q_n=16, window 128 of 512, BSND",
+    "csa_prefill": "CSA prefill (the SparseAttnSharedkv call example's shapes): B=4 x 128 "
+                   "query tokens, q_n=64, window 128 + TopK 512 of 1024 compressed rows "
+                   "(ratio 4), 4096 cached tokens, PA block 128, sinks",
 }
 
 

@@ -127,6 +127,45 @@ def csa_decode_paged(seed=2):
                    "q, kv ~ N(0,1) bf16; 512 of 8192 compressed rows per query")
 
 
+def csa_prefill(seed=6):
+    """CSA prefill with the shapes of the SparseAttnSharedkv README's call
+    example: B=4 sequences of 128 query tokens (TND), q_n=64, d=512, 4096
+    cached tokens each in 128-token pages, window (127, 0), cmp_ratio 4 (1024
+    compressed rows) with one TopK list of 512 compressed rows drawn from the
+    first 1024 - 128 + 1 and shared by every query token, causal cmp mask,
+    sinks ~ U(0, 1); q ~ U(-10, 10) and kv ~ U(-5, 10) as in the example."""
+    s_q, s_ori, s_cmp, s_tab, s_idx, s_sink = _seqs(seed, 6)
+    B, s1, qn, d, bs, L, r, K = 4, 128, 64, 512, 128, 4096, 4, 512
+    C = L // r
+    g_tab = _gen(s_tab)
+    ori_blocks = B * L // bs
+    ori_bt = g_tab.permutation(ori_blocks).astype(np.int32).reshape(B, L // bs)
+    cmp_blocks = B * ((C + bs - 1) // bs)
+    cmp_bt = g_tab.permutation(cmp_blocks).astype(np.int32).reshape(B, cmp_blocks // B)
+    one = _gen(s_idx).choice(C - s1 + 1, K, replace=False).astype(np.int32)
+    idx = np.broadcast_to(one, (B * s1, 1, K)).copy()
+    arrays = dict(
+        q=bf16_bits(_gen(s_q).uniform(-10, 10, (B * s1, qn, d)).astype(np.float32)),
+        ori_kv=bf16_bits(_gen(s_ori).uniform(-5, 10, (ori_blocks * bs, d)).astype(np.float32)),
+        cmp_kv=bf16_bits(_gen(s_cmp).uniform(-5, 10, (cmp_blocks * bs, d)).astype(np.float32)),
+        ori_block_table=ori_bt, cmp_block_table=cmp_bt,
+        cu_seqlens_q=_prefix([s1] * B),
+        seqused_ori_kv=np.full(B, L, np.int32),
+        seqused_cmp_kv=np.full(B, C, np.int32),
+        cmp_residual_kv=np.zeros(B, np.int32),
+        cmp_sparse_indices=idx,
+        sinks=_gen(s_sink).uniform(0, 1, qn).astype(np.float32),
+    )
+    params = _base_params(
+        num_heads_q=qn, batch_size=B, layout_q="TND", layout_kv="PA_BSND",
+        q_t=B * s1, ori_block_size=bs, cmp_block_size=bs, max_seqlen_q=s1,
+        max_seqlen_ori_kv=L, max_seqlen_cmp_kv=C, cmp_topk=K, cmp_ratio=r,
+        ori_mask_mode=4, ori_win_left=127, ori_win_right=0, cmp_mask_mode=3,
+        has_cmp_kv=True, softmax_scale=1.0 / 24.0)
+    return Problem("csa_prefill", seed, params, arrays,
+                   "q ~ U(-10,10), kv ~ U(-5,10) bf16; 128 query tokens per sequence")
+
+
 def _varlen_lengths(seed):
     (s_len,) = _seqs(seed * 1000 + 7, 1)
     return _gen(s_len).integers(16384, 131072 + 1, size=8).astype(np.int64)
@@ -242,6 +281,7 @@ def c8_packed(seed=5, fmt="int8", topk=2048):
 WORKLOADS = {
     "swa_decode": swa_decode,
     "csa_decode_paged": csa_decode_paged,
+    "csa_prefill": csa_prefill,
     "hca_varlen": hca_varlen,
     "sfa_mla_rope": sfa_mla_rope,
     "sfa_mla_rope_fp16": lambda seed=4: sfa_mla_rope(seed, fp16=True),
