@@ -151,9 +151,27 @@ int64_t max_list(const sfmla_params& p) {
   return n;
 }
 
+// KV rows per split: a function of the parameters only (never of the batch),
+// so a query row is split the same way in any batch.  Rows of 2 KB or more
+// (a K row with rope plus a separate V row) get 512-row splits, which keep
+// the number of partials to merge low; lighter rows (1 KB bf16 rows with
+// V = K, packed rows) get 256-row splits, which keep each workgroup's serial
+// chain of tiles short (measured on the six workloads of the benchmark).
+// SFMLA_SPLIT_ROWS (a multiple of 32 up to 512) overrides it (tuning aid).
+int split_rows(const sfmla_params& p) {
+  if (const char* env = getenv("SFMLA_SPLIT_ROWS")) {
+    const int v = atoi(env);
+    if (v >= sfmla::kTile && v <= sfmla::kSplitRows && v % sfmla::kTile == 0) return v;
+  }
+  const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
+  const int row_bytes = packed ? 512 + 2 * p.rope_head_dim + 16
+                               : 2 * (512 + p.rope_head_dim) + (p.has_separate_v ? 1024 : 0);
+  return row_bytes >= 2048 ? sfmla::kSplitRows : sfmla::kSplitRows / 2;
+}
+
 int max_splits(const sfmla_params& p) {
   const int64_t n = max_list(p);
-  const int64_t s = (n + sfmla::kSplitRows - 1) / sfmla::kSplitRows;
+  const int64_t s = (n + split_rows(p) - 1) / split_rows(p);
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, 4096));
 }
 
@@ -371,6 +389,7 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
   a.meta = metadata;
   a.fingerprint = fingerprint(p);
   a.max_splits = max_splits(p);
+  a.split_rows = split_rows(p);
   hipError_t e = sfmla::launch_plan(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "plan launch: %s", hipGetErrorString(e));
   return ok();

@@ -9,7 +9,7 @@
 namespace sfmla {
 
 constexpr int kTile = 32;          // KV rows staged in LDS per step
-constexpr int kSplitRows = 512;    // KV rows per split of one query row
+constexpr int kSplitRows = 512;    // most KV rows per split of one query row (LDS tables)
 constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
 constexpr int kCounterInts = 64;   // arrival counters per query row (one per head group x wave)
@@ -41,6 +41,7 @@ struct PlanArgs {
   int32_t* meta;
   uint32_t fingerprint;
   int32_t max_splits;
+  int32_t split_rows;               // KV rows per split (multiple of the tile, <= kSplitRows)
 };
 
 struct FwdArgs {

@@ -218,8 +218,8 @@ __global__ void plan_kernel(PlanArgs a) {
   }
   if (!valid) { ori_cnt = 0; cmp_cnt = 0; }
   const int n = ori_cnt + cmp_cnt;
-  int nsplit = n > 0 ? (n + kSplitRows - 1) / kSplitRows : 1;
-  int chunk = kSplitRows;
+  int nsplit = n > 0 ? (n + a.split_rows - 1) / a.split_rows : 1;
+  int chunk = a.split_rows;
   if (nsplit > a.max_splits) {
     nsplit = a.max_splits;
     chunk = (n + nsplit - 1) / nsplit;
