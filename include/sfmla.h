@@ -107,8 +107,10 @@ typedef struct sfmla_params {
   int32_t cmp_block_size;   /* PA: tokens per cmp block (1..1024); else 0     */
   int32_t ori_block_table_cols; /* PA: entries per ori block-table row        */
   int32_t cmp_block_table_cols; /* PA: entries per cmp block-table row        */
-  int64_t ori_kv_rows;   /* physical rows in the ori pool (all blocks)        */
-  int64_t cmp_kv_rows;   /* physical rows in the cmp pool (0 if none)         */
+  int64_t ori_kv_rows;   /* physical rows in the ori pool (all blocks),
+                            < 2^31 - 1 (row ids are 31-bit on the device)   */
+  int64_t cmp_kv_rows;   /* physical rows in the cmp pool (0 if none),
+                            < 2^31 - 1                                       */
   int32_t max_seqlen_q;      /* > 0                                           */
   int32_t max_seqlen_ori_kv; /* > 0: longest ori length of any batch          */
   int32_t max_seqlen_cmp_kv; /* longest cmp length (0 without cmp_kv)         */

@@ -92,7 +92,7 @@ sfmla_status validate(const sfmla_params* pp) {
   REQUIRE(p.has_ori_kv == 1, "ori_kv is required");
   REQUIRE(p.max_seqlen_ori_kv > 0, "max_seqlen_ori_kv must be > 0");
   REQUIRE(p.ori_kv_rows > 0, "ori_kv_rows must be > 0");
-  REQUIRE(p.ori_kv_rows < ((int64_t)1 << 40), "ori_kv_rows too large");
+  REQUIRE(p.ori_kv_rows < ((int64_t)1 << 31) - 1, "ori_kv_rows must be < 2^31 - 1");
   REQUIRE(p.ori_win_left >= -1 && p.ori_win_right >= -1, "window bounds must be -1 or >= 0");
   REQUIRE(p.ori_topk >= 0 && p.cmp_topk >= 0, "topk must be >= 0");
   {
@@ -122,7 +122,8 @@ sfmla_status validate(const sfmla_params* pp) {
     REQUIRE(p.has_cmp_kv == 1, "has_cmp_kv must be 0 or 1");
     REQUIRE(p.cmp_ratio >= 1, "cmp_ratio must be >= 1");
     REQUIRE(p.cmp_mask_mode == 0 || p.cmp_mask_mode == 3, "cmp_mask_mode must be 0 or 3");
-    REQUIRE(p.cmp_kv_rows > 0 && p.cmp_kv_rows < ((int64_t)1 << 40), "cmp_kv_rows out of range");
+    REQUIRE(p.cmp_kv_rows > 0 && p.cmp_kv_rows < ((int64_t)1 << 31) - 1,
+            "cmp_kv_rows must be in 1..2^31 - 2");
     if (p.cmp_mask_mode == 3)
       REQUIRE(p.has_cmp_residual_kv, "cmp_mask_mode 3 needs cmp_residual_kv");
     if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.cmp_kv_s > 0, "BSND cmp_kv needs cmp_kv_s > 0");
@@ -152,21 +153,24 @@ int64_t max_list(const sfmla_params& p) {
 }
 
 // KV rows per split: a function of the parameters only (never of the batch),
-// so a query row is split the same way in any batch.  Rows of 2 KB or more
+// so a query row is split the same way in any batch (the planner lets rows
+// of sequences with at least kLongQuery queries take up to kMaxSplitRows per
+// split instead, a property of the row's own sequence).  Rows of 2 KB or more
 // (a K row with rope plus a separate V row) get 512-row splits, which keep
 // the number of partials to merge low; lighter rows (1 KB bf16 rows with
 // V = K, packed rows) get 256-row splits, which keep each workgroup's serial
 // chain of tiles short (measured on the six workloads of the benchmark).
-// SFMLA_SPLIT_ROWS (a multiple of 32 up to 512) overrides it (tuning aid).
+// SFMLA_SPLIT_ROWS (a multiple of 32 up to kMaxSplitRows) overrides it
+// (tuning aid).
 int split_rows(const sfmla_params& p) {
   if (const char* env = getenv("SFMLA_SPLIT_ROWS")) {
     const int v = atoi(env);
-    if (v >= sfmla::kTile && v <= sfmla::kSplitRows && v % sfmla::kTile == 0) return v;
+    if (v >= sfmla::kTile && v <= sfmla::kMaxSplitRows && v % sfmla::kTile == 0) return v;
   }
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int row_bytes = packed ? 512 + 2 * p.rope_head_dim + 16
                                : 2 * (512 + p.rope_head_dim) + (p.has_separate_v ? 1024 : 0);
-  return row_bytes >= 2048 ? sfmla::kSplitRows : sfmla::kSplitRows / 2;
+  return row_bytes >= 2048 ? 512 : 256;
 }
 
 int max_splits(const sfmla_params& p) {
@@ -251,6 +255,11 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int64_t need_row = packed ? 512 + 2 * p.rope_head_dim + 16
                                   : (p.rope_head_dim && !t->ori_rope ? 1152 : 1024);
+  constexpr int64_t kMaxStride = ((int64_t)1 << 31) - 16;   // device row offsets are 32 x 32 bit
+  REQUIRE(t->ori_kv_stride <= kMaxStride && t->ori_rope_stride <= kMaxStride &&
+              t->ori_v_stride <= kMaxStride && t->cmp_kv_stride <= kMaxStride &&
+              t->cmp_rope_stride <= kMaxStride,
+          "row strides must be < 2^31 bytes");
   REQUIRE(t->ori_kv_stride >= need_row && t->ori_kv_stride % 16 == 0,
           "ori_kv_stride must be >= %lld bytes and a multiple of 16", (long long)need_row);
   if (t->ori_rope) {
@@ -315,15 +324,21 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
   f.meta = meta;
   f.q = (const uint16_t*)t->q;
   f.ori_kv = (const char*)t->ori_kv;
-  f.ori_stride = t->ori_kv_stride;
+  f.ori_stride = (uint32_t)t->ori_kv_stride;
   f.ori_rope = (const char*)t->ori_rope;
-  f.ori_rope_stride = t->ori_rope_stride;
+  f.ori_rope_stride = (uint32_t)t->ori_rope_stride;
   f.ori_v = (const char*)t->ori_v;
-  f.ori_v_stride = t->ori_v_stride;
+  f.ori_v_stride = (uint32_t)t->ori_v_stride;
   f.cmp_kv = (const char*)t->cmp_kv;
-  f.cmp_stride = t->cmp_kv_stride;
+  f.cmp_stride = (uint32_t)t->cmp_kv_stride;
   f.cmp_rope = (const char*)t->cmp_rope;
-  f.cmp_rope_stride = t->cmp_rope_stride;
+  f.cmp_rope_stride = (uint32_t)t->cmp_rope_stride;
+  // The kernel takes every row address as base + row * stride: a V that is
+  // the K nope and a rope stored after the nope become bases of their own.
+  if (!f.ori_v) { f.ori_v = f.ori_kv; f.ori_v_stride = f.ori_stride; }
+  if (!f.ori_rope) { f.ori_rope = f.ori_kv + 1024; f.ori_rope_stride = f.ori_stride; }
+  if (!f.cmp_kv) { f.cmp_kv = f.ori_kv; f.cmp_stride = f.ori_stride; }
+  if (!f.cmp_rope) { f.cmp_rope = f.cmp_kv + 1024; f.cmp_rope_stride = f.cmp_stride; }
   f.ori_bt = t->ori_block_table;
   f.cmp_bt = t->cmp_block_table;
   f.ori_idx = t->ori_sparse_indices;
@@ -390,6 +405,7 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
   a.fingerprint = fingerprint(p);
   a.max_splits = max_splits(p);
   a.split_rows = split_rows(p);
+  a.split_rows_long = std::max(a.split_rows, sfmla::kMaxSplitRows);
   hipError_t e = sfmla::launch_plan(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "plan launch: %s", hipGetErrorString(e));
   return ok();

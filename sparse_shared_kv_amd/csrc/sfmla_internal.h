@@ -9,7 +9,8 @@
 namespace sfmla {
 
 constexpr int kTile = 32;          // KV rows staged in LDS per step
-constexpr int kSplitRows = 512;    // most KV rows per split of one query row (LDS tables)
+constexpr int kMaxSplitRows = 2048;   // most KV rows per split of one query row (LDS row table)
+constexpr int kLongQuery = 64;     // queries of a sequence from which its rows split less
 constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
 constexpr int kCounterInts = 64;   // arrival counters per query row (one per head group x wave)
@@ -41,7 +42,8 @@ struct PlanArgs {
   int32_t* meta;
   uint32_t fingerprint;
   int32_t max_splits;
-  int32_t split_rows;               // KV rows per split (multiple of the tile, <= kSplitRows)
+  int32_t split_rows;               // KV rows per split (multiple of the tile, <= kMaxSplitRows)
+  int32_t split_rows_long;          // the same for rows of sequences of >= kLongQuery queries
 };
 
 struct FwdArgs {
@@ -57,11 +59,12 @@ struct FwdArgs {
   float scale_log2;                 // softmax_scale * log2(e)
   const int32_t* meta;
   const uint16_t* q;
-  const char* ori_kv;   int64_t ori_stride;
-  const char* ori_rope; int64_t ori_rope_stride;
-  const char* ori_v;    int64_t ori_v_stride;
-  const char* cmp_kv;   int64_t cmp_stride;
-  const char* cmp_rope; int64_t cmp_rope_stride;
+  // row strides in bytes (< 2^31, so a row's offset is one 32 x 32 -> 64 multiply-add)
+  const char* ori_kv;   uint32_t ori_stride;
+  const char* ori_rope; uint32_t ori_rope_stride;
+  const char* ori_v;    uint32_t ori_v_stride;
+  const char* cmp_kv;   uint32_t cmp_stride;
+  const char* cmp_rope; uint32_t cmp_rope_stride;
   const int32_t* ori_bt;
   const int32_t* cmp_bt;
   const int32_t* ori_idx;

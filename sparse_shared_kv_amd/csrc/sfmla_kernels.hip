@@ -218,8 +218,13 @@ __global__ void plan_kernel(PlanArgs a) {
   }
   if (!valid) { ori_cnt = 0; cmp_cnt = 0; }
   const int n = ori_cnt + cmp_cnt;
-  int nsplit = n > 0 ? (n + a.split_rows - 1) / a.split_rows : 1;
-  int chunk = a.split_rows;
+  // A sequence with many queries already gives the launch many rows: its
+  // rows keep their list in as few splits as the row table allows, which
+  // saves the partials' round trip and merge.  Depends on the row's own
+  // sequence only, so a sequence splits the same way in any batch.
+  const int srows = q_used >= kLongQuery ? a.split_rows_long : a.split_rows;
+  int nsplit = n > 0 ? (n + srows - 1) / srows : 1;
+  int chunk = srows;
   if (nsplit > a.max_splits) {
     nsplit = a.max_splits;
     chunk = (n + nsplit - 1) / nsplit;
@@ -423,46 +428,82 @@ struct Pipe {
   static constexpr int KBYTES = T * RSTR + (ROPE ? T * 128 : 0);
 };
 
+// A resolved list position, as kept in LDS: the physical row id, with bit 31
+// set for the compressed KV; kNoRow for an empty or masked slot, which reads
+// the zero row.  Row ids stay below 2^31 - 1 (checked on the host).
+constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+constexpr uint32_t kCmpBit = 0x80000000u;
+
+__device__ __forceinline__ const char* row_at(const char* base, uint32_t phys, uint32_t stride) {
+  return base + (uint64_t)phys * stride;
+}
+// (the host gives every side a V and a rope base: the K row itself and the
+// bytes after its nope when they are not stored apart)
+__device__ __forceinline__ const char* k_addr(const FwdArgs& a, uint32_t e) {
+  if (e == kNoRow) return (const char*)g_zero_row;
+  const bool c = e & kCmpBit;
+  return row_at(c ? a.cmp_kv : a.ori_kv, e & ~kCmpBit, c ? a.cmp_stride : a.ori_stride);
+}
+__device__ __forceinline__ const char* v_addr(const FwdArgs& a, uint32_t e) {
+  if (e == kNoRow) return (const char*)g_zero_row;
+  const bool c = e & kCmpBit;
+  return row_at(c ? a.cmp_kv : a.ori_v, e & ~kCmpBit, c ? a.cmp_stride : a.ori_v_stride);
+}
+__device__ __forceinline__ const char* rope_addr(const FwdArgs& a, uint32_t e) {
+  if (e == kNoRow) return (const char*)g_zero_row;
+  const bool c = e & kCmpBit;
+  return row_at(c ? a.cmp_rope : a.ori_rope, e & ~kCmpBit,
+                c ? a.cmp_rope_stride : a.ori_rope_stride);
+}
+
 // K side of one tile: 512 nope values per row (1 KB per wave instruction) and,
 // with rope, 8 rows of 64 rope values per instruction (row r's 16-byte chunk c
 // lands at position c ^ ((r >> 1) & 7) of its 128-byte LDS row, which keeps
-// the 16-row reads conflict-free).  All row addresses of the wave's share are
-// read from LDS before the first load is issued (the loads' "memory" clobber
-// would otherwise serialise one LDS round trip per load): nope rows with one
-// read (lane j holds row j, handed out with v_readlane), rope rows per lane.
+// the 16-row reads conflict-free).  The wave's row entries are read from LDS
+// once (lane j holds row j) before the first load is issued (the loads'
+// "memory" clobber would otherwise serialise one LDS round trip per load);
+// each row's addresses are then computed in SGPRs from its entry, handed out
+// with v_readlane, and a rope lane picks its row's address from them.
 template <int NW, int DQK, int VMODE>
-__device__ __forceinline__ void issue_k(const uint64_t* sAK, const uint64_t* sAR, int tbase,
+__device__ __forceinline__ void issue_k(const FwdArgs& a, const uint32_t* sRow, int tbase,
                                         uint32_t ldsK, int w, int l) {
   using C = Pipe<NW, DQK, VMODE>;
   const uint32_t wk = __builtin_amdgcn_readfirstlane(ldsK + w * C::NR * C::RSTR);
-  const uint64_t mine = sAK[tbase + w * C::NR + (l < C::NR ? l : 0)];
+  const uint32_t mine = sRow[tbase + w * C::NR + (l < C::NR ? l : 0)];
   const char* rsrc[C::ROPE ? C::ROPE_INSTR : 1];
+#pragma unroll
+  for (int j = 0; j < C::NR; ++j) {
+    const uint32_t e = __builtin_amdgcn_readlane(mine, j);
+    dma16_s((uint64_t)k_addr(a, e), l * 16, wk + j * C::RSTR);
+    if constexpr (C::ROPE) {
+      // rope instruction j / 8, lanes 8 (j % 8) .. 8 (j % 8) + 7 (row 0's
+      // address also fills the lanes of rows past NR, which issue nothing)
+      const char* ra = rope_addr(a, e);
+      if (j % 8 == 0 || (l >> 3) == j % 8) rsrc[j / 8] = ra;
+    }
+  }
   if constexpr (C::ROPE) {
+    const uint32_t wr = __builtin_amdgcn_readfirstlane(ldsK + kTile * C::RSTR + w * C::NR * 128);
 #pragma unroll
     for (int q = 0; q < C::ROPE_INSTR; ++q) {
       const int rr = w * C::NR + 8 * q + ((l >> 3) < C::NR ? (l >> 3) : 0);
       const int chunk = (l & 7) ^ ((rr >> 1) & 7);
-      rsrc[q] = (const char*)sAR[tbase + rr] + chunk * 16;
+      if (C::NR >= 8 || (l >> 3) < C::NR) dma16(rsrc[q] + chunk * 16, wr + q * 1024);
     }
-  }
-#pragma unroll
-  for (int j = 0; j < C::NR; ++j) dma16_s(readlane64(mine, j), l * 16, wk + j * C::RSTR);
-  if constexpr (C::ROPE) {
-    const uint32_t wr = __builtin_amdgcn_readfirstlane(ldsK + kTile * C::RSTR + w * C::NR * 128);
-#pragma unroll
-    for (int q = 0; q < C::ROPE_INSTR; ++q)
-      if (C::NR >= 8 || (l >> 3) < C::NR) dma16(rsrc[q], wr + q * 1024);
   }
 }
 
 template <int NW, int DQK, int VMODE>
-__device__ __forceinline__ void issue_v(const uint64_t* sAV, int tbase, uint32_t ldsV, int w,
-                                        int l) {
+__device__ __forceinline__ void issue_v(const FwdArgs& a, const uint32_t* sRow, int tbase,
+                                        uint32_t ldsV, int w, int l) {
   using C = Pipe<NW, DQK, VMODE>;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(ldsV + w * C::NR * C::RSTR);
-  const uint64_t mine = sAV[tbase + w * C::NR + (l < C::NR ? l : 0)];
+  const uint32_t mine = sRow[tbase + w * C::NR + (l < C::NR ? l : 0)];
 #pragma unroll
-  for (int j = 0; j < C::NR; ++j) dma16_s(readlane64(mine, j), l * 16, wv + j * C::RSTR);
+  for (int j = 0; j < C::NR; ++j) {
+    const uint32_t e = __builtin_amdgcn_readlane(mine, j);
+    dma16_s((uint64_t)v_addr(a, e), l * 16, wv + j * C::RSTR);
+  }
 }
 
 // Packed rows (512 INT8 / FP8-E4M3 codes, the bf16 rope, four fp32 scales of
@@ -481,8 +522,8 @@ struct PackedPipe {
 };
 
 template <int NW, int DQK>
-__device__ __forceinline__ void issue_raw(const uint64_t* sAK, int tbase, uint32_t ldsRaw, int w,
-                                          int l) {
+__device__ __forceinline__ void issue_raw(const FwdArgs& a, const uint32_t* sRow, int tbase,
+                                          uint32_t ldsRaw, int w, int l) {
   using P = PackedPipe<NW, DQK>;
   const uint32_t base = __builtin_amdgcn_readfirstlane(ldsRaw + w * P::PER * 1024);
   constexpr int B = 8;                                        // addresses read per batch
@@ -493,7 +534,7 @@ __device__ __forceinline__ void issue_raw(const uint64_t* sAK, int tbase, uint32
     for (int q = q0; q < q0 + B && q < P::PER; ++q) {
       const int c = (w * P::PER + q) * 64 + l;                // chunk index in the tile
       const int r = c < kTile * P::CPR ? c / P::CPR : 0;
-      const char* rowp = (const char*)sAK[tbase + r];
+      const char* rowp = k_addr(a, sRow[tbase + r]);
       src[q - q0] = c < kTile * P::CPR ? rowp + 16 * (c - r * P::CPR) : (const char*)g_zero_row;
     }
 #pragma unroll
@@ -563,7 +604,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   static_assert(!PK || VMODE == 0, "packed KV has no separate V");
   static_assert(FMT == SFMLA_KV_BF16 || FMT == SFMLA_KV_INT8_PACKED ||
                 FMT == SFMLA_KV_FP8_E4M3_PACKED || FMT == SFMLA_KV_FP16, "KV format");
-  constexpr bool BROPE = C::ROPE && !PK;          // rope gathered from its own address
   constexpr int T = C::T;
   constexpr int NKS = DQK / 32;
   constexpr int NTHR = NW * 64;
@@ -580,22 +620,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   __shared__ __align__(16) char sW1[PK ? PP::RAWB : 16];
   __shared__ __align__(16) char sW2[PK ? PP::RAWB : 16];
   __shared__ __align__(16) float sScale[PK ? 4 * T : 4];
-  __shared__ uint64_t sAK[kSplitRows + T];
-  __shared__ uint64_t sAR[BROPE ? kSplitRows + T : 1];
-  __shared__ uint64_t sAV[VMODE ? kSplitRows + T : 1];
-  __shared__ uint8_t sValid[kSplitRows + T];
+  __shared__ uint32_t sRow[kMaxSplitRows + T];      // resolved positions of the split
 
   // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so XCD x = bid
   // mod 8 takes the query rows 8k + x, and within it slot bid / 8 runs over
-  // (k, split, head group): every split and head group of a row is on one
-  // XCD, dispatched together; the groups' repeated gathers and the merger's
-  // reads of the other splits' partials stay within that XCD's L2.
+  // (split, k, head group), split slowest: every split and head group of a
+  // row is on one XCD, so the groups' repeated gathers and the merger's reads
+  // of the other splits' partials stay within that XCD's L2.  Split-major
+  // order puts the workgroups of splits a row does not have (its list is
+  // shorter than the longest) after all the real ones; interleaved between
+  // them they were measured to slow a one-split launch by a third.
   const int G = a.groups;
+  const int K8 = (a.q_t + 7) >> 3;
   const int bid = blockIdx.x;
   const int slot = bid >> 3;
   const int hg = slot % G;
-  const int split = (slot / G) % a.max_splits;
-  const int row = (slot / G / a.max_splits) * 8 + (bid & 7);
+  const int split = slot / G / K8;
+  const int row = ((slot / G) % K8) * 8 + (bid & 7);
   if (row >= a.q_t) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g = l >> 4, t = l & 15;
@@ -623,7 +664,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   if (split >= nsplit) return;
   const int n = rec[R_NTOTAL];
   const int chunk = rec[R_CHUNK];
-  if (chunk > kSplitRows) {
+  if (chunk > kMaxSplitRows) {
     // a list longer than the parameters' maxima allow: refuse the row
     if (split == 0) {
 #pragma unroll
@@ -646,69 +687,63 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // index loads of the resolve below: loads complete in order, so the checks
   // on the indices do not wait for Q, while Q travels during the table step.
   bf16x8 qreg[HB][NKS];
-  // ---- resolve every list position of this split once, into row addresses
-  //      (empty or masked slots read a zero row).  Each thread takes up to
-  //      PPT positions; the index loads of all of them, then the table loads
-  //      of all of them, are in flight together.
+  // ---- resolve every list position of this split once, into physical row
+  //      entries in LDS (empty or masked slots: kNoRow).  Positions go in
+  //      batches of PPT per thread: the index loads of a batch, then its
+  //      table loads, are all in flight together; the first batch covers a
+  //      512-row split, the Q loads travel behind its index loads.
   {
-    constexpr int PPT = (kSplitRows + T + NTHR - 1) / NTHR;
-    const char* zero = (const char*)g_zero_row;
+    constexpr int PPT = (512 + T + NTHR - 1) / NTHR;
     const RowInfo ri = row_info(rec);
     const int ntT = nt * T;
-    int vv[PPT], jj[PPT], sd[PPT], ee[PPT];
-    bool he[PPT];
-    // loads are unconditional (a position without an entry reads its own
-    // plan record) so that no branch join waits for one before the next issues
+    auto batch = [&](int i0, auto&& between) {
+      int vv[PPT], jj[PPT], sd[PPT], ee[PPT];
+      bool he[PPT];
+      // loads are unconditional (a position without an entry reads its own
+      // plan record) so that no branch join waits for one before the next issues
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int k = k0 + tid + u * NTHR;
-      const int32_t* ep = (tid + u * NTHR < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
-      vv[u] = *(ep ? ep : rec);
-    }
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      // unconditional loads (a branch join would wait for them): lanes of
-      // heads past q_n read head 0; their scores stay in their own lanes and
-      // their outputs are never written
-      const int h = h0 + 16 * hb + t;
-      const uint16_t* qp = a.q + ((int64_t)row * a.qn + (h < a.qn ? h : 0)) * DQK + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
-    }
-
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int k = k0 + tid + u * NTHR;
-      sd[u] = 0;
-      jj[u] = (tid + u * NTHR < ntT && k < k1) ? slot_row(a, ri, k, vv[u], &sd[u]) : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int32_t* tp = table_entry(a, ri, jj[u], sd[u]);
-      he[u] = tp != nullptr;
-      ee[u] = *(tp ? tp : rec);
-    }
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int i = tid + u * NTHR;
-      if (i >= ntT) break;
-      const int side = sd[u];
-      const int64_t phys = phys_row(a, ri, jj[u], side, he[u], ee[u]);
-      const char* ka = zero;
-      const char* va = zero;
-      const char* ra = zero;
-      if (phys >= 0) {
-        ka = side ? a.cmp_kv + phys * a.cmp_stride : a.ori_kv + phys * a.ori_stride;
-        va = (side || !a.ori_v) ? ka : a.ori_v + phys * a.ori_v_stride;
-        const char* rp = side ? a.cmp_rope : a.ori_rope;
-        ra = rp ? rp + phys * (side ? a.cmp_rope_stride : a.ori_rope_stride) : ka + 1024;
+      for (int u = 0; u < PPT; ++u) {
+        const int i = i0 + tid + u * NTHR;
+        const int k = k0 + i;
+        const int32_t* ep = (i < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
+        vv[u] = *(ep ? ep : rec);
       }
-      sAK[i] = (uint64_t)ka;
-      if constexpr (BROPE) sAR[i] = (uint64_t)ra;
-      if constexpr (VMODE) sAV[i] = (uint64_t)va;
-      sValid[i] = phys >= 0;
-    }
+      between();
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int i = i0 + tid + u * NTHR;
+        const int k = k0 + i;
+        sd[u] = 0;
+        jj[u] = (i < ntT && k < k1) ? slot_row(a, ri, k, vv[u], &sd[u]) : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int32_t* tp = table_entry(a, ri, jj[u], sd[u]);
+        he[u] = tp != nullptr;
+        ee[u] = *(tp ? tp : rec);
+      }
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int i = i0 + tid + u * NTHR;
+        if (i >= ntT) break;
+        const int64_t phys = phys_row(a, ri, jj[u], sd[u], he[u], ee[u]);
+        sRow[i] = phys >= 0 ? (uint32_t)phys | (sd[u] ? kCmpBit : 0u) : kNoRow;
+      }
+    };
+    batch(0, [&] {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        // unconditional loads (a branch join would wait for them): lanes of
+        // heads past q_n read head 0; their scores stay in their own lanes
+        // and their outputs are never written
+        const int h = h0 + 16 * hb + t;
+        const uint16_t* qp = a.q + ((int64_t)row * a.qn + (h < a.qn ? h : 0)) * DQK + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
+      }
+    });
+    for (int i0 = PPT * NTHR; i0 < ntT; i0 += PPT * NTHR) batch(i0, [] {});
   }
   wait_lgkm0();
   block_barrier();
@@ -732,8 +767,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     bool valid[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      valid[i] = sValid[tbase + 4 * g + i];
-      valid[4 + i] = sValid[tbase + 16 + 4 * g + i];
+      valid[i] = sRow[tbase + 4 * g + i] != kNoRow;
+      valid[4 + i] = sRow[tbase + 16 + 4 * g + i] != kNoRow;
     }
     // packed: the scales of this lane's rows (4g+i and 16+4g+i), per tile
     f32x4 sc[PK ? 4 : 1][2];
@@ -861,7 +896,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       if (tt + 1 < nt) wait_vmcnt<PP::PER>(); else wait_vmcnt<0>();   // raw(tt) landed
       wait_lgkm0();
       block_barrier();                          // ... and tile tt-1 is consumed
-      if (tt + 2 < nt) issue_raw<NW, DQK>(sAK, (tt + 2) * T, lds_addr(sWn2), w, l);
+      if (tt + 2 < nt) issue_raw<NW, DQK>(a, sRow, (tt + 2) * T, lds_addr(sWn2), w, l);
       decode_tile<NW, DQK, FMT>(sWc, sK0, sScale, tid);
       wait_lgkm0();
       block_barrier();                          // decoded tile complete
@@ -870,10 +905,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         pv(sK0);
       }
     };
-    if (nt > 0) issue_raw<NW, DQK>(sAK, 0, lds_addr(sW0), w, l);
+    if (nt > 0) issue_raw<NW, DQK>(a, sRow, 0, lds_addr(sW0), w, l);
     wait_vmcnt<0>();                            // raw(0) and the Q slices
     settle(qreg);
-    if (nt > 1) issue_raw<NW, DQK>(sAK, T, lds_addr(sW1), w, l);
+    if (nt > 1) issue_raw<NW, DQK>(a, sRow, T, lds_addr(sW1), w, l);
     for (int tt = 0; tt < nt; tt += 3) {
       step(tt, sW0, sW2);
       if (tt + 1 < nt) step(tt + 1, sW1, sW0);
@@ -885,23 +920,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       if (tt + 1 < nt) wait_vmcnt<C::NV + C::NK>(); else wait_vmcnt<C::NV>();   // K(tt) landed
       wait_lgkm0();
       block_barrier();                                    // ... and V(tt-1) reads are done
-      if (tt + 1 < nt) issue_v<NW, DQK, VMODE>(sAV, (tt + 1) * T, lds_addr(sVn), w, l);
+      if (tt + 1 < nt) issue_v<NW, DQK, VMODE>(a, sRow, (tt + 1) * T, lds_addr(sVn), w, l);
       if (wave_on) qk_softmax(sKc, tt * T);
       if (tt + 1 < nt) wait_vmcnt<C::NK + C::NV>(); else wait_vmcnt<0>();        // V(tt) landed
       wait_lgkm0();
       block_barrier();                                    // ... and K(tt) reads are done
-      if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(sAK, sAR, (tt + 2) * T, lds_addr(sKc), w, l);
+      if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(a, sRow, (tt + 2) * T, lds_addr(sKc), w, l);
       if (wave_on) pv(sVc);
     };
     // K(0) and the Q slices land first; the explicit full wait also tells
     // the compiler the Q loads are done, so no wait for them remains inside
     // the loop (where it would wait for every gather in flight).
-    if (nt > 0) issue_k<NW, DQK, VMODE>(sAK, sAR, 0, lds_addr(sK0), w, l);
+    if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
     wait_vmcnt<0>();
     settle(qreg);
     if (nt > 0) {
-      issue_v<NW, DQK, VMODE>(sAV, 0, lds_addr(sV0), w, l);
-      if (nt > 1) issue_k<NW, DQK, VMODE>(sAK, sAR, T, lds_addr(sK1), w, l);
+      issue_v<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sV0), w, l);
+      if (nt > 1) issue_k<NW, DQK, VMODE>(a, sRow, T, lds_addr(sK1), w, l);
     }
     for (int tt = 0; tt < nt; tt += 2) {
       step(tt, sK0, sV0, sV1);
@@ -913,16 +948,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       if (tt + 1 < nt) wait_vmcnt<C::NK>(); else wait_vmcnt<0>();   // K(tt) landed
       wait_lgkm0();
       block_barrier();                                    // ... and tile tt-1 is consumed
-      if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(sAK, sAR, (tt + 2) * T, lds_addr(sKn2), w, l);
+      if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(a, sRow, (tt + 2) * T, lds_addr(sKn2), w, l);
       if (wave_on) {
         qk_softmax(sKc, tt * T);
         pv(sKc);
       }
     };
-    if (nt > 0) issue_k<NW, DQK, VMODE>(sAK, sAR, 0, lds_addr(sK0), w, l);
+    if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
     wait_vmcnt<0>();                                      // K(0) and the Q slices
     settle(qreg);
-    if (nt > 1) issue_k<NW, DQK, VMODE>(sAK, sAR, T, lds_addr(sK1), w, l);
+    if (nt > 1) issue_k<NW, DQK, VMODE>(a, sRow, T, lds_addr(sK1), w, l);
     for (int tt = 0; tt < nt; tt += 3) {
       step(tt, sK0, sK2);
       if (tt + 1 < nt) step(tt + 1, sK1, sK0);

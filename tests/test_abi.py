@@ -89,6 +89,7 @@ BAD = [
     ("ori_sparse_block_size", 3, "ori_sparse_block_size"),
     ("ori_sparse_block_size", 256, "ori_sparse_block_size"),
     ("ori_sparse_block_size", 4, "needs an ori TopK list"),
+    ("ori_kv_rows", 2 ** 31 - 1, "ori_kv_rows"),
 ]
 
 

@@ -166,6 +166,28 @@ def test_head_grouping_invariance_bitwise(fmt, monkeypatch):
     check_outputs(P, res, ref, [0, 1])
 
 
+@pytest.mark.parametrize("split_rows", ["32", "1024", "2048"])
+@pytest.mark.parametrize("fmt", ["bf16", "int8_packed"])
+def test_split_sizes_match_oracle(fmt, split_rows, monkeypatch):
+    """Lists cut into 32-row splits (many partials to merge) or held whole in
+    one workgroup's row table (up to 2048 rows) give the oracle's result."""
+    import sparse_shared_kv_amd as s
+    kw = dict(family="sfa", max_kv=4000, topk=2100, num_heads_q=64)
+    if fmt != "bf16":
+        kw.update(kv_dtype=fmt, rope_head_dim=64)
+    P = synth.random_tiny(507, **kw)
+    monkeypatch.setenv("SFMLA_SPLIT_ROWS", split_rows)
+    call = s.Call(P.params, P.arrays)
+    out = [None if t is None else t.clone() for t in call.run()]
+    torch.cuda.synchronize()
+    rows = [0, 1, P.params["q_t"] - 1] if "q_t" in P.params else [0, 1]
+    rows = sorted(set(r for r in rows if r >= 0))
+    ref = oracle.forward(P, rows=rows)
+    res = dict(O=out[0].float().cpu().numpy(), status=int(call.status.item()),
+               lse=None if out[1] is None else out[1].cpu().numpy())
+    check_outputs(P, res, ref, rows)
+
+
 def test_batch_invariance_bitwise():
     """A sequence alone and inside a batch gives bit-identical rows."""
     L = logical(21, q_lens=[2, 3, 1, 2], ori_lens=[900, 1400, 300, 2000], qn=32, ratio=4,
@@ -175,6 +197,24 @@ def test_batch_invariance_bitwise():
     out_full = run_gpu(full)["O"]
     per_b = unplace_o(full, out_full, L)
     for b in (1, 3):
+        Lb = {k: ([v[b]] if isinstance(v, list) and len(v) == 4 else v) for k, v in L.items()}
+        one = place(Lb, "TND", "PA_BSND", bs=16, seed=2)
+        got = run_gpu(one)["O"]
+        assert np.array_equal(got, per_b[b]), b
+
+
+def test_batch_invariance_with_long_query_sequences_bitwise():
+    """Rows of sequences with many queries keep their list in one split while
+    short sequences split theirs; either way a sequence alone and inside a
+    batch gives bit-identical rows."""
+    L = logical(25, q_lens=[70, 2, 64, 1], ori_lens=[3000, 2600, 1900, 2200], qn=16, ratio=4,
+                cmp_topk=600, win=(127, 0))
+    full = place(L, "TND", "PA_BSND", bs=16, seed=1)
+    res = run_gpu(full)
+    rows = [0, 69, 70, 135, 136]
+    check_outputs(full, res, oracle.forward(full, rows=rows), rows)
+    per_b = unplace_o(full, res["O"], L)
+    for b in (0, 1, 2):
         Lb = {k: ([v[b]] if isinstance(v, list) and len(v) == 4 else v) for k, v in L.items()}
         one = place(Lb, "TND", "PA_BSND", bs=16, seed=2)
         got = run_gpu(one)["O"]
