@@ -132,9 +132,9 @@ def profile_commands(outdir: str, workload: str) -> list:
         "rocprofv3 --kernel-trace --stats --output-format csv -d %s/trace -o trace -- %s"
         % (outdir, b),
         "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s/fetch -o fetch -- %s --steps 5 "
-        "--warmup 2 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
+        "--warmup 2 --settle-ms 0 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s/write -o write -- %s --steps 5 "
-        "--warmup 2 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
+        "--warmup 2 --settle-ms 0 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
     ]
 
 
@@ -211,8 +211,11 @@ def write_profiles(outdir: str, workload: str) -> None:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps run for at least this long before the warm-up "
+                         "steps (the GPU clocks settle under sustained load)")
     ap.add_argument("--workload", default="sfa_mla_rope", choices=sorted(DESCR))
     ap.add_argument("--replicas", type=int, default=4,
                     help="index-set replicas rotated between steps (TopK workloads)")
@@ -280,6 +283,18 @@ def main():
         if idx_sets:
             setattr(call.tensors, reps[0][0], idx_ptrs[k % nrep])
 
+    # clock settle: the first ~150 back-to-back steps on an idle GPU run
+    # ~10 % slower than the steady state, whatever the warm-up count
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for k in range(25):
+            select(k)
+            call.plan(stream)
+            call.forward(stream)
+            call.combine(stream)
+        settle_steps += 25
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for k in range(args.warmup):
         select(k)
         call.plan(stream)
@@ -353,6 +368,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -89,6 +89,7 @@ sfmla_status validate(const sfmla_params* pp) {
     REQUIRE(p.q_t > 0, "TND q needs q_t > 0");
   }
   REQUIRE(p.max_seqlen_q > 0, "max_seqlen_q must be > 0");
+  REQUIRE((int64_t)p.q_t * p.num_heads_q < ((int64_t)1 << 31), "q_t * num_heads_q must be < 2^31");
   REQUIRE(p.has_ori_kv == 1, "ori_kv is required");
   REQUIRE(p.max_seqlen_ori_kv > 0, "max_seqlen_ori_kv must be > 0");
   REQUIRE(p.ori_kv_rows > 0, "ori_kv_rows must be > 0");

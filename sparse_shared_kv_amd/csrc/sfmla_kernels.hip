@@ -736,8 +736,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         // unconditional loads (a branch join would wait for them): lanes of
         // heads past q_n read head 0; their scores stay in their own lanes
         // and their outputs are never written
+        // (row * q_n + head < 2^31, checked on the host; a 32-bit index
+        // here also keeps it from being held until the epilogue)
         const int h = h0 + 16 * hb + t;
-        const uint16_t* qp = a.q + ((int64_t)row * a.qn + (h < a.qn ? h : 0)) * DQK + 8 * g;
+        const int qi = row * a.qn + (h < a.qn ? h : 0);
+        const uint16_t* qp = a.q + (uint32_t)qi * (uint64_t)DQK + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
           qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
@@ -1248,6 +1251,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s) {
   b.groups = groups;
   if (b.bpg < 1 || b.bpg > NW) return hipErrorInvalidConfiguration;
   const int64_t blocks = (int64_t)(a.q_t + 7) / 8 * 8 * a.max_splits * groups;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      s, b);
   return hipGetLastError();
