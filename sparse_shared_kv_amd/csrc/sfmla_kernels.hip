@@ -644,6 +644,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const int h0 = (hg * a.bpg + w) * HPW;           // first head of this wave
   const bool wave_on = w < a.bpg && h0 < a.qn;
 
+  // The row's plan record is read together with the plan header (the buffer
+  // always holds both; its size is checked on the host), so the two reads
+  // cost one round trip; the record is only used once the header matches.
+  const int32_t* rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
+  const int nsplit = rec[R_NSPLIT];
+  const int n = rec[R_NTOTAL];
+  const int chunk = rec[R_CHUNK];
+  const RowInfo ri = row_info(rec);
   if (!plan_matches(a)) {
     if (split == 0) {
       const float nan = __builtin_nanf("");
@@ -659,11 +667,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     }
     return;
   }
-  const int32_t* rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
-  const int nsplit = rec[R_NSPLIT];
   if (split >= nsplit) return;
-  const int n = rec[R_NTOTAL];
-  const int chunk = rec[R_CHUNK];
   if (chunk > kMaxSplitRows) {
     // a list longer than the parameters' maxima allow: refuse the row
     if (split == 0) {
@@ -684,17 +688,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const int nt = (k1 - k0 + T - 1) / T;
 
   // Q slices (B operand: k = d, n = head).  They are loaded right after the
-  // index loads of the resolve below: loads complete in order, so the checks
-  // on the indices do not wait for Q, while Q travels during the table step.
+  // table loads of the resolve below: loads complete in order, so waiting
+  // for the table entries does not wait for Q, which travels while the
+  // entries go to LDS and the first tile's rows are requested.
   bf16x8 qreg[HB][NKS];
   // ---- resolve every list position of this split once, into physical row
   //      entries in LDS (empty or masked slots: kNoRow).  Positions go in
   //      batches of PPT per thread: the index loads of a batch, then its
   //      table loads, are all in flight together; the first batch covers a
-  //      512-row split, the Q loads travel behind its index loads.
+  //      512-row split, the Q loads follow its table loads.
   {
     constexpr int PPT = (512 + T + NTHR - 1) / NTHR;
-    const RowInfo ri = row_info(rec);
     const int ntT = nt * T;
     auto batch = [&](int i0, auto&& between) {
       int vv[PPT], jj[PPT], sd[PPT], ee[PPT];
@@ -708,7 +712,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         const int32_t* ep = (i < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
         vv[u] = *(ep ? ep : rec);
       }
-      between();
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
         const int i = i0 + tid + u * NTHR;
@@ -722,6 +725,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         he[u] = tp != nullptr;
         ee[u] = *(tp ? tp : rec);
       }
+      __builtin_amdgcn_sched_barrier(0);            // every table load before the Q loads
+      between();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
         const int i = i0 + tid + u * NTHR;
