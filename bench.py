@@ -302,18 +302,23 @@ def main():
         call.combine(stream)
     torch.cuda.synchronize()
 
-    # timed region: K whole steps; HIP events on the launch stream bracket
-    # every forward launch
+    # timed region: K whole steps.  Every forward kernel's duration comes
+    # from a pair of HIP events on the launch stream that the kernel's own
+    # dispatch stamps at its start and end (sfmla_time_next_forward): event
+    # records queued around the launch would add a dispatch gap of ~5 us to
+    # each step and to the measured duration.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    for a, b in ev:                     # create the events (a first record)
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         select(k)
         call.plan(stream)
-        ev[k][0].record(stream)
+        s.sfmla_time_next_forward(ev[k][0], ev[k][1])
         call.forward(stream)
-        ev[k][1].record(stream)
         call.combine(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

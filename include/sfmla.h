@@ -272,6 +272,17 @@ sfmla_status sfmla_debug_resolve(const sfmla_params* params, const sfmla_tensors
                                  const int32_t* metadata, size_t n_ints, int64_t* rows_out,
                                  int32_t max_rows, int32_t* counts_out, void* stream);
 
+/*
+ * Measurement hook: the next sfmla_forward() call on this thread launches its
+ * kernel with these HIP events (hipEvent_t, either may be NULL) stamped by
+ * the dispatch itself at the kernel's start and end, so that
+ * hipEventElapsedTime() of the pair is that kernel's duration with no event
+ * packets queued around it.  The events must exist (created or recorded once
+ * before); the library keeps no reference after that call, which uses them
+ * whether or not it succeeds.  Always SFMLA_OK.
+ */
+sfmla_status sfmla_time_next_forward(void* start_event, void* stop_event);
+
 /* Thread-local description of the last failed call ("" after success). */
 const char* sfmla_last_error(void);
 const char* sfmla_version(void);

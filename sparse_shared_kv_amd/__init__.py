@@ -21,7 +21,8 @@ from . import _abi
 from ._abi import KV_DTYPES, LAYOUTS, Lengths, Params, SfmlaError, Tensors
 
 __all__ = ["sfmla_metadata_size", "sfmla_metadata", "sfmla_workspace_size", "sfmla_forward",
-           "sfmla_combine", "sfmla_merge_partials", "sfmla_debug_resolve", "sfmla_version", "Params", "Lengths",
+           "sfmla_combine", "sfmla_merge_partials", "sfmla_debug_resolve", "sfmla_time_next_forward",
+           "sfmla_version", "Params", "Lengths",
            "Tensors", "SfmlaError", "Call", "make_params", "CMP_BIT"]
 
 CMP_BIT = 1 << 62
@@ -93,6 +94,17 @@ def sfmla_debug_resolve(params: Params, tensors: Tensors, metadata: torch.Tensor
     _abi.check(_lib().sfmla_debug_resolve(ctypes.byref(params), ctypes.byref(tensors),
                                           _ptr(metadata), metadata.numel(), _ptr(rows_out),
                                           rows_out.shape[1], _ptr(counts_out), _stream(stream)))
+
+
+def sfmla_time_next_forward(start: torch.cuda.Event, stop: torch.cuda.Event):
+    """The next sfmla_forward on this thread has its kernel's start and end
+    stamped into these events by the dispatch (no event packets around it).
+    The events must already exist: record each once beforehand."""
+    for e in (start, stop):
+        if not e.cuda_event:
+            raise ValueError("record the event once before passing it")
+    _abi.check(_lib().sfmla_time_next_forward(ctypes.c_void_p(start.cuda_event),
+                                              ctypes.c_void_p(stop.cuda_event)))
 
 
 # ---------------------------------------------------------------------------

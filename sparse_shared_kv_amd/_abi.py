@@ -67,7 +67,7 @@ class Tensors(ctypes.Structure):
 
 SYMBOLS = ("sfmla_metadata_size", "sfmla_metadata", "sfmla_workspace_size",
            "sfmla_forward", "sfmla_combine", "sfmla_merge_partials", "sfmla_debug_resolve",
-           "sfmla_last_error", "sfmla_version")
+           "sfmla_time_next_forward", "sfmla_last_error", "sfmla_version")
 
 _lib = None
 
@@ -90,7 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfmla_combine.argtypes = [P(Params), P(Tensors), _vp, sz, _vp, sz, _vp]
     lib.sfmla_merge_partials.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.sfmla_debug_resolve.argtypes = [P(Params), P(Tensors), _vp, sz, _vp, _i32, _vp, _vp]
-    for name in SYMBOLS[:7]:
+    lib.sfmla_time_next_forward.argtypes = [_vp, _vp]
+    for name in SYMBOLS[:8]:
         getattr(lib, name).restype = ctypes.c_int
     lib.sfmla_last_error.restype = ctypes.c_char_p
     lib.sfmla_last_error.argtypes = []

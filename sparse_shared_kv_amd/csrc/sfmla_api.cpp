@@ -20,6 +20,9 @@
 namespace {
 
 thread_local std::string g_err;
+// events for the next sfmla_forward launch on this thread (sfmla_time_next_forward)
+thread_local void* g_time_start = nullptr;
+thread_local void* g_time_stop = nullptr;
 
 sfmla_status fail(sfmla_status s, const char* fmt, ...) {
   char buf[512];
@@ -355,6 +358,12 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
 
 extern "C" {
 
+sfmla_status sfmla_time_next_forward(void* start_event, void* stop_event) {
+  g_time_start = start_event;
+  g_time_stop = stop_event;
+  return ok();
+}
+
 const char* sfmla_last_error(void) { return g_err.c_str(); }
 
 const char* sfmla_version(void) { return SFMLA_VERSION; }
@@ -415,6 +424,9 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
 sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
                            int32_t* metadata, size_t n_ints, float softmax_scale,
                            void* workspace, size_t ws_bytes, void* stream) {
+  // events asked for by sfmla_time_next_forward serve this call only
+  const hipEvent_t t0 = (hipEvent_t)g_time_start, t1 = (hipEvent_t)g_time_stop;
+  g_time_start = g_time_stop = nullptr;
   sfmla_status s = validate(params);
   if (s != SFMLA_OK) return s;
   const sfmla_params& p = *params;
@@ -438,7 +450,7 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
   const int dqk = 512 + p.rope_head_dim;
   const int vmode = p.has_separate_v ? 1 : 0;
   hipError_t e =
-      sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream);
+      sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream, t0, t1);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }

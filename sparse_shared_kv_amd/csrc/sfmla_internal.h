@@ -97,8 +97,9 @@ struct CombineArgs {
 
 // Kernel launchers (defined in sfmla_kernels.hip).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+// t0 / t1 (may be null): events the dispatch stamps at the kernel's start / end
 hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
-                          hipStream_t s);
+                          hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_debug_resolve(const FwdArgs& a, hipStream_t s);
 

@@ -22,6 +22,7 @@
 // (within a 16-lane group, lane t gets column t of a 4 x 16 block whose row r
 // is addressed by lanes 4r..4r+3).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1252,42 +1253,47 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 }
 
 template <int NW, int DQK, int VMODE, int FMT>
-static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s) {
+static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s, hipEvent_t t0,
+                               hipEvent_t t1) {
   FwdArgs b = a;
   b.groups = groups;
   if (b.bpg < 1 || b.bpg > NW) return hipErrorInvalidConfiguration;
   const int64_t blocks = (int64_t)(a.q_t + 7) / 8 * 8 * a.max_splits * groups;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     s, b);
+  if (t0 || t1)   // events that the dispatch itself stamps at the kernel's start and end
+    hipExtLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks),
+                          dim3(NW * 64), 0, s, t0, t1, 0, b);
+  else
+    hipLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks),
+                       dim3(NW * 64), 0, s, b);
   return hipGetLastError();
 }
 
 // Eight waves per workgroup for bf16 rows; four for packed rows, whose
 // decode needs more registers per wave.
 hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
-                          hipStream_t s) {
+                          hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   switch (fmt) {
     case SFMLA_KV_INT8_PACKED:
       if (nw != 4) return hipErrorInvalidConfiguration;
-      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_INT8_PACKED>(a, groups, s)
-                        : launch_fwd_t<4, 576, 0, SFMLA_KV_INT8_PACKED>(a, groups, s);
+      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1)
+                        : launch_fwd_t<4, 576, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1);
     case SFMLA_KV_FP8_E4M3_PACKED:
       if (nw != 4) return hipErrorInvalidConfiguration;
-      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s)
-                        : launch_fwd_t<4, 576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s);
+      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1)
+                        : launch_fwd_t<4, 576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1);
     case SFMLA_KV_FP16:
       if (nw != 8) return hipErrorInvalidConfiguration;
-      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, SFMLA_KV_FP16>(a, groups, s)
-                                   : launch_fwd_t<8, 512, 0, SFMLA_KV_FP16>(a, groups, s);
-      return vmode ? launch_fwd_t<8, 576, 1, SFMLA_KV_FP16>(a, groups, s)
-                   : launch_fwd_t<8, 576, 0, SFMLA_KV_FP16>(a, groups, s);
+      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
+                                   : launch_fwd_t<8, 512, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
+      return vmode ? launch_fwd_t<8, 576, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
+                   : launch_fwd_t<8, 576, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
     default:
       if (nw != 8) return hipErrorInvalidConfiguration;
-      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, 0>(a, groups, s)
-                                   : launch_fwd_t<8, 512, 0, 0>(a, groups, s);
-      return vmode ? launch_fwd_t<8, 576, 1, 0>(a, groups, s)
-                   : launch_fwd_t<8, 576, 0, 0>(a, groups, s);
+      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, 0>(a, groups, s, t0, t1)
+                                   : launch_fwd_t<8, 512, 0, 0>(a, groups, s, t0, t1);
+      return vmode ? launch_fwd_t<8, 576, 1, 0>(a, groups, s, t0, t1)
+                   : launch_fwd_t<8, 576, 0, 0>(a, groups, s, t0, t1);
   }
 }
 

@@ -335,3 +335,30 @@ def test_graph_replay_matches_eager():
         oc.run()                                     # unrelated eager work between replays
         torch.cuda.synchronize()
         assert int(call.status.item()) == 0
+
+
+def test_timing_hook_stamps_the_forward_kernel():
+    """sfmla_time_next_forward: the next forward's kernel start and end land
+    in the two events (positive duration, result unchanged), and only that
+    call is timed."""
+    import sparse_shared_kv_amd as s
+    P = synth.random_tiny(611, family="sfa", max_kv=3000, topk=1500, num_heads_q=64)
+    call = s.Call(P.params, P.arrays)
+    ref = [t.clone() for t in call.run() if t is not None]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    call.plan()
+    s.sfmla_time_next_forward(e0, e1)
+    call.forward()
+    call.combine()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 100.0
+    call.forward()                                 # not timed: the events keep their stamps
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == ms
+    got = [t for t in (call.out, call.lse) if t is not None]
+    for x, y in zip(ref, got):
+        assert torch.equal(x, y)
