@@ -322,6 +322,7 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
   f.win_r = p.ori_win_right;
   f.has_cmp = p.has_cmp_kv;
   f.max_splits = max_splits(p);
+  f.split_rows = split_rows(p);
   f.has_sinks = p.has_sinks;
   f.fingerprint = fingerprint(p);
   f.scale_log2 = scale * 1.4426950408889634f;

@@ -55,6 +55,7 @@ struct FwdArgs {
   int32_t max_splits, has_sinks;
   int32_t groups;                   // head groups of the launch
   int32_t bpg;                      // 16-head blocks per head group (<= waves; spare waves only load)
+  int32_t split_rows;               // list positions per split of a short-query row
   uint32_t fingerprint;
   float scale_log2;                 // softmax_scale * log2(e)
   const int32_t* meta;

@@ -245,9 +245,10 @@ __global__ void plan_kernel(PlanArgs a) {
 // forward
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ bool plan_matches(const FwdArgs& a) {
-  return a.meta[0] == kMagic && (uint32_t)a.meta[1] == a.fingerprint && a.meta[2] == a.q_t &&
-         a.meta[3] == a.max_splits;
+// h: the plan header, read as one 16-byte value (no chain of dependent reads)
+__device__ __forceinline__ bool plan_matches(const FwdArgs& a, int4 h) {
+  return (h.x == kMagic) & ((uint32_t)h.y == a.fingerprint) & (h.z == a.q_t) &
+         (h.w == a.max_splits);
 }
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -648,12 +649,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // The row's plan record is read together with the plan header (the buffer
   // always holds both; its size is checked on the host), so the two reads
   // cost one round trip; the record is only used once the header matches.
+  const int4 hdr = *(const int4*)a.meta;
   const int32_t* rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
   const int nsplit = rec[R_NSPLIT];
   const int n = rec[R_NTOTAL];
   const int chunk = rec[R_CHUNK];
   const RowInfo ri = row_info(rec);
-  if (!plan_matches(a)) {
+  // Index loads of the first resolve batch, issued in the same round trip:
+  // where the original-KV list is a TopK list its length is fixed by the
+  // parameters, so a position's entry does not depend on the plan record
+  // unless the row is empty or split in other chunks (a long-query row);
+  // the resolve below reloads in those cases.  Every load is in bounds
+  // (positions past the lists read the plan header instead).
+  constexpr int PPT = (512 + T + NTHR - 1) / NTHR;   // positions per thread and batch
+  const int spec_cnt = a.ori_topk << a.ori_sbs_log2;
+  const int spec_cap = a.ori_topk > 0 ? spec_cnt + (a.cmp_topk > 0 ? a.cmp_topk : 0) : 0;
+  int vspec[PPT];
+#pragma unroll
+  for (int u = 0; u < PPT; ++u) {
+    const int i = tid + u * NTHR;
+    const int k = split * a.split_rows + i;
+    const int32_t* ep = (const int32_t*)a.meta;
+    if (i < a.split_rows && k < spec_cap)
+      ep = k < spec_cnt ? a.ori_idx + (int64_t)row * a.ori_topk + (k >> a.ori_sbs_log2)
+                        : a.cmp_idx + (int64_t)row * a.cmp_topk + (k - spec_cnt);
+    vspec[u] = *ep;
+  }
+  if (!plan_matches(a, hdr)) {
     if (split == 0) {
       const float nan = __builtin_nanf("");
 #pragma unroll
@@ -699,19 +721,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   //      table loads, are all in flight together; the first batch covers a
   //      512-row split, the Q loads follow its table loads.
   {
-    constexpr int PPT = (512 + T + NTHR - 1) / NTHR;
     const int ntT = nt * T;
-    auto batch = [&](int i0, auto&& between) {
+    const bool spec = a.ori_topk > 0 && chunk == a.split_rows && ri.ori_cnt == spec_cnt;
+    auto batch = [&](int i0, bool use_spec, auto&& between) {
       int vv[PPT], jj[PPT], sd[PPT], ee[PPT];
       bool he[PPT];
-      // loads are unconditional (a position without an entry reads its own
-      // plan record) so that no branch join waits for one before the next issues
+      if (use_spec) {
 #pragma unroll
-      for (int u = 0; u < PPT; ++u) {
-        const int i = i0 + tid + u * NTHR;
-        const int k = k0 + i;
-        const int32_t* ep = (i < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
-        vv[u] = *(ep ? ep : rec);
+        for (int u = 0; u < PPT; ++u) vv[u] = vspec[u];
+      } else {
+        // loads are unconditional (a position without an entry reads its own
+        // plan record), and waited for inside this branch, so that no branch
+        // join waits for them
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) {
+          const int i = i0 + tid + u * NTHR;
+          const int k = k0 + i;
+          const int32_t* ep = (i < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
+          vv[u] = *(ep ? ep : rec);
+        }
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) asm volatile("" ::"v"(vv[u]));
       }
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
@@ -737,7 +767,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         sRow[i] = phys >= 0 ? (uint32_t)phys | (sd[u] ? kCmpBit : 0u) : kNoRow;
       }
     };
-    batch(0, [&] {
+    batch(0, spec, [&] {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         // unconditional loads (a branch join would wait for them): lanes of
@@ -753,7 +783,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
       }
     });
-    for (int i0 = PPT * NTHR; i0 < ntT; i0 += PPT * NTHR) batch(i0, [] {});
+    for (int i0 = PPT * NTHR; i0 < ntT; i0 += PPT * NTHR) batch(i0, false, [] {});
   }
   wait_lgkm0();
   block_barrier();
@@ -1206,7 +1236,7 @@ __global__ __launch_bounds__(256) void resolve_kernel(FwdArgs a) {
   __shared__ int32_t sFlag[256];
   __shared__ int32_t sBase;
   const int row = blockIdx.x;
-  if (!plan_matches(a)) {
+  if (!plan_matches(a, *(const int4*)a.meta)) {
     if (threadIdx.x == 0) {
       a.dbg_counts[row] = -1;
       if (a.status) atomicOr(a.status, SFMLA_STATUS_METADATA_MISMATCH);
