@@ -623,6 +623,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   __shared__ __align__(16) char sW2[PK ? PP::RAWB : 16];
   __shared__ __align__(16) float sScale[PK ? 4 * T : 4];
   __shared__ uint32_t sRow[kMaxSplitRows + T];      // resolved positions of the split
+  // bf16 / fp16 with a separate V: a merging wave stages its output in the
+  // K / V stage buffers (two waves per buffer) once every wave of the
+  // workgroup is done with them (sOut counts the waves out)
+  constexpr bool STAGE = VMODE && !PK;
+  constexpr int kStgRow = 1040;                      // staged output row (one head), padded
+  static_assert(!STAGE || (NW == 8 && 2 * 16 * kStgRow <= T * RS && T * RS <= C::KBYTES),
+                "output staging: two waves' 16 heads per stage buffer");
+  __shared__ int32_t sOut;
 
   // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so XCD x = bid
   // mod 8 takes the query rows 8k + x, and within it slot bid / 8 runs over
@@ -785,6 +793,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     });
     for (int i0 = PPT * NTHR; i0 < ntT; i0 += PPT * NTHR) batch(i0, false, [] {});
   }
+  if (STAGE && tid == 0) sOut = 0;
   wait_lgkm0();
   block_barrier();
 
@@ -1005,6 +1014,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     }
   }
 
+  if constexpr (STAGE) {
+    // this wave's last reads of the stage buffers have returned
+    wait_lgkm0();
+    if (l == 0) atomicAdd(&sOut, 1);
+  }
   float lt[HB], lse2[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
@@ -1093,6 +1107,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
   const int R = NJ * ns4;                               // load rounds
   const int split_bytes = a.groups * NW * WAVE_BYTES;
+  // Staged output: rounds write their results to LDS and the wave stores all
+  // 16 heads at the end.  Vector-memory stores count in vmcnt with the loads
+  // and complete in order, so stores between rounds would make each next
+  // round's wait include them.  Every wave of the workgroup counts itself
+  // out right after its main loop, so this wait ends.
+  char* stg = nullptr;
+  if constexpr (STAGE) {
+    stg = (w < 2 ? sK0 : w < 4 ? sK1 : w < 6 ? sV0 : sV1) + (w & 1) * 16 * kStgRow;
+    while (*(volatile int32_t*)&sOut < NW) __builtin_amdgcn_s_sleep(1);
+  }
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int h = h0 + 16 * hb + t;
@@ -1163,7 +1187,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         }
       }
       if (s0 + MS < nsplit) continue;                    // more splits for these columns
-      if (on) {
+      if (STAGE || on) {
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
           const int jj = jr * JB + j;
@@ -1172,8 +1196,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           p0.y = (uint32_t)to16<HALF>(acc[j][2] * inv) | ((uint32_t)to16<HALF>(acc[j][3] * inv) << 16);
           p1.x = (uint32_t)to16<HALF>(acc[j][4] * inv) | ((uint32_t)to16<HALF>(acc[j][5] * inv) << 16);
           p1.y = (uint32_t)to16<HALF>(acc[j][6] * inv) | ((uint32_t)to16<HALF>(acc[j][7] * inv) << 16);
-          *(uint2*)(op + 16 * (2 * jj)) = p0;
-          *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
+          if constexpr (STAGE) {
+            char* sp = stg + (16 * hb + t) * kStgRow + 2 * (32 * jj + 4 * g);
+            *(uint2*)sp = p0;
+            *(uint2*)(sp + 32) = p1;
+          } else {
+            *(uint2*)(op + 16 * (2 * jj)) = p0;
+            *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
+          }
         }
       }
 #pragma unroll
@@ -1183,6 +1213,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     }
     if (on && a.lse && g == 0)
       a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;
+  }
+  if constexpr (STAGE) {
+    // the staged heads (1 KB each, contiguous in the output) go out 16 bytes
+    // a lane; heads past q_n are not written
+    wait_lgkm0();
+    uint4 rowv[16 * HB];
+#pragma unroll
+    for (int i = 0; i < 16 * HB; ++i) rowv[i] = *(const uint4*)(stg + i * kStgRow + 16 * l);
+#pragma unroll
+    for (int i = 0; i < 16 * HB; ++i)
+      if (h0 + i < a.qn) *(uint4*)(a.out + ((int64_t)row * a.qn + h0 + i) * 512 + 8 * l) = rowv[i];
   }
 }
 
