@@ -362,3 +362,18 @@ def test_timing_hook_stamps_the_forward_kernel():
     got = [t for t in (call.out, call.lse) if t is not None]
     for x, y in zip(ref, got):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("separate_v", [True, False])
+def test_topk_rows_long_and_short_sequences_partial_head_block(separate_v):
+    """TopK lists in a sequence of 70 queries (one split of up to 2048 rows
+    per row, so the first index batch is reloaded, not taken from the
+    early loads) next to a short sequence (three 512-row splits merged,
+    through LDS staging when V is separate), with 20 heads (the second
+    16-head block is partly past q_n)."""
+    P = synth.random_tiny(613, family="sfa", layout_q="TND", layout_kv="PA_BSND", q_lens=[70, 3],
+                          ori_lens=[3000, 2500], topk=1100, num_heads_q=20, rope_head_dim=64,
+                          separate_v=separate_v, block_size=16, win=(-1, -1), masks=(3, 0))
+    rows = [0, 35, 69, 70, 72]
+    res = run_gpu(P)
+    check_outputs(P, res, oracle.forward(P, rows=rows), rows)
