@@ -29,6 +29,7 @@ HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "sparse_shared_kv_amd", "csrc", "sfmla_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_%s_%s.txt")      # (kernel, workload)
+MFMA_FILE = os.path.join(PROFILES, "mfma_%s_%s.txt")            # (kernel, workload)
 
 DESCR = {
     "sfa_mla_rope": "token-wise sparse MLA-absorb decode with rope: B=32, q_s=2, q_n=128, "
@@ -76,6 +77,33 @@ def row_bytes(P) -> tuple:
 def kernel_name(P) -> str:
     """The forward kernel (one template for every KV format)."""
     return "fwd_kernel"
+
+
+def read_summary(path: str):
+    """key = value lines of a committed rocprofv3 summary, if it was taken
+    on the current kernel source (else None)."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for ln in open(path):
+        if "=" in ln and not ln.startswith("#"):
+            k, v = ln.split("=", 1)
+            vals[k.strip()] = v.strip()
+    return vals if vals.get("kernel_source_sha256_16") == kernel_source_hash() else None
+
+
+def read_mfma(kernel: str, workload: str):
+    """MFMA utilisation (%) and issued MFMA flops per launch from the committed
+    counter summary of the current kernel source (else None)."""
+    v = read_summary(MFMA_FILE % (kernel, workload))
+    if v is None:
+        return None
+    try:
+        return {"util_pct": float(v["mfma_util_pct"]),
+                "flops_issued": float(v["mfma_flops_bf16_per_dispatch"]) +
+                                float(v["mfma_flops_f16_per_dispatch"])}
+    except (KeyError, ValueError):
+        return None
 
 
 def read_traffic(kernel: str, workload: str):
@@ -126,7 +154,10 @@ COPY_PROBE_MB = 256
 def profile_commands(outdir: str, workload: str) -> list:
     """The rocprofv3 runs whose summaries are kept under profiles/: one
     kernel trace with statistics, then one counter pass each for FETCH_SIZE
-    and WRITE_SIZE (with a plain device copy of known size for calibration)."""
+    and WRITE_SIZE (with a plain device copy of known size for calibration)
+    and one for the MFMA counters (rocprofv3's derived MfmaUtil, MFMA busy
+    cycles over active cycles of all SIMDs, and MfmaFlopsBF16 / F16, the
+    MFMA operations issued)."""
     b = "python3 bench.py --workload %s --no-cpu-baseline" % workload
     return [
         "rocprofv3 --kernel-trace --stats --output-format csv -d %s/trace -o trace -- %s"
@@ -135,6 +166,8 @@ def profile_commands(outdir: str, workload: str) -> list:
         "--warmup 2 --settle-ms 0 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s/write -o write -- %s --steps 5 "
         "--warmup 2 --settle-ms 0 --copy-probe-mb %d" % (outdir, b, COPY_PROBE_MB),
+        "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 --output-format csv -d %s/mfma "
+        "-o mfma -- %s --steps 5 --warmup 2 --settle-ms 0" % (outdir, b),
     ]
 
 
@@ -204,6 +237,31 @@ def write_profiles(outdir: str, workload: str) -> None:
              "hbm_write_bytes_per_launch = %.0f" % (wk * 1024.0 * wf),
              "hbm_bytes_per_launch = %.0f" % hbm]
     path = TRAFFIC_FILE % (kern, workload)
+    open(path, "w").write("\n".join(lines) + "\n")
+    log("[profiles] wrote", path)
+
+    # MFMA utilisation and issued MFMA flops
+    f = glob.glob(os.path.join(outdir, "mfma", "**", "*counter_collection.csv"), recursive=True)
+    assert f, "no counter_collection.csv under %s/mfma" % outdir
+    per = defaultdict(list)
+    for r in csv.DictReader(open(f[0])):
+        if kern + "<" in r["Kernel_Name"] or ("::" + kern + "(") in r["Kernel_Name"]:
+            per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    assert per.get("MfmaUtil"), "no MfmaUtil values for %s in %s" % (kern, f[0])
+    mean = lambda k: sum(per[k]) / len(per[k]) if per.get(k) else 0.0
+    lines = ["# MFMA counters of %s, workload %s (rocprofv3 derived counters, per dispatch)"
+             % (kern, workload),
+             "# command (from the repository root):", "#   " + cmds[3],
+             "# MfmaUtil = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs);",
+             "# MfmaFlops* = SQ_INSTS_VALU_MFMA_MOPS_* * 512 (issued MFMA flops)",
+             "kernel = %s" % kern,
+             "workload = %s" % workload,
+             "kernel_source_sha256_16 = %s" % src,
+             "dispatches = %d" % len(per["MfmaUtil"]),
+             "mfma_util_pct = %.2f" % mean("MfmaUtil"),
+             "mfma_flops_bf16_per_dispatch = %.0f" % mean("MfmaFlopsBF16"),
+             "mfma_flops_f16_per_dispatch = %.0f" % mean("MfmaFlopsF16")]
+    path = MFMA_FILE % (kern, workload)
     open(path, "w").write("\n".join(lines) + "\n")
     log("[profiles] wrote", path)
 
@@ -363,6 +421,7 @@ def main():
         achieved, peak, unit = fwd_flops / fwd_avg_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     kern = kernel_name(P)
     traffic = read_traffic(kern, args.workload)
+    mfma = read_mfma(kern, args.workload)
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 4
@@ -405,7 +464,10 @@ def main():
                      "algorithmic_bytes_per_launch": round(fwd_bytes, 0),
                      "algorithmic_flops_per_launch": round(fwd_flops, 0),
                      "bytes_per_row": rb, "flops_per_row_head": fl_row,
-                     "timed_launches": len(fwd_ms)},
+                     "timed_launches": len(fwd_ms),
+                     # rocprofv3 MfmaUtil of the same kernel source (profiles/), or null
+                     "mfma_util_pct": None if mfma is None else mfma["util_pct"],
+                     "mfma_flops_issued": None if mfma is None else round(mfma["flops_issued"], 0)},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
