@@ -528,19 +528,24 @@ __device__ __forceinline__ void issue_raw(const FwdArgs& a, const uint32_t* sRow
                                           uint32_t ldsRaw, int w, int l) {
   using P = PackedPipe<NW, DQK>;
   const uint32_t base = __builtin_amdgcn_readfirstlane(ldsRaw + w * P::PER * 1024);
-  constexpr int B = 8;                                        // addresses read per batch
+  // every row entry first (one LDS round trip for all), then branch-free
+  // addresses: a slot without a row, and chunks past the tile (the last
+  // wave's tail), read the zero row
+  uint32_t e[P::PER];
 #pragma unroll
-  for (int q0 = 0; q0 < P::PER; q0 += B) {
-    const char* src[B];
+  for (int q = 0; q < P::PER; ++q) {
+    const int c = (w * P::PER + q) * 64 + l;                  // chunk index in the tile
+    e[q] = sRow[tbase + min(c / P::CPR, kTile - 1)];
+  }
 #pragma unroll
-    for (int q = q0; q < q0 + B && q < P::PER; ++q) {
-      const int c = (w * P::PER + q) * 64 + l;                // chunk index in the tile
-      const int r = c < kTile * P::CPR ? c / P::CPR : 0;
-      const char* rowp = k_addr(a, sRow[tbase + r]);
-      src[q - q0] = c < kTile * P::CPR ? rowp + 16 * (c - r * P::CPR) : (const char*)g_zero_row;
-    }
-#pragma unroll
-    for (int q = q0; q < q0 + B && q < P::PER; ++q) dma16(src[q - q0], base + q * 1024);
+  for (int q = 0; q < P::PER; ++q) {
+    const int c = (w * P::PER + q) * 64 + l;
+    const int r = c / P::CPR;
+    const bool cmp = e[q] & kCmpBit;
+    const char* rowp = row_at(cmp ? a.cmp_kv : a.ori_kv, e[q] & ~kCmpBit,
+                              cmp ? a.cmp_stride : a.ori_stride);
+    const bool zero = e[q] == kNoRow || c >= kTile * P::CPR;
+    dma16(zero ? (const char*)g_zero_row : rowp + 16 * (c - r * P::CPR), base + q * 1024);
   }
 }
 
@@ -594,7 +599,7 @@ __device__ __forceinline__ void decode_tile(const char* raw, char* kbf, float* s
 // same (stale) max, so the result is unchanged while the accumulators are
 // touched only when the max jumps.
 constexpr float kRescaleThreshold = 8.0f;
-constexpr int kMergeSplits = 4;       // splits whose partials one merge round loads
+constexpr int kMergeSplits = 4;       // splits whose partials one merge round loads (8 waves)
 
 // HB head blocks of 16 heads per wave; FMT is the KV storage format.
 template <int NW, int HB, int DQK, int VMODE, int FMT>
@@ -1100,10 +1105,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   if (l == 0)                                       // ready for the next call
     __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // merge from the stored partials (this split's own included).  Round r
-  // loads column blocks [JB*(r / ns4), +JB) of kMergeSplits splits (16 loads
-  // of 16 bytes per lane in flight); the first round travels together with
-  // the loads of the LSEs, which give the max and the normaliser in one pass.
-  constexpr int MS = kMergeSplits, JB = 4, NJ = 16 / JB;
+  // loads column blocks [JB*(r / ns4), +JB) of MS splits (MS*JB loads of 16
+  // bytes per lane in flight: 16, or 32 where one wave per SIMD leaves the
+  // registers); the first round travels together with the loads of the
+  // LSEs, which give the max and the normaliser in one pass.
+  constexpr int MS = NW <= 4 ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = 16 / JB;
   const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
   const int R = NJ * ns4;                               // load rounds
   const int split_bytes = a.groups * NW * WAVE_BYTES;
