@@ -45,6 +45,11 @@ DESCR = {
                      "TopK 2048 of 16K-131K tokens",
     "hca_varlen": "HCA varlen TND: B=8, q_n=128, window 128 + all visible compressed rows "
                   "(ratio 128), contexts 16K-131K, sinks",
+    "c8_packed_int8_q32": "throughput mode of c8_packed_int8: the same 8 contexts with 32 query "
+                          "tokens each (256 query rows, each its own causal TopK 2048), INT8 "
+                          "packed KV, q_n=128, d_qk=576",
+    "hca_varlen_q32": "throughput mode of hca_varlen: the same 8 contexts with 32 query tokens "
+                      "each (256 query rows, window 128 + all visible compressed rows), sinks",
     "csa_decode_paged": "CSA paged decode: B=4, q_n=64, window 128 + TopK 512 of 8192 "
                         "compressed rows (ratio 4), PA block 128, sinks",
     "swa_decode": "SWA decode: B=2, q_n=16, window 128 of 512, BSND",

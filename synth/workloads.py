@@ -171,31 +171,34 @@ def _varlen_lengths(seed):
     return _gen(s_len).integers(16384, 131072 + 1, size=8).astype(np.int64)
 
 
-def hca_varlen(seed=3):
+def hca_varlen(seed=3, qps=1):
     """HCA varlen TND: B=8, q_n=128, d=512; contexts ~ U[16384, 131072];
     window 128; cmp_ratio 128 with every causally visible compressed row;
-    kv ~ N(0,1), q ~ N(0, 0.5^2); sinks ~ N(0,1); LSE returned."""
+    kv ~ N(0,1), q ~ N(0, 0.5^2); sinks ~ N(0,1); LSE returned.  qps > 1:
+    the same contexts with qps query tokens per sequence (the last qps
+    positions, each with its own window and compressed-row limit), a
+    throughput-mode variant of the decode."""
     s_q, s_ori, s_cmp, s_sink = _seqs(seed, 4)
     B, qn, d, r = 8, 128, 512, 128
     L = _varlen_lengths(seed)
     C = L // r
     arrays = dict(
-        q=normal_bf16(s_q, (B, qn, d), std=0.5),
+        q=normal_bf16(s_q, (B * qps, qn, d), std=0.5),
         ori_kv=banked_rows(s_ori, int(L.sum()), lambda s, n: normal_bf16(s, (n, d))),
         cmp_kv=banked_rows(s_cmp, int(C.sum()), lambda s, n: normal_bf16(s, (n, d))),
-        cu_seqlens_q=np.arange(B + 1, dtype=np.int32),
+        cu_seqlens_q=_prefix([qps] * B),
         cu_seqlens_ori_kv=_prefix(L), cu_seqlens_cmp_kv=_prefix(C),
         cmp_residual_kv=(L % r).astype(np.int32),
         sinks=_gen(s_sink).standard_normal(qn, dtype=np.float32),
     )
     params = _base_params(
-        num_heads_q=qn, batch_size=B, layout_q="TND", layout_kv="TND", q_t=B,
-        max_seqlen_q=1, max_seqlen_ori_kv=int(L.max()),
+        num_heads_q=qn, batch_size=B, layout_q="TND", layout_kv="TND", q_t=B * qps,
+        max_seqlen_q=qps, max_seqlen_ori_kv=int(L.max()),
         max_seqlen_cmp_kv=int(C.max()), cmp_ratio=r, ori_mask_mode=4,
         ori_win_left=127, ori_win_right=0, cmp_mask_mode=3, has_cmp_kv=True,
         softmax_scale=1.0 / math.sqrt(d))
-    return Problem("hca_varlen", seed, params, arrays,
-                   "contexts %s" % L.tolist())
+    name = "hca_varlen" if qps == 1 else "hca_varlen_q%d" % qps
+    return Problem(name, seed, params, arrays, "contexts %s" % L.tolist())
 
 
 def _sfa_indices(seq, batch, q_s, kv_len, topk, sbs=1):
@@ -245,36 +248,42 @@ def sfa_mla_rope(seed=4, batch=32, q_s=2, kv_len=65536, topk=2048, bs=64, fp16=F
                    "q, K, V ~ N(0,1) %s; %s" % ("float16" if fp16 else "bf16", what))
 
 
-def _c8_indices(seq, L, topk):
+def _c8_indices(seq, L, topk, qps=1):
+    """Per query token, TopK entries drawn without replacement from its
+    causal range: the token at position p = L - qps + i sees [0, p]."""
     g_idx = _gen(seq)
-    idx = np.stack([g_idx.choice(int(n), topk, replace=False) for n in L]).astype(np.int32)
-    return idx.reshape(len(L), 1, topk)
+    idx = np.stack([g_idx.choice(int(n) - qps + 1 + i, topk, replace=False)
+                    for n in L for i in range(qps)]).astype(np.int32)
+    return idx.reshape(len(L) * qps, 1, topk)
 
 
-def c8_packed(seed=5, fmt="int8", topk=2048):
+def c8_packed(seed=5, fmt="int8", topk=2048, qps=1):
     """Quantised packed KV: the HCA-varlen shapes (TND, B=8, q_n=128, the same
     context lengths) with Q_D=576 and 656-byte packed rows (512 INT8 or
     FP8-E4M3 codes, 64 bf16 rope values, 4 fp32 per-128-tile scales), V =
-    dequantised nope; TopK 2048 over each sequence's positions."""
+    dequantised nope; TopK 2048 over each sequence's positions.  qps > 1:
+    qps query tokens per sequence (the last qps positions, each with its own
+    causal TopK list), a throughput-mode variant of the decode."""
     s_q, s_kv, s_idx = _seqs(seed, 3)
     B, qn, dq = 8, 128, 576
     L = _varlen_lengths(3)
-    idx = _c8_indices(s_idx, L, topk)
+    idx = _c8_indices(s_idx, L, topk, qps)
     arrays = dict(
-        q=normal_bf16(s_q, (B, qn, dq), std=0.5),
+        q=normal_bf16(s_q, (B * qps, qn, dq), std=0.5),
         ori_kv=banked_rows(s_kv, int(L.sum()), lambda s, n: packed_rows(s, n, 64, fmt)),
-        cu_seqlens_q=np.arange(B + 1, dtype=np.int32),
+        cu_seqlens_q=_prefix([qps] * B),
         cu_seqlens_ori_kv=_prefix(L),
         ori_sparse_indices=idx,
     )
     params = _base_params(
         num_heads_q=qn, rope_head_dim=64, batch_size=B, layout_q="TND",
-        layout_kv="TND", q_t=B, max_seqlen_q=1,
+        layout_kv="TND", q_t=B * qps, max_seqlen_q=qps,
         max_seqlen_ori_kv=int(L.max()), ori_topk=topk, ori_mask_mode=3,
         has_cmp_kv=False,
         kv_dtype="int8_packed" if fmt == "int8" else "fp8_e4m3_packed",
         softmax_scale=1.0 / math.sqrt(dq))
-    return Problem("c8_packed_" + fmt, seed, params, arrays,
+    name = "c8_packed_" + fmt + ("" if qps == 1 else "_q%d" % qps)
+    return Problem(name, seed, params, arrays,
                    "packed %s rows, contexts %s" % (fmt, L.tolist()))
 
 
@@ -288,6 +297,9 @@ WORKLOADS = {
     "sfa_mla_rope_block16": lambda seed=4: sfa_mla_rope(seed, sbs=16),
     "c8_packed_int8": lambda seed=5: c8_packed(seed, "int8"),
     "c8_packed_fp8": lambda seed=5: c8_packed(seed, "fp8"),
+    # throughput mode: 32 query tokens per sequence, 256 query rows per call
+    "c8_packed_int8_q32": lambda seed=5: c8_packed(seed, "int8", qps=32),
+    "hca_varlen_q32": lambda seed=3: hca_varlen(seed, qps=32),
 }
 
 
@@ -310,7 +322,8 @@ def index_replicas(P: Problem, n: int):
                 p["sparse_block_size"])))
         elif P.name.startswith("c8_packed"):
             cu = P.arrays["cu_seqlens_ori_kv"]
-            out.append(("ori_sparse_indices", _c8_indices(seq, np.diff(cu), P.params["ori_topk"])))
+            out.append(("ori_sparse_indices", _c8_indices(
+                seq, np.diff(cu), P.params["ori_topk"], P.params["max_seqlen_q"])))
         elif P.name == "csa_decode_paged":
             p = P.params
             out.append(("cmp_sparse_indices", _csa_indices(
