@@ -45,6 +45,13 @@ DESCR = {
                      "TopK 2048 of 16K-131K tokens",
     "hca_varlen": "HCA varlen TND: B=8, q_n=128, window 128 + all visible compressed rows "
                   "(ratio 128), contexts 16K-131K, sinks",
+    "hca_prefill": "HCA prefill (the SparseAttnSharedkv call example's shapes with all "
+                   "visible compressed rows): B=4 x 128 query tokens, q_n=64, window 128 + "
+                   "<=1024 compressed rows (ratio 4), 4096 cached tokens, PA block 128, sinks",
+    "swa_prefill": "SWA prefill: B=4 x 128 query tokens, q_n=64, window 128 of 4096 cached "
+                   "tokens, PA block 128, sinks",
+    "swa_prefill_h16": "SWA prefill with 16 heads: B=4 x 128 query tokens, q_n=16, window 128 "
+                       "of 4096 cached tokens, PA block 128, sinks",
     "c8_packed_int8_q32": "throughput mode of c8_packed_int8: the same 8 contexts with 32 query "
                           "tokens each (256 query rows, each its own causal TopK 2048), INT8 "
                           "packed KV, q_n=128, d_qk=576",

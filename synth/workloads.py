@@ -166,6 +166,47 @@ def csa_prefill(seed=6):
                    "q ~ U(-10,10), kv ~ U(-5,10) bf16; 128 query tokens per sequence")
 
 
+def rule_prefill(seed=7, family="hca", qn=64):
+    """Prefill whose lists are rules, with the shapes of the SparseAttnSharedkv
+    README's call example: B=4 sequences of 128 query tokens (TND), d=512,
+    4096 cached tokens each in 128-token pages, window (127, 0); "hca" adds
+    cmp_ratio 4 (1024 compressed rows) with every causally visible compressed
+    row, "swa" has the window only.  q ~ U(-10, 10), kv ~ U(-5, 10), sinks ~
+    U(0, 1) as in the example."""
+    s_q, s_ori, s_cmp, s_tab, s_sink = _seqs(seed, 5)
+    B, s1, d, bs, L, r = 4, 128, 512, 128, 4096, 4
+    C = L // r
+    g_tab = _gen(s_tab)
+    ori_blocks = B * L // bs
+    ori_bt = g_tab.permutation(ori_blocks).astype(np.int32).reshape(B, L // bs)
+    arrays = dict(
+        q=bf16_bits(_gen(s_q).uniform(-10, 10, (B * s1, qn, d)).astype(np.float32)),
+        ori_kv=bf16_bits(_gen(s_ori).uniform(-5, 10, (ori_blocks * bs, d)).astype(np.float32)),
+        ori_block_table=ori_bt,
+        cu_seqlens_q=_prefix([s1] * B),
+        seqused_ori_kv=np.full(B, L, np.int32),
+        sinks=_gen(s_sink).uniform(0, 1, qn).astype(np.float32),
+    )
+    hca = family == "hca"
+    if hca:
+        cmp_blocks = B * ((C + bs - 1) // bs)
+        arrays.update(
+            cmp_kv=bf16_bits(_gen(s_cmp).uniform(-5, 10, (cmp_blocks * bs, d)).astype(np.float32)),
+            cmp_block_table=g_tab.permutation(cmp_blocks).astype(np.int32).reshape(
+                B, cmp_blocks // B),
+            seqused_cmp_kv=np.full(B, C, np.int32),
+            cmp_residual_kv=np.zeros(B, np.int32))
+    params = _base_params(
+        num_heads_q=qn, batch_size=B, layout_q="TND", layout_kv="PA_BSND",
+        q_t=B * s1, ori_block_size=bs, cmp_block_size=bs if hca else 0, max_seqlen_q=s1,
+        max_seqlen_ori_kv=L, max_seqlen_cmp_kv=C if hca else 0, cmp_ratio=r if hca else 1,
+        ori_mask_mode=4, ori_win_left=127, ori_win_right=0, cmp_mask_mode=3 if hca else 0,
+        has_cmp_kv=hca, softmax_scale=1.0 / 24.0)
+    name = "%s_prefill" % family + ("" if qn == 64 else "_h%d" % qn)
+    return Problem(name, seed, params, arrays,
+                   "q ~ U(-10,10), kv ~ U(-5,10) bf16; 128 query tokens per sequence")
+
+
 def _varlen_lengths(seed):
     (s_len,) = _seqs(seed * 1000 + 7, 1)
     return _gen(s_len).integers(16384, 131072 + 1, size=8).astype(np.int64)
@@ -297,6 +338,9 @@ WORKLOADS = {
     "sfa_mla_rope_block16": lambda seed=4: sfa_mla_rope(seed, sbs=16),
     "c8_packed_int8": lambda seed=5: c8_packed(seed, "int8"),
     "c8_packed_fp8": lambda seed=5: c8_packed(seed, "fp8"),
+    "hca_prefill": lambda seed=7: rule_prefill(seed, "hca"),
+    "swa_prefill": lambda seed=8: rule_prefill(seed, "swa"),
+    "swa_prefill_h16": lambda seed=9: rule_prefill(seed, "swa", qn=16),
     # throughput mode: 32 query tokens per sequence, 256 query rows per call
     "c8_packed_int8_q32": lambda seed=5: c8_packed(seed, "int8", qps=32),
     "hca_varlen_q32": lambda seed=3: hca_varlen(seed, qps=32),
