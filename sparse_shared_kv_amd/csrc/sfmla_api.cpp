@@ -157,9 +157,10 @@ int64_t max_list(const sfmla_params& p) {
 }
 
 // KV rows per split: a function of the parameters only (never of the batch),
-// so a query row is split the same way in any batch (the planner lets rows
-// of sequences with at least kLongQuery queries take up to kMaxSplitRows per
-// split instead, a property of the row's own sequence).  Rows of 2 KB or more
+// so a query row is split the same way in any batch (the planner lengthens
+// the splits of rows of sequences with many queries, one more step of this
+// size per kQueriesPerStep queries up to kMaxSplitRows, a property of the
+// row's own sequence).  Rows of 2 KB or more
 // (a K row with rope plus a separate V row) get 512-row splits, which keep
 // the number of partials to merge low; lighter rows (1 KB bf16 rows with
 // V = K, packed rows) get 256-row splits, which keep each workgroup's serial

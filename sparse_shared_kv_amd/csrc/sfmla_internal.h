@@ -10,7 +10,7 @@ namespace sfmla {
 
 constexpr int kTile = 32;          // KV rows staged in LDS per step
 constexpr int kMaxSplitRows = 2048;   // most KV rows per split of one query row (LDS row table)
-constexpr int kLongQuery = 64;     // queries of a sequence from which its rows split less
+constexpr int kQueriesPerStep = 16;   // queries of a sequence per step of longer splits
 constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
 constexpr int kCounterInts = 64;   // arrival counters per query row (one per head group x wave)
@@ -43,7 +43,7 @@ struct PlanArgs {
   uint32_t fingerprint;
   int32_t max_splits;
   int32_t split_rows;               // KV rows per split (multiple of the tile, <= kMaxSplitRows)
-  int32_t split_rows_long;          // the same for rows of sequences of >= kLongQuery queries
+  int32_t split_rows_long;          // the longest split of a row of a sequence with many queries
 };
 
 struct FwdArgs {

@@ -220,10 +220,12 @@ __global__ void plan_kernel(PlanArgs a) {
   if (!valid) { ori_cnt = 0; cmp_cnt = 0; }
   const int n = ori_cnt + cmp_cnt;
   // A sequence with many queries already gives the launch many rows: its
-  // rows keep their list in as few splits as the row table allows, which
-  // saves the partials' round trip and merge.  Depends on the row's own
-  // sequence only, so a sequence splits the same way in any batch.
-  const int srows = q_used >= kLongQuery ? a.split_rows_long : a.split_rows;
+  // rows take longer splits, one more split_rows per kQueriesPerStep
+  // queries, up to what the row table holds (fewer partials to write, read
+  // back and merge).  Depends on the row's own sequence only, so a sequence
+  // splits the same way in any batch.
+  const int steps = q_used / kQueriesPerStep;
+  const int srows = min(a.split_rows_long, a.split_rows * (steps > 1 ? steps : 1));
   int nsplit = n > 0 ? (n + srows - 1) / srows : 1;
   int chunk = srows;
   if (nsplit > a.max_splits) {
