@@ -227,6 +227,24 @@ def test_batch_invariance_with_long_query_sequences_bitwise():
         assert np.array_equal(got, per_b[b]), b
 
 
+def test_split_steps_by_query_count_bitwise():
+    """Sequences of 17, 33 and 48 queries take 1, 2 and 3 steps of the split
+    length (one per 16 queries); each sequence gives the same bits alone and
+    inside a batch, and matches the oracle."""
+    L = logical(27, q_lens=[33, 17, 48, 2], ori_lens=[2600, 2200, 3000, 900], qn=32, ratio=2,
+                cmp_topk=900, win=(127, 0))
+    full = place(L, "TND", "PA_BSND", bs=16, seed=1)
+    res = run_gpu(full)
+    rows = [0, 32, 33, 49, 50, 97, 98, 99]
+    check_outputs(full, res, oracle.forward(full, rows=rows), rows)
+    per_b = unplace_o(full, res["O"], L)
+    for b in (0, 1, 2):
+        Lb = {k: ([v[b]] if isinstance(v, list) and len(v) == 4 else v) for k, v in L.items()}
+        one = place(Lb, "TND", "PA_BSND", bs=16, seed=2)
+        got = run_gpu(one)["O"]
+        assert np.array_equal(got, per_b[b]), b
+
+
 def test_layout_invariance_bitwise():
     L = logical(23, q_lens=[3, 1, 4], ori_lens=[700, 90, 1500], qn=64, ratio=4, cmp_topk=100)
     outs = []
