@@ -45,6 +45,8 @@ DESCR = {
                      "TopK 2048 of 16K-131K tokens",
     "hca_varlen": "HCA varlen TND: B=8, q_n=128, window 128 + all visible compressed rows "
                   "(ratio 128), contexts 16K-131K, sinks",
+    "c8_packed_int8_rope0": "INT8 packed KV without rope (528-B rows), TND B=8, q_n=128, "
+                            "d_qk=512, TopK 2048 of 16K-131K tokens",
     "hca_prefill": "HCA prefill (the SparseAttnSharedkv call example's shapes with all "
                    "visible compressed rows): B=4 x 128 query tokens, q_n=64, window 128 + "
                    "<=1024 compressed rows (ratio 4), 4096 cached tokens, PA block 128, sinks",

@@ -31,7 +31,8 @@ def _gpu():
 
 FULL = ["swa_decode", "csa_decode_paged", "hca_varlen", "sfa_mla_rope", "c8_packed_int8",
         "c8_packed_fp8", "csa_prefill", "sfa_mla_rope_fp16", "sfa_mla_rope_block16",
-        "c8_packed_int8_q32", "hca_varlen_q32", "hca_prefill", "swa_prefill", "swa_prefill_h16"]
+        "c8_packed_int8_q32", "hca_varlen_q32", "hca_prefill", "swa_prefill", "swa_prefill_h16",
+        "c8_packed_int8_rope0"]
 # query rows the oracle recomputes at full size (all rows for the others)
 SAMPLE = {"sfa_mla_rope": [0, 1, 2, 17, 30, 31, 45, 62, 63],
           "sfa_mla_rope_fp16": [0, 5, 33, 63], "sfa_mla_rope_block16": [0, 7, 40, 63],
