@@ -210,7 +210,7 @@ sfmla_status sfmla_metadata_size(const sfmla_params* params, size_t* n_ints);
  * Build the split plan (sparse_flash_mla_metadata on the API page): per query
  * row its batch, position, resolved window / list extents and split count,
  * plus a fingerprint of `params`.  Reads the length tensors on the device.
- * `metadata` holds at least sfmla_metadata_size() int32.
+ * `metadata` holds at least sfmla_metadata_size() int32, 16-byte aligned.
  */
 sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* lengths,
                             int32_t* metadata, size_t n_ints, void* stream);

@@ -251,6 +251,7 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
                            size_t n_ints, float scale, sfmla::FwdArgs* a) {
   REQUIRE(t != nullptr, "tensors is NULL");
   REQUIRE(meta != nullptr, "metadata is NULL");
+  REQUIRE(aligned16(meta), "metadata must be 16-byte aligned");
   if (n_ints < metadata_ints(p))
     return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "metadata holds %zu int32, needs %zu", n_ints,
                 metadata_ints(p));
@@ -393,6 +394,7 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
   const sfmla_params& p = *params;
   REQUIRE(len != nullptr, "lengths is NULL");
   REQUIRE(metadata != nullptr, "metadata is NULL");
+  REQUIRE(aligned16(metadata), "metadata must be 16-byte aligned");
   if (n_ints < metadata_ints(p))
     return fail(SFMLA_ERR_BUFFER_TOO_SMALL, "metadata holds %zu int32, needs %zu", n_ints,
                 metadata_ints(p));

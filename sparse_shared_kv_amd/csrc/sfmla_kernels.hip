@@ -152,6 +152,13 @@ __global__ void plan_kernel(PlanArgs a) {
     a.meta[3] = a.max_splits;
     for (int i = 4; i < kHeaderInts; ++i) a.meta[i] = 0;
   }
+  {
+    // arrival counters of every row, zeroed by all threads with coalesced
+    // 16-byte stores (q_t * kCounterInts ints, a multiple of 4)
+    uint4* cnt = (uint4*)(a.meta + kHeaderInts + (int64_t)p.q_t * kRecInts);
+    const int64_t n4 = (int64_t)p.q_t * (kCounterInts / 4);
+    for (int64_t k = row; k < n4; k += (int64_t)gridDim.x * blockDim.x) cnt[k] = make_uint4(0, 0, 0, 0);
+  }
   if (row >= p.q_t) return;
   int b, i, q_len;
   if (p.layout_q == SFMLA_LAYOUT_BSND) {
@@ -239,8 +246,6 @@ __global__ void plan_kernel(PlanArgs a) {
   r[R_ORI_BASE] = ori_base; r[R_CMP_BASE] = cmp_base; r[R_ORI_LEN] = ori_len;
   r[R_CMP_LEN] = cmp_len; r[R_NSPLIT] = nsplit; r[R_CHUNK] = chunk;
   r[R_CMP_LIMIT] = cmp_limit; r[R_NTOTAL] = n;
-  int32_t* cnt = a.meta + kHeaderInts + (int64_t)p.q_t * kRecInts + (int64_t)row * kCounterInts;
-  for (int i = 0; i < kCounterInts; ++i) cnt[i] = 0;
 }
 
 // ---------------------------------------------------------------------------

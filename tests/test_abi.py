@@ -131,6 +131,14 @@ def test_metadata_buffer_too_small():
     assert e.value.status == 3
 
 
+def test_metadata_buffer_misaligned():
+    p = _params()
+    lens = s.Lengths()
+    with pytest.raises(s.SfmlaError, match="16-byte aligned"):
+        s._abi.check(s._abi.load().sfmla_metadata(ctypes.byref(p), ctypes.byref(lens),
+                                                   ctypes.c_void_p(20), 10 ** 6, None))
+
+
 def test_forward_rejects_bad_tensors_without_launching():
     p = _params()
     t = s.Tensors()
