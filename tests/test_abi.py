@@ -170,6 +170,44 @@ def test_workspace_sizes():
         assert (ws > 0) == expect_split, name
 
 
+def _expected_workspace(P):
+    """The split partials' workspace from the host's documented policy:
+    512-row splits for rows of 2 KB or more, 256 otherwise; head groups of
+    1/2/4/8 16-head blocks (at most 4 per group for packed rows), halved
+    while the grid would have fewer than 256 workgroups; one bf16 partial
+    (1 KB per padded head) and one fp32 LSE per (row, split, padded head)."""
+    p = P.params
+    packed = p["kv_dtype"] not in ("bf16", "fp16")
+    rope = p["rope_head_dim"]
+    row = 512 + 2 * rope + 16 if packed else 2 * (512 + rope) + (1024 if p["separate_v"] else 0)
+    srows = 512 if row >= 2048 else 256
+    n = p["ori_topk"] * p["sparse_block_size"]          # TopK-only lists here
+    splits = -(-n // srows)
+    if splits <= 1:
+        return 0
+    blocks = -(-p["num_heads_q"] // 16)
+    wmax = 4 if packed else 8
+    per = 1
+    while per < wmax and per < blocks:
+        per *= 2
+    units = p["q_t"] * splits
+    while per > 1 and units * -(-blocks // per) < 256:
+        per //= 2
+    heads = -(-blocks // per) * wmax * 16
+    slots = p["q_t"] * splits * heads
+    up = lambda x: -(-x // 256) * 256
+    return up(slots * 1024) + up(slots * 4)
+
+
+def test_workspace_size_follows_split_and_group_policy():
+    from synth.workloads import sfa_mla_rope
+    cases = [_small_sfa(), sfa_mla_rope(batch=32, q_s=2, kv_len=4096, topk=2048),
+             synth.make_workload("c8_packed_int8")]
+    for P in cases:
+        p = s.make_params(P.params, P.arrays)
+        assert s.sfmla_workspace_size(p) == _expected_workspace(P), P.name
+
+
 def _small_sfa():
     from synth.workloads import sfa_mla_rope
     return sfa_mla_rope(batch=2, q_s=2, kv_len=4096, topk=2048)
