@@ -328,12 +328,19 @@ def test_rope_free_rows_equal_zero_rope_rows_bitwise(fmt):
     check_outputs(P528, b, ref, [0, 1])
 
 
-def test_graph_replay_matches_eager():
+GRAPH_CASES = [dict(),                                        # bf16, separate V (staged merge)
+               dict(kv_dtype="int8_packed", rope_head_dim=64),
+               dict(separate_v=False, rope_head_dim=0)]         # V = K nope
+
+
+@pytest.mark.parametrize("kw", GRAPH_CASES, ids=["separate_v", "packed", "shared_v"])
+def test_graph_replay_matches_eager(kw):
     """plan + forward + combine captured in one HIP graph: every replay,
     with other eager work and synchronisations in between, reproduces the
-    eager result bit for bit."""
+    eager result bit for bit (split rows merged in the launch: the arrival
+    counters must come back to zero on every replay)."""
     import sparse_shared_kv_amd as s
-    P = synth.random_tiny(602, family="sfa", max_kv=3000, topk=1500, num_heads_q=128)
+    P = synth.random_tiny(602, family="sfa", max_kv=3000, topk=1500, num_heads_q=128, **kw)
     other = synth.random_tiny(603, family="csa", num_heads_q=64, max_kv=900)
     call = s.Call(P.params, P.arrays)
     eager = [t.clone() for t in call.run() if t is not None]
