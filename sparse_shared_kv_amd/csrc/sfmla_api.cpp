@@ -175,7 +175,23 @@ int split_rows(const sfmla_params& p) {
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int row_bytes = packed ? 512 + 2 * p.rope_head_dim + 16
                                : 2 * (512 + p.rope_head_dim) + (p.has_separate_v ? 1024 : 0);
-  return row_bytes >= 2048 ? 512 : 256;
+  const int base = row_bytes >= 2048 ? 512 : 256;
+  // Where the parameters alone bound the list (TopK slot counts, a window
+  // open on both sides), the longest list is cut into even splits of at most
+  // `base` rows, so its last split is not a short tail
+  int64_t n = 0;
+  if (p.ori_topk > 0) n = (int64_t)p.ori_topk * p.ori_sparse_block_size;
+  else if (p.ori_mask_mode == SFMLA_MASK_BAND && p.ori_win_left >= 0 && p.ori_win_right >= 0)
+    n = (int64_t)p.ori_win_left + p.ori_win_right + 1;
+  else return base;
+  if (p.has_cmp_kv) {
+    if (p.cmp_topk <= 0) return base;                    // all visible rows: data-dependent
+    n += p.cmp_topk;
+  }
+  if (n <= base) return base;
+  const int64_t s = (n + base - 1) / base;
+  const int64_t even = ((n + s - 1) / s + sfmla::kTile - 1) / sfmla::kTile * sfmla::kTile;
+  return (int)even;
 }
 
 int max_splits(const sfmla_params& p) {

@@ -180,8 +180,10 @@ def _expected_workspace(P):
     packed = p["kv_dtype"] not in ("bf16", "fp16")
     rope = p["rope_head_dim"]
     row = 512 + 2 * rope + 16 if packed else 2 * (512 + rope) + (1024 if p["separate_v"] else 0)
-    srows = 512 if row >= 2048 else 256
-    n = p["ori_topk"] * p["sparse_block_size"]          # TopK-only lists here
+    base = 512 if row >= 2048 else 256
+    n = p["ori_topk"] * p["sparse_block_size"] + p["cmp_topk"]   # TopK lists here
+    parts = -(-n // base)
+    srows = -(-(-(-n // parts)) // 32) * 32 if n > base else base   # even splits
     splits = -(-n // srows)
     if splits <= 1:
         return 0
@@ -202,7 +204,8 @@ def _expected_workspace(P):
 def test_workspace_size_follows_split_and_group_policy():
     from synth.workloads import sfa_mla_rope
     cases = [_small_sfa(), sfa_mla_rope(batch=32, q_s=2, kv_len=4096, topk=2048),
-             synth.make_workload("c8_packed_int8")]
+             synth.make_workload("c8_packed_int8"), sfa_mla_rope(batch=2, q_s=1, kv_len=4096,
+                                                                 topk=1100)]
     for P in cases:
         p = s.make_params(P.params, P.arrays)
         assert s.sfmla_workspace_size(p) == _expected_workspace(P), P.name
