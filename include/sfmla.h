@@ -37,6 +37,9 @@
  *     pages (约束说明: values are user-guaranteed); gathered rows are
  *     nevertheless bounds-checked against the pool sizes given here, and an
  *     out-of-range row is skipped and reported through `status`.
+ *   - Size limits of this implementation, also checked on the host: a query
+ *     row's list (as bounded by the parameters) holds at most 4096 x 2048
+ *     rows, and one query row's split partials stay below 2^31 bytes.
  *   - bf16 tensors hold IEEE bfloat16 values; fp32 is IEEE binary32.
  */
 #ifndef SFMLA_H

@@ -68,6 +68,10 @@ uint32_t fingerprint(const sfmla_params& p) {
   return h;
 }
 
+int64_t max_list(const sfmla_params& p);
+int max_splits(const sfmla_params& p);
+void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg);
+
 sfmla_status validate(const sfmla_params* pp) {
   REQUIRE(pp != nullptr, "params is NULL");
   const sfmla_params& p = *pp;
@@ -140,6 +144,19 @@ sfmla_status validate(const sfmla_params* pp) {
     REQUIRE(p.cmp_topk == 0, "cmp_topk must be 0 without cmp_kv");
     REQUIRE(p.cmp_ratio == 1, "cmp_ratio must be 1 without cmp_kv");
   }
+  // A query row's list goes in at most 4096 splits of at most kMaxSplitRows
+  // rows (the kernel's LDS row table), and one row's split partials are
+  // addressed with 32-bit offsets.
+  const int64_t n = max_list(p);
+  REQUIRE(n <= (int64_t)4096 * sfmla::kMaxSplitRows,
+          "a query row's list may hold %lld rows; at most %lld are supported", (long long)n,
+          (long long)4096 * sfmla::kMaxSplitRows);
+  int nw, groups, bpg;
+  choose_groups(p, &nw, &groups, &bpg);
+  const int64_t part_bytes = (int64_t)max_splits(p) * groups * nw * 16 * 512 * 2;
+  REQUIRE(part_bytes < ((int64_t)1 << 31),
+          "split partials of one query row would take %lld bytes (limit 2^31)",
+          (long long)part_bytes);
   return ok();
 }
 
@@ -207,7 +224,6 @@ size_t metadata_ints(const sfmla_params& p) {
 
 // Workgroups below which a launch spreads a row's heads over several groups.
 constexpr int64_t kMinGroups = 256;
-void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg);
 
 // Split partials: normalised bf16 partial O for every (row, split, padded
 // head), laid out per wave in MFMA fragment order, then the log2-domain LSEs.

@@ -231,3 +231,30 @@ def test_block_wise_topk_must_divide_the_page():
     p.ori_sparse_block_size = 32                    # does not divide the 16-token page
     with pytest.raises(s.SfmlaError, match="divide ori_block_size"):
         s.sfmla_metadata_size(p)
+
+
+def test_list_longer_than_the_row_table_allows_is_rejected():
+    # 4096 splits of at most 2048 rows per query row
+    lib = s._abi.load()
+    p = _params(ori_mask_mode=0, ori_win_left=-1, ori_win_right=-1,
+                max_seqlen_ori_kv=4096 * 2048 + 1, ori_kv_rows=4096 * 2048 + 1)
+    n = ctypes.c_size_t()
+    assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 1
+    assert b"at most 8388608" in lib.sfmla_last_error()
+    p = _params(ori_mask_mode=0, ori_win_left=-1, ori_win_right=-1,
+                max_seqlen_ori_kv=4096 * 2048, ori_kv_rows=4096 * 2048)
+    assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+
+
+def test_partials_of_one_row_beyond_32_bit_offsets_are_rejected(monkeypatch):
+    # one 16-head block per group (the tuning override) lays 128 heads out
+    # as 8 groups of 8 waves: 4096 splits x 1024 padded heads x 1 KB = 2^32
+    lib = s._abi.load()
+    monkeypatch.setenv("SFMLA_BPG", "1")
+    p = _params(num_heads_q=128, ori_mask_mode=0, ori_win_left=-1, ori_win_right=-1,
+                max_seqlen_ori_kv=4096 * 256, ori_kv_rows=4096 * 256)
+    n = ctypes.c_size_t()
+    assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 1
+    assert b"2^31" in lib.sfmla_last_error()
+    monkeypatch.delenv("SFMLA_BPG")
+    assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
