@@ -1,8 +1,8 @@
 """Throughput of shared-KV sparse flash MLA attention on one MI355X.
 
 One step is one pass of the whole path on one batch: the plan
-(sfmla_metadata), the forward kernel (resolve, gather, QK^T, online softmax,
-PV) and the split merge (sfmla_combine), all through the C ABI.  Inputs are
+(sfmla_metadata) and the forward kernel (resolve, gather, QK^T, online
+softmax, PV and the merge of the KV splits), all through the C ABI.  Inputs are
 resident in HBM before timing starts.  Between steps the TopK index set is
 rotated through several independently drawn replicas, so consecutive steps
 gather different rows and the 256 MB Infinity Cache cannot serve them.
@@ -366,7 +366,6 @@ def main():
             select(k)
             call.plan(stream)
             call.forward(stream)
-            call.combine(stream)
         settle_steps += 25
         torch.cuda.synchronize()
     settle_ms = (time.perf_counter() - t_settle) * 1e3
@@ -374,7 +373,6 @@ def main():
         select(k)
         call.plan(stream)
         call.forward(stream)
-        call.combine(stream)
     torch.cuda.synchronize()
 
     # timed region: K whole steps.  The forward kernel of every N-th step is
@@ -398,16 +396,14 @@ def main():
         if k % every == 0:
             s.sfmla_time_next_forward(ev[k // every][0], ev[k // every][1])
         call.forward(stream)
-        call.combine(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert int(call.status.item()) == 0, "device status %d" % int(call.status.item())
     fwd_ms = [a.elapsed_time(b) for a, b in ev]
 
-    # untimed: plan duration for the report.  The plan is bracketed by event
-    # records on the stream; sfmla_combine launches nothing (the forward
-    # merges split rows itself), so its bracket measures what an empty pair
-    # of event records costs, reported beside the plan's bracketed time.
+    # untimed: plan duration for the report, bracketed by event records on
+    # the stream (which include the cost of the records themselves; an empty
+    # bracket is measured beside it)
     pe = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
     for k, e in enumerate(pe):
         select(k)
@@ -416,11 +412,10 @@ def main():
         e[1].record(stream)
         call.forward(stream)
         e[2].record(stream)
-        call.combine(stream)
         e[3].record(stream)
     torch.cuda.synchronize()
     plan_ms = [e[0].elapsed_time(e[1]) for e in pe]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in pe]
+    empty_ms = [e[2].elapsed_time(e[3]) for e in pe]
 
     ms_per_step = wall * 1e3 / args.steps
     tot_flops = sum(flops_step[k % nrep] for k in range(args.steps))
@@ -472,8 +467,7 @@ def main():
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernel_ms": {"plan": round(float(np.mean(plan_ms)), 5),
                       "forward": round(float(np.mean(fwd_ms)), 5),
-                      "combine": 0.0,
-                      "empty_event_bracket": round(float(np.mean(comb_ms)), 5)},
+                      "empty_event_bracket": round(float(np.mean(empty_ms)), 5)},
         "roofline": {"kernel": "sfmla::" + kern,
                      "bound": "hbm" if hbm_bound else "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": unit,

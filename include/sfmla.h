@@ -19,9 +19,12 @@
  *
  * Call pattern (sparse_flash_mla API page, 功能说明 typical flow): build the
  * split plan with sfmla_metadata() from the same parameters, then call
- * sfmla_forward() and sfmla_combine() with that plan.  A plan built from other parameters is
- * rejected on the device (outputs become NaN and *status is set), because the
- * host never reads device memory.
+ * sfmla_forward() with that plan.  The forward merges the partial results of
+ * the KV splits it plans itself (the FLASH_DECODE split); sfmla_combine() is
+ * the same LSE merge for partial results a caller produced over disjoint
+ * parts of a row set (e.g. KV shards held by different devices).  A plan built
+ * from other parameters is rejected on the device (outputs become NaN and
+ * *status is set), because the host never reads device memory.
  *
  * Conventions for every entry point:
  *   - All pointers in sfmla_lengths / sfmla_tensors and the metadata and
@@ -139,6 +142,20 @@ typedef struct sfmla_params {
   int32_t has_seqused_ori_kv;
   int32_t has_seqused_cmp_kv;
   int32_t has_cmp_residual_kv;
+  /* Work-split overrides (0 = the library's rule, which depends on the
+   * parameters only).  They enter the plan fingerprint and the workspace
+   * size, so a plan and a workspace always match the split they were built
+   * for; nothing is read from the environment.
+   *   split_rows            list rows per KV split of a short-query row:
+   *                         0, or a multiple of 32 in 32..2048.  Changes the
+   *                         rounding order of the split merge (results stay
+   *                         within the stated tolerances).
+   *   head_blocks_per_group 16-head blocks that share one gathered KV row
+   *                         set: 0, or 1, 2, 4, 8 (at most the kernel's
+   *                         waves).  Results are bitwise the same for every
+   *                         value.                                           */
+  int32_t split_rows;
+  int32_t head_blocks_per_group;
 } sfmla_params;
 
 /*
@@ -237,31 +254,24 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* tens
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Split-KV merge step (the FLASH_DECODE split of the kv_quant_sparse_flash_attention
- * blog's kernel structure): O = sum_k e^{lse_k} O_k / (sum_k e^{lse_k} + e^{sink}),
- * LSE = log sum_k e^{lse_k}, the sink added once.  sfmla_forward() performs
- * this merge itself for every split row, so this call validates its
- * arguments like sfmla_forward() and launches nothing; it is kept so that a
- * caller's plan / forward / combine sequence stays valid.
- */
-sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* tensors,
-                           const int32_t* metadata, size_t n_ints, const void* workspace,
-                           size_t workspace_bytes, void* stream);
-
-/*
- * Generic LSE merge of partial results over disjoint parts of each row set
- * (kv_quant_sparse_flash_attention blog, usage notes: the max / sum outputs
- * serve the merge of KV-sharded (DCP) partial results).  For r in [0, rows), h in [0, heads):
+ * LSE merge of partial results over disjoint parts of each row set (the
+ * FLASH_DECODE split of the kv_quant_sparse_flash_attention blog's kernel
+ * structure; its usage notes name the max / sum outputs as what merges
+ * KV-sharded (DCP) partial results).  For r in [0, rows), h in [0, heads):
  *   part_o[(k*rows + r)*heads + h][0..dv)  fp32, part k's output normalised
  *                                           without the sink
  *   part_lse[(k*rows + r)*heads + h]        fp32, part k's LSE (-inf = empty)
  *   out  bf16 (rows, heads, dv) = sum_k e^{lse_k} O_k / (sum_k e^{lse_k} + e^{sink_h})
  *   lse_out fp32 (rows, heads) = log sum_k e^{lse_k}  (may be NULL)
- * sinks (heads) may be NULL (no sink).  dv must be a multiple of 4, <= 4096.
+ * The sink (sinks: fp32 (heads), NULL = no sink) is applied once, here.  A
+ * (row, head) whose parts are all empty gives O = 0, LSE = -inf.  part_o is
+ * 16-byte aligned, out 8-byte aligned; dv is a multiple of 4 in 4..4096,
+ * heads <= 65535.  sfmla_forward() needs no call of this: it merges the
+ * splits it plans itself.
  */
-sfmla_status sfmla_merge_partials(int32_t n_parts, int32_t rows, int32_t heads, int32_t dv,
-                                  const float* part_o, const float* part_lse, const float* sinks,
-                                  void* out, float* lse_out, void* stream);
+sfmla_status sfmla_combine(int32_t n_parts, const float* part_o, const float* part_lse,
+                           const float* sinks, void* out, float* lse_out, int32_t rows,
+                           int32_t heads, int32_t dv, void* stream);
 
 /*
  * Debug view of the resolver: writes each query row's resolved physical rows

@@ -21,7 +21,7 @@ from . import _abi
 from ._abi import KV_DTYPES, LAYOUTS, Lengths, Params, SfmlaError, Tensors
 
 __all__ = ["sfmla_metadata_size", "sfmla_metadata", "sfmla_workspace_size", "sfmla_forward",
-           "sfmla_combine", "sfmla_merge_partials", "sfmla_debug_resolve", "sfmla_time_next_forward",
+           "sfmla_combine", "sfmla_debug_resolve", "sfmla_time_next_forward",
            "sfmla_version", "Params", "Lengths",
            "Tensors", "SfmlaError", "Call", "make_params", "CMP_BIT"]
 
@@ -42,6 +42,32 @@ def _stream(stream):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtype, shape=None):
+    """A tensor handed to the library as a bare pointer: contiguous, of the
+    given dtype (and shape).  None passes (an absent optional tensor)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise SfmlaError(1, "%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise SfmlaError(1, "%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise SfmlaError(1, "%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _require_rows(t, name, dtypes):
+    """A KV pool: 2-D (physical rows, row elements), each row contiguous;
+    consecutive rows may be further apart (row stride >= row, padding
+    allowed, a multiple of 16 bytes)."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise SfmlaError(1, "%s must be one of %s (got %s)" % (name, dtypes, t.dtype))
+    if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+        raise SfmlaError(1, "%s must be 2-D with contiguous rows (stride(1) == 1, "
+                            "stride(0) >= row width)" % name)
 
 
 def sfmla_version() -> str:
@@ -73,20 +99,19 @@ def sfmla_forward(params: Params, tensors: Tensors, metadata: torch.Tensor, soft
                                     _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def sfmla_combine(params: Params, tensors: Tensors, metadata: torch.Tensor,
-                  workspace: torch.Tensor | None = None, stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _abi.check(_lib().sfmla_combine(ctypes.byref(params), ctypes.byref(tensors), _ptr(metadata),
-                                    metadata.numel(), _ptr(workspace), ws_bytes, _stream(stream)))
-
-
-def sfmla_merge_partials(part_o: torch.Tensor, part_lse: torch.Tensor, sinks, out: torch.Tensor,
-                         lse_out=None, stream=None):
-    """part_o fp32 (n_parts, rows, heads, dv), part_lse fp32 (n_parts, rows, heads)."""
+def sfmla_combine(part_o: torch.Tensor, part_lse: torch.Tensor, sinks, out: torch.Tensor,
+                  lse_out=None, stream=None):
+    """LSE merge of caller-supplied partials: part_o fp32 (n_parts, rows, heads,
+    dv), part_lse fp32 (n_parts, rows, heads), sinks fp32 (heads) or None,
+    out bf16 (rows, heads, dv), lse_out fp32 (rows, heads) or None."""
     n_parts, rows, heads, dv = part_o.shape
-    _abi.check(_lib().sfmla_merge_partials(n_parts, rows, heads, dv, _ptr(part_o),
-                                           _ptr(part_lse), _ptr(sinks), _ptr(out),
-                                           _ptr(lse_out), _stream(stream)))
+    _require(part_o, "part_o", torch.float32, (n_parts, rows, heads, dv))
+    _require(part_lse, "part_lse", torch.float32, (n_parts, rows, heads))
+    _require(sinks, "sinks", torch.float32, (heads,))
+    _require(out, "out", torch.bfloat16, (rows, heads, dv))
+    _require(lse_out, "lse_out", torch.float32, (rows, heads))
+    _abi.check(_lib().sfmla_combine(n_parts, _ptr(part_o), _ptr(part_lse), _ptr(sinks),
+                                    _ptr(out), _ptr(lse_out), rows, heads, dv, _stream(stream)))
 
 
 def sfmla_debug_resolve(params: Params, tensors: Tensors, metadata: torch.Tensor,
@@ -155,6 +180,8 @@ def make_params(spec: dict, arrays: dict) -> Params:
     p.has_seqused_ori_kv = int(arrays.get("seqused_ori_kv") is not None)
     p.has_seqused_cmp_kv = int(arrays.get("seqused_cmp_kv") is not None)
     p.has_cmp_residual_kv = int(arrays.get("cmp_residual_kv") is not None)
+    p.split_rows = int(g("split_rows", 0))
+    p.head_blocks_per_group = int(g("head_blocks_per_group", 0))
     return p
 
 
@@ -201,8 +228,31 @@ class Call:
                           if ws else None)
         self.tensors = self._tensors()
 
+    def _check(self):
+        """dtype and layout of every tensor the library reads through a bare
+        pointer: q, index lists, block tables, length tensors and sinks
+        contiguous with their pages' dtypes; KV pools with contiguous rows."""
+        d = self.d
+        half = torch.float16 if self.spec.get("kv_dtype") == "fp16" else torch.bfloat16
+        for name in ("q",):
+            if d[name].dtype not in (half, torch.int16):
+                raise SfmlaError(1, "q must be %s (or its int16 bits)" % half)
+            if not d[name].is_contiguous():
+                raise SfmlaError(1, "q must be contiguous")
+        for name in ("ori_block_table", "cmp_block_table", "ori_sparse_indices",
+                     "cmp_sparse_indices") + tuple(n for n, _ in Lengths._fields_):
+            _require(d.get(name), name, torch.int32)
+        _require(d.get("sinks"), "sinks", torch.float32)
+        packed = self.spec.get("kv_dtype") in ("int8_packed", "fp8_e4m3_packed")
+        kv_types = (torch.uint8,) if packed else (half, torch.int16)
+        for name in ("ori_kv", "cmp_kv"):
+            _require_rows(d.get(name), name, kv_types)
+        for name in ("ori_v", "ori_rope", "cmp_rope"):
+            _require_rows(d.get(name), name, (half, torch.int16))
+
     def _tensors(self) -> Tensors:
         d = self.d
+        self._check()
         t = Tensors()
 
         def row_bytes(x):
@@ -220,6 +270,9 @@ class Call:
         if d.get("cmp_kv") is not None:
             t.cmp_kv = d["cmp_kv"].data_ptr()
             t.cmp_kv_stride = row_bytes(d["cmp_kv"])
+        if d.get("cmp_rope") is not None:
+            t.cmp_rope = d["cmp_rope"].data_ptr()
+            t.cmp_rope_stride = row_bytes(d["cmp_rope"])
         for name in ("ori_block_table", "cmp_block_table", "ori_sparse_indices",
                      "cmp_sparse_indices", "sinks"):
             if d.get(name) is not None:
@@ -235,14 +288,11 @@ class Call:
     def forward(self, stream=None):
         sfmla_forward(self.params, self.tensors, self.metadata, self.scale, self.workspace, stream)
 
-    def combine(self, stream=None):
-        sfmla_combine(self.params, self.tensors, self.metadata, self.workspace, stream)
-
     def run(self, stream=None):
-        """One pass of the whole path: plan, forward, split merge."""
+        """One pass of the whole path: plan, then the forward (which merges
+        the KV splits it plans)."""
         self.plan(stream)
         self.forward(stream)
-        self.combine(stream)
         return self.out, self.lse
 
     def resolve(self, max_rows, stream=None):

@@ -41,7 +41,8 @@ class Params(ctypes.Structure):
         ("kv_dtype", _i32), ("has_separate_v", _i32), ("has_sinks", _i32),
         ("return_softmax_lse", _i32), ("has_seqused_q", _i32),
         ("has_seqused_ori_kv", _i32), ("has_seqused_cmp_kv", _i32),
-        ("has_cmp_residual_kv", _i32),
+        ("has_cmp_residual_kv", _i32), ("split_rows", _i32),
+        ("head_blocks_per_group", _i32),
     ]
 
 
@@ -66,7 +67,7 @@ class Tensors(ctypes.Structure):
 
 
 SYMBOLS = ("sfmla_metadata_size", "sfmla_metadata", "sfmla_workspace_size",
-           "sfmla_forward", "sfmla_combine", "sfmla_merge_partials", "sfmla_debug_resolve",
+           "sfmla_forward", "sfmla_combine", "sfmla_debug_resolve",
            "sfmla_time_next_forward", "sfmla_last_error", "sfmla_version")
 
 _lib = None
@@ -87,11 +88,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfmla_metadata.argtypes = [P(Params), P(Lengths), _vp, sz, _vp]
     lib.sfmla_workspace_size.argtypes = [P(Params), P(sz)]
     lib.sfmla_forward.argtypes = [P(Params), P(Tensors), _vp, sz, ctypes.c_float, _vp, sz, _vp]
-    lib.sfmla_combine.argtypes = [P(Params), P(Tensors), _vp, sz, _vp, sz, _vp]
-    lib.sfmla_merge_partials.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.sfmla_combine.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
     lib.sfmla_debug_resolve.argtypes = [P(Params), P(Tensors), _vp, sz, _vp, _i32, _vp, _vp]
     lib.sfmla_time_next_forward.argtypes = [_vp, _vp]
-    for name in SYMBOLS[:8]:
+    for name in SYMBOLS[:7]:
         getattr(lib, name).restype = ctypes.c_int
     lib.sfmla_last_error.restype = ctypes.c_char_p
     lib.sfmla_last_error.argtypes = []

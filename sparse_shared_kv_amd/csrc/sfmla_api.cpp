@@ -61,7 +61,8 @@ uint32_t fingerprint(const sfmla_params& p) {
       p.ori_mask_mode,
       p.cmp_mask_mode, p.ori_win_left, p.ori_win_right, p.has_ori_kv, p.has_cmp_kv,
       p.kv_dtype, p.has_separate_v, p.has_sinks, p.return_softmax_lse, p.has_seqused_q,
-      p.has_seqused_ori_kv, p.has_seqused_cmp_kv, p.has_cmp_residual_kv};
+      p.has_seqused_ori_kv, p.has_seqused_cmp_kv, p.has_cmp_residual_kv, p.split_rows,
+      p.head_blocks_per_group};
   for (int32_t v : f32) mix(v);
   mix(p.ori_kv_rows);
   mix(p.cmp_kv_rows);
@@ -118,6 +119,15 @@ sfmla_status validate(const sfmla_params* pp) {
               p.kv_dtype == SFMLA_KV_INT8_PACKED ||
               p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED,
           "unknown kv_dtype");
+  REQUIRE(p.split_rows == 0 ||
+              (p.split_rows >= sfmla::kTile && p.split_rows <= sfmla::kMaxSplitRows &&
+               p.split_rows % sfmla::kTile == 0),
+          "split_rows must be 0 or a multiple of %d in %d..%d", sfmla::kTile, sfmla::kTile,
+          sfmla::kMaxSplitRows);
+  REQUIRE(p.head_blocks_per_group == 0 || p.head_blocks_per_group == 1 ||
+              p.head_blocks_per_group == 2 || p.head_blocks_per_group == 4 ||
+              p.head_blocks_per_group == 8,
+          "head_blocks_per_group must be 0, 1, 2, 4 or 8");
   REQUIRE(!(p.has_separate_v && p.kv_dtype != SFMLA_KV_BF16 && p.kv_dtype != SFMLA_KV_FP16),
           "a separate V is only supported for bf16 KV (packed V is the dequantised nope)");
   if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.ori_kv_s > 0, "BSND ori_kv needs ori_kv_s > 0");
@@ -182,13 +192,9 @@ int64_t max_list(const sfmla_params& p) {
 // the number of partials to merge low; lighter rows (1 KB bf16 rows with
 // V = K, packed rows) get 256-row splits, which keep each workgroup's serial
 // chain of tiles short (measured on the six workloads of the benchmark).
-// SFMLA_SPLIT_ROWS (a multiple of 32 up to kMaxSplitRows) overrides it
-// (tuning aid).
+// params.split_rows, when nonzero, overrides the rule.
 int split_rows(const sfmla_params& p) {
-  if (const char* env = getenv("SFMLA_SPLIT_ROWS")) {
-    const int v = atoi(env);
-    if (v >= sfmla::kTile && v <= sfmla::kMaxSplitRows && v % sfmla::kTile == 0) return v;
-  }
+  if (p.split_rows) return p.split_rows;
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int row_bytes = packed ? 512 + 2 * p.rope_head_dim + 16
                                : 2 * (512 + p.rope_head_dim) + (p.has_separate_v ? 1024 : 0);
@@ -261,14 +267,11 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int wmax = packed ? 4 : 8;                     // packed rows: more registers per wave
   *nw = wmax;
-  // SFMLA_BPG=<blocks per group> overrides the split of the heads (tuning aid)
-  if (const char* env = getenv("SFMLA_BPG")) {
-    const int b = atoi(env);
-    if (b == 1 || b == 2 || b == 4 || b == 8) {
-      *bpg = std::min(b, wmax);
-      *groups = (blocks + *bpg - 1) / *bpg;
-      return;
-    }
+  // params.head_blocks_per_group, when nonzero, overrides the rule
+  if (p.head_blocks_per_group) {
+    *bpg = std::min(p.head_blocks_per_group, wmax);
+    *groups = (blocks + *bpg - 1) / *bpg;
+    return;
   }
   int per = 1;                                         // blocks per group: 1, 2, 4 or 8
   while (per < wmax && per < blocks) per *= 2;
@@ -491,32 +494,16 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
   return ok();
 }
 
-sfmla_status sfmla_combine(const sfmla_params* params, const sfmla_tensors* t,
-                           const int32_t* metadata, size_t n_ints, const void* workspace,
-                           size_t ws_bytes, void* stream) {
-  sfmla_status s = validate(params);
-  if (s != SFMLA_OK) return s;
-  const sfmla_params& p = *params;
-  sfmla::FwdArgs a;
-  s = fill_fwd_args(p, t, metadata, n_ints, 1.0f, &a);
-  if (s != SFMLA_OK) return s;
-  // the forward kernel merges split rows itself (the last split of a row to
-  // finish merges them), so there is nothing left to launch
-  (void)workspace;
-  (void)ws_bytes;
-  (void)stream;
-  return ok();
-}
-
-sfmla_status sfmla_merge_partials(int32_t n_parts, int32_t rows, int32_t heads, int32_t dv,
-                                  const float* part_o, const float* part_lse, const float* sinks,
-                                  void* out, float* lse_out, void* stream) {
+sfmla_status sfmla_combine(int32_t n_parts, const float* part_o, const float* part_lse,
+                           const float* sinks, void* out, float* lse_out, int32_t rows,
+                           int32_t heads, int32_t dv, void* stream) {
   REQUIRE(n_parts >= 1, "n_parts must be >= 1");
   REQUIRE(rows >= 1 && heads >= 1, "rows and heads must be >= 1");
   REQUIRE(dv >= 4 && dv <= 4096 && dv % 4 == 0, "dv must be a multiple of 4 in 4..4096");
   REQUIRE(part_o && aligned16(part_o) && part_lse, "part_o (16-byte aligned) and part_lse are required");
   REQUIRE(out && ((uintptr_t)out & 7) == 0, "out must be an 8-byte aligned device pointer");
   REQUIRE(heads <= 65535, "heads must be <= 65535");
+  REQUIRE((int64_t)n_parts * rows * heads * dv < ((int64_t)1 << 40), "partials too large");
   sfmla::CombineArgs c;
   std::memset(&c, 0, sizeof c);
   c.rows = rows;

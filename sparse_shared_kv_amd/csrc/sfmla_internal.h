@@ -85,8 +85,7 @@ struct FwdArgs {
 
 struct CombineArgs {
   int32_t rows, heads, dv;
-  int32_t n_parts;                  // fixed part count (exported merge) or 0
-  const int32_t* meta;              // per-row split counts (internal merge)
+  int32_t n_parts;
   int64_t o_part_stride, o_row_stride;      // in floats
   int64_t lse_part_stride, lse_row_stride;  // in floats
   const float* part_o;

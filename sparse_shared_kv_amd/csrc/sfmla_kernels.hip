@@ -10,7 +10,8 @@
 //                      online softmax, O^T += V^T P^T on bf16 MFMA, then the
 //                      final output, or a partial that the last split of the
 //                      row to finish merges.
-//   combine_kernel     generic LSE merge of fp32 partials, sink applied once.
+//   combine_kernel     LSE merge of caller-supplied fp32 partials (sfmla_combine),
+//                      sink applied once.
 //   resolve_kernel     debug dump of the resolved rows in canonical order.
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l holds A[m = l%16][k = 8(l/16)+i],
@@ -352,28 +353,31 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One global_load_lds_dwordx4: every lane moves 16 bytes from `g` to LDS at
-// lds_wave_base + 16 * lane.  Issued through inline asm so that the
-// compiler's wait insertion neither tracks these loads (it cannot tell the
-// in-flight stage apart from the stage being read and would wait for all of
-// them) nor reorders LDS reads across them ("memory" clobber).  Every wait on
-// this data is explicit (wait_vmcnt + block_barrier).  Untracked vector-memory
-// ops only make the compiler's own in-order vmcnt waits stricter, never
-// insufficient.
+// lds_wave_base + 16 * lane (the LDS base is taken from M0).  Issued through
+// inline asm so that the compiler's wait insertion neither tracks these loads
+// (it cannot tell the in-flight stage apart from the stage being read and
+// would wait for all of them) nor reorders LDS reads across them ("memory"
+// clobber).  Every wait on this data is explicit (wait_vmcnt +
+// block_barrier).  Untracked vector-memory ops only make the compiler's own
+// in-order vmcnt waits stricter, never insufficient.  M0 is an input operand
+// ("{m0}"): the compiler writes it and knows its value is read here, so no
+// register it holds is clobbered behind its back; s_nop 0 gives the one wait
+// state an LDS DMA needs after an M0 write.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
+               : "v"(g), "{m0}"(lds_addr)
+               : "memory");
 }
 
 // The same with a uniform row address in an SGPR pair (lane offset in a
 // VGPR).  s_nop 4 gives the five wait states a VMEM instruction needs after a
 // VALU write (v_readlane) of an SGPR it reads, which also covers the M0 write.
 __device__ __forceinline__ void dma16_s(uint64_t base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(base), "s"(lds_addr)
-               : "memory", "m0");
+               : "v"(voff), "s"(base), "{m0}"(lds_addr)
+               : "memory");
 }
 
 // 64-bit value held by lane j, as a uniform (SGPR) value.
@@ -1246,23 +1250,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int row = blockIdx.x, h = blockIdx.y;
-  int np = a.n_parts;
-  if (a.meta) {
-    const int32_t* rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
-    np = rec[R_NSPLIT];
-    if (np <= 1) return;   // written directly by the forward
-  }
+  const int np = a.n_parts;
   const float* lp = a.part_lse + row * a.lse_row_stride + h;
+  // Weights are taken relative to the largest part LSE only, so the sum of
+  // the parts' weights is >= 1 whenever a part is non-empty and the merged
+  // LSE stays finite however far the sink lies above it; the sink enters the
+  // denominator alone (a sink far above every part drives O to 0).
   float m = kNegInf;
   for (int k = 0; k < np; ++k) m = fmaxf(m, lp[k * a.lse_part_stride]);
-  float mm = m;
-  const bool sink = a.sinks != nullptr;
-  const float sig = sink ? a.sinks[h] : kNegInf;
-  if (sink) mm = fmaxf(mm, sig);
-  const float ref = mm == kNegInf ? 0.f : mm;
+  const float ref = m == kNegInf ? 0.f : m;
   float tot = 0.f;
   for (int k = 0; k < np; ++k) tot += expf(lp[k * a.lse_part_stride] - ref);
-  const float den = tot + (sink ? expf(sig - ref) : 0.f);
+  const float den = tot + (a.sinks ? expf(a.sinks[h] - ref) : 0.f);
   const float inv = tot > 0.f ? 1.f / den : 0.f;
   const float* op = a.part_o + row * a.o_row_stride + (int64_t)h * a.dv;
   uint16_t* out = a.out + ((int64_t)row * a.heads + h) * a.dv;

@@ -389,7 +389,7 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
                 cmp_ratio=None, sinks=None, dist="normal", topk=None,
                 separate_v=None, q_lens=None, ori_lens=None,
                 seqused_q=None, duplicates=False, win=None, masks=None,
-                sparse_block_size=1):
+                sparse_block_size=1, lse=None):
     """A small random problem.
 
     family: "swa" (ori window only), "csa" (window + TopK compressed rows),
@@ -399,10 +399,12 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
     the SparseAttnSharedKV example's draws (q ~ U(-10,10), kv ~ U(-5,10),
     sinks ~ U(0,1)), which give very peaked softmaxes.  sparse_block_size
     (sfa only) > 1 makes each TopK entry select that many consecutive tokens;
-    paged block sizes are then multiples of it.
+    paged block sizes are then multiples of it.  lse: whether the LSE output
+    is asked for (drawn, one case in three without, when not given).
     """
     ss = np.random.SeedSequence(seed)
     s_cfg, s_q, s_ori, s_v, s_cmp, s_idx, s_tab, s_sink = ss.spawn(8)
+    (s_lse,) = ss.spawn(1)
     g = _gen(s_cfg)
     family = family or g.choice(["swa", "csa", "hca", "sfa"])
     B = batch or int(g.integers(1, 4))
@@ -472,7 +474,8 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
         cmp_ratio=r, ori_mask_mode=masks[0], cmp_mask_mode=masks[1],
         ori_win_left=win[0], ori_win_right=win[1], has_cmp_kv=has_cmp,
         kv_dtype=kv_dtype, separate_v=separate_v,
-        softmax_scale=(1.0 / 24.0) if dist == "p4" else 1.0 / math.sqrt(d_qk))
+        softmax_scale=(1.0 / 24.0) if dist == "p4" else 1.0 / math.sqrt(d_qk),
+        return_softmax_lse=bool(lse) if lse is not None else bool(_gen(s_lse).integers(0, 3)))
     if layout_q == "TND":
         arrays["cu_seqlens_q"] = _prefix(q_lens)
     elif use_seqused_q:

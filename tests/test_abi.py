@@ -23,8 +23,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for need in ("sfmla_metadata", "sfmla_forward", "sfmla_combine", "sfmla_merge_partials",
-                 "sfmla_metadata_size",
+    for need in ("sfmla_metadata", "sfmla_forward", "sfmla_combine", "sfmla_metadata_size",
                  "sfmla_workspace_size", "sfmla_debug_resolve", "sfmla_last_error",
                  "sfmla_version"):
         assert need in names
@@ -218,9 +217,63 @@ def _small_sfa():
 
 def test_combine_rejects_bad_dv():
     lib = s._abi.load()
-    st = lib.sfmla_merge_partials(2, 4, 8, 6, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
-                           ctypes.c_void_p(4096), None, None)
+    st = lib.sfmla_combine(2, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
+                           ctypes.c_void_p(4096), None, 4, 8, 6, None)
     assert st == 1 and b"dv" in lib.sfmla_last_error()
+
+
+def test_work_split_overrides_are_validated_and_fingerprinted():
+    """split_rows / head_blocks_per_group come from the parameters (never the
+    environment): out-of-range values are refused, and a different value
+    changes the workspace the library asks for."""
+    P = _small_sfa()
+    p = s.make_params(P.params, P.arrays)
+    base = s.sfmla_workspace_size(p)
+    for field, bad in (("split_rows", 48), ("split_rows", 4096), ("head_blocks_per_group", 3)):
+        q = s.make_params(P.params, P.arrays)
+        setattr(q, field, bad)
+        with pytest.raises(s.SfmlaError, match=field):
+            s.sfmla_workspace_size(q)
+    q = s.make_params(dict(P.params, split_rows=256), P.arrays)
+    assert s.sfmla_workspace_size(q) == 2 * base          # 2048 rows: 8 splits instead of 4
+    q = s.make_params(dict(P.params, head_blocks_per_group=8), P.arrays)
+    assert s.sfmla_workspace_size(q) < base               # one group: no padding per group
+
+
+def test_environment_does_not_change_the_split(monkeypatch):
+    P = _small_sfa()
+    p = s.make_params(P.params, P.arrays)
+    base = s.sfmla_workspace_size(p)
+    monkeypatch.setenv("SFMLA_SPLIT_ROWS", "64")
+    monkeypatch.setenv("SFMLA_BPG", "1")
+    assert s.sfmla_workspace_size(p) == base
+
+
+def test_binding_rejects_wrong_dtypes_and_layouts():
+    """The binding hands q, index lists, tables and sinks over as bare
+    pointers: a transposed view or a wrong dtype is refused instead of being
+    read with the wrong layout."""
+    import torch
+    P = synth.random_tiny(31, family="sfa", layout_q="TND", layout_kv="PA_BSND", num_heads_q=4,
+                          sinks=True)
+    bad = dict(P.arrays)
+    bad["ori_sparse_indices"] = P.arrays["ori_sparse_indices"].astype(np.int64)
+    with pytest.raises(s.SfmlaError, match="ori_sparse_indices"):
+        s.Call(P.params, bad, device="cpu")
+    bad = dict(P.arrays)
+    bad["sinks"] = P.arrays["sinks"].astype(np.float64)
+    with pytest.raises(s.SfmlaError, match="sinks"):
+        s.Call(P.params, bad, device="cpu")
+    bad = dict(P.arrays)
+    q = torch.from_numpy(P.arrays["q"].view(np.int16))
+    bad["q"] = q.transpose(0, 1).contiguous().transpose(0, 1)     # same shape, not contiguous
+    with pytest.raises(s.SfmlaError, match="q must be contiguous"):
+        s.Call(P.params, bad, device="cpu")
+    bad = dict(P.arrays)
+    kv = torch.from_numpy(P.arrays["ori_kv"].view(np.int16))
+    bad["ori_kv"] = kv.t().contiguous().t()                       # rows not contiguous
+    with pytest.raises(s.SfmlaError, match="ori_kv"):
+        s.Call(P.params, bad, device="cpu")
 
 
 def test_block_wise_topk_must_divide_the_page():
@@ -246,15 +299,14 @@ def test_list_longer_than_the_row_table_allows_is_rejected():
     assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
 
 
-def test_partials_of_one_row_beyond_32_bit_offsets_are_rejected(monkeypatch):
-    # one 16-head block per group (the tuning override) lays 128 heads out
-    # as 8 groups of 8 waves: 4096 splits x 1024 padded heads x 1 KB = 2^32
+def test_partials_of_one_row_beyond_32_bit_offsets_are_rejected():
+    # one 16-head block per group (the override) lays 128 heads out as 8
+    # groups of 8 waves: 4096 splits x 1024 padded heads x 1 KB = 2^32
     lib = s._abi.load()
-    monkeypatch.setenv("SFMLA_BPG", "1")
     p = _params(num_heads_q=128, ori_mask_mode=0, ori_win_left=-1, ori_win_right=-1,
-                max_seqlen_ori_kv=4096 * 256, ori_kv_rows=4096 * 256)
+                max_seqlen_ori_kv=4096 * 256, ori_kv_rows=4096 * 256, head_blocks_per_group=1)
     n = ctypes.c_size_t()
     assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 1
     assert b"2^31" in lib.sfmla_last_error()
-    monkeypatch.delenv("SFMLA_BPG")
+    p.head_blocks_per_group = 0
     assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0

@@ -33,28 +33,19 @@ FULL = ["swa_decode", "csa_decode_paged", "hca_varlen", "sfa_mla_rope", "c8_pack
         "c8_packed_fp8", "csa_prefill", "sfa_mla_rope_fp16", "sfa_mla_rope_block16",
         "c8_packed_int8_q32", "hca_varlen_q32", "hca_prefill", "swa_prefill", "swa_prefill_h16",
         "c8_packed_int8_rope0"]
-# query rows the oracle recomputes at full size (all rows for the others)
-SAMPLE = {"sfa_mla_rope": [0, 1, 2, 17, 30, 31, 45, 62, 63],
-          "sfa_mla_rope_fp16": [0, 5, 33, 63], "sfa_mla_rope_block16": [0, 7, 40, 63],
-          "csa_prefill": [0, 1, 63, 127, 128, 300, 383, 511],
-          "c8_packed_int8_q32": [0, 31, 32, 100, 223, 255],
-          "hca_varlen_q32": [0, 1, 31, 64, 150, 255],
-          "hca_prefill": [0, 1, 2, 127, 128, 300, 383, 511],
-          "swa_prefill": [0, 1, 2, 127, 128, 300, 383, 511],
-          "swa_prefill_h16": [0, 7, 8, 127, 128, 300, 383, 511]}
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_config_parity(name):
+    """Every query row of the workload, at the size the benchmark times."""
     say("[parity] building", name)
     P = synth.make_workload(name)
-    rows = SAMPLE.get(name)
     say("[parity] gpu run", name)
     res = run_gpu(P)
-    say("[parity] oracle", name, "rows", "all" if rows is None else rows)
-    ref = oracle.forward(P, rows=rows)
-    n = check_lists(P, res["call"], ref, rows)
-    err = check_outputs(P, res, ref, rows)
+    say("[parity] oracle", name, "all", P.query_rows, "rows")
+    ref = oracle.forward(P)
+    n = check_lists(P, res["call"], ref)
+    err = check_outputs(P, res, ref)
     say("[parity] %s ok: %d resolved rows bit-exact, max |dO| %.3g" % (name, n, err))
 
 
@@ -140,7 +131,7 @@ def test_no_valid_query_rows():
 
 def test_deterministic_bitwise():
     import sparse_shared_kv_amd as s
-    P = synth.random_tiny(502, family="sfa", max_kv=3000, topk=1100, num_heads_q=128)
+    P = synth.random_tiny(502, family="sfa", max_kv=3000, topk=1100, num_heads_q=128, lse=True)
     call = s.Call(P.params, P.arrays)
     a = [t.clone() for t in call.run()]
     b = [t.clone() for t in call.run()]
@@ -149,18 +140,18 @@ def test_deterministic_bitwise():
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "int8_packed"])
-def test_head_grouping_invariance_bitwise(fmt, monkeypatch):
+def test_head_grouping_invariance_bitwise(fmt):
     """Spreading a row's heads over 1, 2, 4 or 8 head groups (the rest of the
     workgroup's waves only gathering) leaves every output bit unchanged."""
     import sparse_shared_kv_amd as s
-    kw = dict(family="sfa", max_kv=2500, topk=1100, num_heads_q=128)
+    kw = dict(family="sfa", max_kv=2500, topk=1100, num_heads_q=128, lse=True)
     if fmt != "bf16":
         kw.update(kv_dtype=fmt, rope_head_dim=64)
     P = synth.random_tiny(503, **kw)
     outs, status = [], 0
-    for bpg in ("1", "2", "4", "8"):
-        monkeypatch.setenv("SFMLA_BPG", bpg)
-        call = s.Call(P.params, P.arrays)            # workspace sized for this grouping
+    for bpg in (1, 2, 4, 8):
+        # plan and workspace sized for this grouping
+        call = s.Call(dict(P.params, head_blocks_per_group=bpg), P.arrays)
         outs.append([None if t is None else t.clone() for t in call.run()])
         torch.cuda.synchronize()
         status |= int(call.status.item())
@@ -173,9 +164,9 @@ def test_head_grouping_invariance_bitwise(fmt, monkeypatch):
     check_outputs(P, res, ref, [0, 1])
 
 
-@pytest.mark.parametrize("split_rows", ["32", "1024", "2048"])
+@pytest.mark.parametrize("split_rows", [32, 1024, 2048])
 @pytest.mark.parametrize("fmt", ["bf16", "int8_packed"])
-def test_split_sizes_match_oracle(fmt, split_rows, monkeypatch):
+def test_split_sizes_match_oracle(fmt, split_rows):
     """Lists cut into 32-row splits (many partials to merge) or held whole in
     one workgroup's row table (up to 2048 rows) give the oracle's result."""
     import sparse_shared_kv_amd as s
@@ -183,8 +174,7 @@ def test_split_sizes_match_oracle(fmt, split_rows, monkeypatch):
     if fmt != "bf16":
         kw.update(kv_dtype=fmt, rope_head_dim=64)
     P = synth.random_tiny(507, **kw)
-    monkeypatch.setenv("SFMLA_SPLIT_ROWS", split_rows)
-    call = s.Call(P.params, P.arrays)
+    call = s.Call(dict(P.params, split_rows=split_rows), P.arrays)
     out = [None if t is None else t.clone() for t in call.run()]
     torch.cuda.synchronize()
     rows = [0, 1, P.params["q_t"] - 1] if "q_t" in P.params else [0, 1]
@@ -269,13 +259,16 @@ def test_metadata_from_other_params_is_rejected():
     call.metadata.copy_(call_b.metadata)       # plan of different parameters
     call.status.zero_()
     call.forward()
-    call.combine()
     torch.cuda.synchronize()
     assert torch.isnan(call.out.float()).all()
     assert int(call.status.item()) & 1
 
 
-def test_merge_partials_entry_point_matches_oracle_merge():
+@pytest.mark.parametrize("far_sink", [False, True])
+def test_combine_entry_point_matches_oracle_merge(far_sink):
+    """sfmla_combine (the LSE merge of caller-supplied partials) against the
+    oracle's merge; far_sink puts every head's sink 200 above its largest
+    part LSE, where O goes to 0 and the LSE must stay finite."""
     import sparse_shared_kv_amd as s
     g = np.random.default_rng(3)
     n_parts, rows, heads, dv = 5, 7, 12, 512
@@ -284,11 +277,14 @@ def test_merge_partials_entry_point_matches_oracle_merge():
     part_lse[1, 2, :] = -np.inf                    # an empty part
     part_lse[:, 4, 3] = -np.inf                    # a fully empty (row, head)
     sinks = g.standard_normal(heads).astype(np.float32)
+    if far_sink:
+        top = np.where(np.isfinite(part_lse), part_lse, -np.inf).max(axis=(0, 1))
+        sinks = (top + 200.0).astype(np.float32)
     dev = torch.device("cuda")
     out = torch.empty((rows, heads, dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((rows, heads), dtype=torch.float32, device=dev)
-    s.sfmla_merge_partials(torch.from_numpy(part_o).to(dev), torch.from_numpy(part_lse).to(dev),
-                           torch.from_numpy(sinks).to(dev), out, lse)
+    s.sfmla_combine(torch.from_numpy(part_o).to(dev), torch.from_numpy(part_lse).to(dev),
+                    torch.from_numpy(sinks).to(dev), out, lse)
     torch.cuda.synchronize()
     for r in range(rows):
         O, L = oracle.combine(part_o[:, r], part_lse[:, r], sinks)
@@ -308,7 +304,7 @@ def test_rope_free_rows_equal_zero_rope_rows_bitwise(fmt):
     import copy
     import sparse_shared_kv_amd as s
     P = synth.random_tiny(601, family="sfa", kv_dtype=fmt, rope_head_dim=64, num_heads_q=64,
-                          max_kv=700, topk=600)
+                          max_kv=700, topk=600, lse=True)
     P656 = copy.deepcopy(P)
     P656.arrays["ori_kv"] = P656.arrays["ori_kv"].copy()
     P656.arrays["ori_kv"][:, 512:640] = 0                      # zero rope
@@ -340,7 +336,8 @@ def test_graph_replay_matches_eager(kw):
     eager result bit for bit (split rows merged in the launch: the arrival
     counters must come back to zero on every replay)."""
     import sparse_shared_kv_amd as s
-    P = synth.random_tiny(602, family="sfa", max_kv=3000, topk=1500, num_heads_q=128, **kw)
+    P = synth.random_tiny(602, family="sfa", max_kv=3000, topk=1500, num_heads_q=128, lse=True,
+                          **kw)
     other = synth.random_tiny(603, family="csa", num_heads_q=64, max_kv=900)
     call = s.Call(P.params, P.arrays)
     eager = [t.clone() for t in call.run() if t is not None]
@@ -384,7 +381,6 @@ def test_timing_hook_stamps_the_forward_kernel():
     call.plan()
     s.sfmla_time_next_forward(e0, e1)
     call.forward()
-    call.combine()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     assert 0.0 < ms < 100.0
@@ -409,3 +405,106 @@ def test_topk_rows_long_and_short_sequences_partial_head_block(separate_v):
     rows = [0, 35, 69, 70, 72]
     res = run_gpu(P)
     check_outputs(P, res, oracle.forward(P, rows=rows), rows)
+
+
+# ---------------------------------------------------------------------------
+# tensor layouts the boundary accepts: rope stored apart, padded rows
+# ---------------------------------------------------------------------------
+
+def _strided(rows_np, width, pad, dev, fill):
+    """Device view (rows, width) of a buffer whose rows are width + pad
+    elements long; the padding holds `fill` (a NaN pattern for 16-bit
+    floats) so that a read of it shows in the output."""
+    dt = torch.uint8 if rows_np.dtype == np.uint8 else torch.int16
+    src = torch.from_numpy(np.ascontiguousarray(rows_np[:, :width]).view(
+        np.uint8 if rows_np.dtype == np.uint8 else np.int16))
+    buf = torch.full((rows_np.shape[0], width + pad), fill, dtype=dt, device=dev)
+    buf[:, :width] = src.to(dev)
+    return buf[:, :width]
+
+
+def _relayout(P, split_rope, pad):
+    """Device arrays of P with the KV rows relaid: the 64 rope values in a
+    tensor of their own (SparseFlashAttention page, 参数说明 key_rope:
+    the rope part passed apart from the nope part) and / or every row
+    stride padded (sparse_flash_mla API page, 约束说明: ori_kv and cmp_kv
+    may have padding between rows).  The oracle keeps reading P itself."""
+    dev = torch.device("cuda")
+    packed = P.params["kv_dtype"] not in ("bf16", "fp16")
+    nan16, junk8 = -1, 255                          # 0xFFFF: NaN in bf16 and float16
+    arrays = dict(P.arrays)
+    rope = P.params["rope_head_dim"]
+    for side, pk, pr in (("ori", 8, 8), ("cmp", 24, 0)):
+        a = P.arrays.get(side + "_kv")
+        if a is None:
+            continue
+        if packed:
+            arrays[side + "_kv"] = _strided(a, a.shape[1], 16 * (pad // 8), dev, junk8)
+        elif split_rope and rope:
+            arrays[side + "_kv"] = _strided(a, 512, pk if pad else 0, dev, nan16)
+            arrays[side + "_rope"] = _strided(a[:, 512:], 64, pr if pad else 0, dev, nan16)
+        else:
+            arrays[side + "_kv"] = _strided(a, a.shape[1], pk if pad else 0, dev, nan16)
+    if P.arrays.get("ori_v") is not None:
+        arrays["ori_v"] = _strided(P.arrays["ori_v"], 512, 512 if pad else 0, dev, nan16)
+    return arrays
+
+
+LAYOUT_CASES = [
+    # rope stored apart: token-wise TopK (shared and separate V), CSA / HCA
+    # with rope on both KV sides, float16
+    dict(seed=900, family="sfa", rope_head_dim=64, separate_v=False, split_rope=True),
+    dict(seed=901, family="sfa", rope_head_dim=64, separate_v=True, split_rope=True,
+         max_kv=1500, topk=700, num_heads_q=128),
+    dict(seed=902, family="csa", rope_head_dim=64, split_rope=True, num_heads_q=64),
+    dict(seed=903, family="hca", rope_head_dim=64, split_rope=True, num_heads_q=16,
+         max_kv=900, cmp_ratio=2),
+    dict(seed=904, family="sfa", rope_head_dim=64, kv_dtype="fp16", split_rope=True,
+         num_heads_q=32),
+    # padded row strides (garbage in the padding), with and without rope apart
+    dict(seed=910, family="swa", pad=8, num_heads_q=16, max_kv=600),
+    dict(seed=911, family="csa", pad=8, num_heads_q=64),
+    dict(seed=912, family="sfa", rope_head_dim=64, separate_v=True, pad=8, num_heads_q=128,
+         max_kv=1500, topk=1100),
+    dict(seed=913, family="hca", rope_head_dim=64, split_rope=True, pad=8, num_heads_q=32,
+         cmp_ratio=4, max_kv=700),
+    dict(seed=914, family="sfa", kv_dtype="int8_packed", rope_head_dim=64, pad=8,
+         num_heads_q=128, max_kv=900, topk=600),
+    dict(seed=915, family="sfa", kv_dtype="fp8_e4m3_packed", rope_head_dim=0, pad=16,
+         num_heads_q=16),
+]
+
+
+@pytest.mark.parametrize("kw", LAYOUT_CASES, ids=lambda k: "-".join(str(v) for v in k.values()))
+def test_kv_layout_parity(kw):
+    """Rope given as its own tensor and / or padded row strides: the oracle on
+    the plain rows, the GPU on the relaid device tensors."""
+    import sparse_shared_kv_amd as s
+    kw = dict(kw)
+    split_rope, pad = kw.pop("split_rope", False), kw.pop("pad", 0)
+    P = synth.random_tiny(**kw)
+    arrays = _relayout(P, split_rope, pad)
+    call = s.Call(P.params, arrays)
+    if split_rope:
+        assert call.tensors.ori_rope and call.tensors.ori_kv_stride == 2 * (512 + (8 if pad else 0))
+    ref = oracle.forward(P)
+    res = run_gpu(P, call)
+    check_lists(P, call, ref)
+    check_outputs(P, res, ref)
+
+
+def test_lse_off_matches_lse_on_bitwise():
+    """return_softmax_lse = 0 (no LSE tensor) leaves attention_out bit for
+    bit what it is with the LSE returned, over split and unsplit rows."""
+    import sparse_shared_kv_amd as s
+    for seed, kw in ((920, dict(family="sfa", max_kv=3000, topk=1500, num_heads_q=128,
+                                rope_head_dim=64, separate_v=True)),
+                     (921, dict(family="csa", num_heads_q=64, max_kv=900, sinks=True)),
+                     (922, dict(family="sfa", kv_dtype="int8_packed", rope_head_dim=64,
+                                num_heads_q=128, max_kv=2500, topk=1100))):
+        P_on = synth.random_tiny(seed, lse=True, **kw)
+        P_off = synth.random_tiny(seed, lse=False, **kw)
+        on, off = run_gpu(P_on), run_gpu(P_off)
+        assert off["lse"] is None and on["lse"] is not None
+        assert np.array_equal(on["O"], off["O"]), seed
+        check_outputs(P_off, off, oracle.forward(P_off, rows=[0]), [0])
