@@ -254,6 +254,27 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* tens
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture that must not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation.  The same as sfmla_forward(), except that the split
+ * workspace is a buffer the library owns: one static device array of
+ * SFMLA_STATIC_WORKSPACE_BYTES on each GPU the library runs on, held from the
+ * time the library's code is loaded on that GPU until the process ends.  The
+ * call allocates and frees nothing.  A call whose parameters need a larger
+ * workspace (sfmla_workspace_size()) is refused with
+ * SFMLA_ERR_BUFFER_TOO_SMALL before anything is launched.  The stream must
+ * belong to the current device.  Every call on one GPU shares that GPU's
+ * array, and its contents from the last call stay there (nothing in it has
+ * to start at zero: every byte a call reads was written earlier in the same
+ * call).  Calls that overlap in time on one GPU (e.g. on two streams) race on
+ * it and give undefined results.
+ */
+#define SFMLA_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+sfmla_status sfmla_forward_static_workspace(const sfmla_params* params,
+                                            const sfmla_tensors* tensors, int32_t* metadata,
+                                            size_t n_ints, float softmax_scale, void* stream);
+
+/*
  * LSE merge of partial results over disjoint parts of each row set (the
  * FLASH_DECODE split of the kv_quant_sparse_flash_attention blog's kernel
  * structure; its usage notes name the max / sum outputs as what merges

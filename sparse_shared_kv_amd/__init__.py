@@ -21,7 +21,7 @@ from . import _abi
 from ._abi import KV_DTYPES, LAYOUTS, Lengths, Params, SfmlaError, Tensors
 
 __all__ = ["sfmla_metadata_size", "sfmla_metadata", "sfmla_workspace_size", "sfmla_forward",
-           "sfmla_combine", "sfmla_debug_resolve", "sfmla_time_next_forward",
+           "sfmla_forward_static_workspace", "sfmla_combine", "sfmla_debug_resolve", "sfmla_time_next_forward",
            "sfmla_version", "Params", "Lengths",
            "Tensors", "SfmlaError", "Call", "make_params", "CMP_BIT"]
 
@@ -97,6 +97,15 @@ def sfmla_forward(params: Params, tensors: Tensors, metadata: torch.Tensor, soft
     _abi.check(_lib().sfmla_forward(ctypes.byref(params), ctypes.byref(tensors), _ptr(metadata),
                                     metadata.numel(), ctypes.c_float(softmax_scale),
                                     _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sfmla_forward_static_workspace(params: Params, tensors: Tensors, metadata: torch.Tensor,
+                                   softmax_scale: float, stream=None):
+    """sfmla_forward with the split workspace held by the library (one static
+    device buffer per GPU; allocates nothing)."""
+    _abi.check(_lib().sfmla_forward_static_workspace(
+        ctypes.byref(params), ctypes.byref(tensors), _ptr(metadata), metadata.numel(),
+        ctypes.c_float(softmax_scale), _stream(stream)))
 
 
 def sfmla_combine(part_o: torch.Tensor, part_lse: torch.Tensor, sinks, out: torch.Tensor,

@@ -67,8 +67,9 @@ class Tensors(ctypes.Structure):
 
 
 SYMBOLS = ("sfmla_metadata_size", "sfmla_metadata", "sfmla_workspace_size",
-           "sfmla_forward", "sfmla_combine", "sfmla_debug_resolve",
-           "sfmla_time_next_forward", "sfmla_last_error", "sfmla_version")
+           "sfmla_forward", "sfmla_forward_static_workspace", "sfmla_combine",
+           "sfmla_debug_resolve", "sfmla_time_next_forward", "sfmla_last_error",
+           "sfmla_version")
 
 _lib = None
 
@@ -88,10 +89,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfmla_metadata.argtypes = [P(Params), P(Lengths), _vp, sz, _vp]
     lib.sfmla_workspace_size.argtypes = [P(Params), P(sz)]
     lib.sfmla_forward.argtypes = [P(Params), P(Tensors), _vp, sz, ctypes.c_float, _vp, sz, _vp]
+    lib.sfmla_forward_static_workspace.argtypes = [P(Params), P(Tensors), _vp, sz,
+                                                   ctypes.c_float, _vp]
     lib.sfmla_combine.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
     lib.sfmla_debug_resolve.argtypes = [P(Params), P(Tensors), _vp, sz, _vp, _i32, _vp, _vp]
     lib.sfmla_time_next_forward.argtypes = [_vp, _vp]
-    for name in SYMBOLS[:7]:
+    for name in SYMBOLS[:8]:
         getattr(lib, name).restype = ctypes.c_int
     lib.sfmla_last_error.restype = ctypes.c_char_p
     lib.sfmla_last_error.argtypes = []

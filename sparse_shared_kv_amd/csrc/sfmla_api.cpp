@@ -460,6 +460,26 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
   return ok();
 }
 
+sfmla_status sfmla_forward_static_workspace(const sfmla_params* params, const sfmla_tensors* t,
+                                            int32_t* metadata, size_t n_ints,
+                                            float softmax_scale, void* stream) {
+  sfmla_status s = validate(params);
+  if (s != SFMLA_OK) return s;
+  const size_t need = workspace_bytes(*params);
+  if (need > sfmla::kStaticWorkspaceBytes)
+    return fail(SFMLA_ERR_BUFFER_TOO_SMALL,
+                "these parameters need %zu bytes of split workspace; the library-owned one "
+                "holds %zu (use sfmla_forward with a caller workspace)",
+                need, (size_t)sfmla::kStaticWorkspaceBytes);
+  void* ws = nullptr;
+  if (need) {
+    const hipError_t e = sfmla::static_workspace(&ws);
+    if (e != hipSuccess)
+      return fail(SFMLA_ERR_LAUNCH, "library workspace address: %s", hipGetErrorString(e));
+  }
+  return sfmla_forward(params, t, metadata, n_ints, softmax_scale, ws, need ? need : 0, stream);
+}
+
 sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
                            int32_t* metadata, size_t n_ints, float softmax_scale,
                            void* workspace, size_t ws_bytes, void* stream) {

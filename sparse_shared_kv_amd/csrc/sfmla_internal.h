@@ -15,6 +15,8 @@ constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
 constexpr int kCounterInts = 64;   // arrival counters per query row (one per head group x wave)
 constexpr int32_t kMagic = 0x534d4c41;
+// size of the library-owned split workspace (one static device array per GPU)
+constexpr size_t kStaticWorkspaceBytes = SFMLA_STATIC_WORKSPACE_BYTES;
 
 // Per-query-row plan record written by the planner (int32 each).
 enum RecField {
@@ -102,5 +104,8 @@ hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt,
                           hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_debug_resolve(const FwdArgs& a, hipStream_t s);
+// device address of the library-owned split workspace on the current device
+// (looked up once per device; allocates nothing)
+hipError_t static_workspace(void** ptr);
 
 }  // namespace sfmla

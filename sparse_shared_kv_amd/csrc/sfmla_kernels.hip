@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sfmla_internal.h"
 
 namespace sfmla {
@@ -1378,6 +1380,39 @@ hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt,
       return vmode ? launch_fwd_t<8, 576, 1, 0>(a, groups, s, t0, t1)
                    : launch_fwd_t<8, 576, 0, 0>(a, groups, s, t0, t1);
   }
+}
+
+// ---------------------------------------------------------------------------
+// library-owned split workspace (sfmla_forward_static_workspace)
+// ---------------------------------------------------------------------------
+
+// Every GPU the library runs on holds one copy of this array from the time
+// the code object is loaded on it until the process ends.  Its name is a
+// host-side stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, never the name.
+static __device__ __align__(256) char scratch[kStaticWorkspaceBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t static_workspace(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // once per device, with that device current (two threads racing here
+    // read the same address)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
