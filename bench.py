@@ -295,6 +295,11 @@ def main():
     ap.add_argument("--replicas", type=int, default=4,
                     help="index-set replicas rotated between steps (TopK workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--merge-wait-us", type=int, default=0,
+                    help="sfmla_params.merge_wait_us (0: the library's rule; -1: the last "
+                         "split to arrive merges)")
+    ap.add_argument("--split-rows", type=int, default=0,
+                    help="sfmla_params.split_rows (0: the library's rule)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--profile-commands", metavar="OUTDIR",
@@ -327,7 +332,8 @@ def main():
 
     log("[bench] building workload", args.workload)
     P = synth.make_workload(args.workload)
-    call = s.Call(P.params, P.arrays, device=dev)
+    spec = dict(P.params, merge_wait_us=args.merge_wait_us, split_rows=args.split_rows)
+    call = s.Call(spec, P.arrays, device=dev)
     reps = synth.index_replicas(P, args.replicas - 1) if args.replicas > 1 else []
     idx_sets = []
     if reps:

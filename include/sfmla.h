@@ -156,6 +156,13 @@ typedef struct sfmla_params {
    *                         value.                                           */
   int32_t split_rows;
   int32_t head_blocks_per_group;
+  /* How the partials of a split row are merged inside sfmla_forward
+   * (0 = the library's rule): -1 = the last split to arrive merges them; a
+   * positive value = the split that owns a block of heads waits at most that
+   * many microseconds (1..10000) for the others and merges them itself
+   * (used only when every workgroup of the launch is resident at once; on
+   * time-out the last to arrive merges).  Every setting gives the same bits. */
+  int32_t merge_wait_us;
 } sfmla_params;
 
 /*

@@ -191,6 +191,7 @@ def make_params(spec: dict, arrays: dict) -> Params:
     p.has_cmp_residual_kv = int(arrays.get("cmp_residual_kv") is not None)
     p.split_rows = int(g("split_rows", 0))
     p.head_blocks_per_group = int(g("head_blocks_per_group", 0))
+    p.merge_wait_us = int(g("merge_wait_us", 0))
     return p
 
 

@@ -62,7 +62,7 @@ uint32_t fingerprint(const sfmla_params& p) {
       p.cmp_mask_mode, p.ori_win_left, p.ori_win_right, p.has_ori_kv, p.has_cmp_kv,
       p.kv_dtype, p.has_separate_v, p.has_sinks, p.return_softmax_lse, p.has_seqused_q,
       p.has_seqused_ori_kv, p.has_seqused_cmp_kv, p.has_cmp_residual_kv, p.split_rows,
-      p.head_blocks_per_group};
+      p.head_blocks_per_group, p.merge_wait_us};
   for (int32_t v : f32) mix(v);
   mix(p.ori_kv_rows);
   mix(p.cmp_kv_rows);
@@ -128,6 +128,8 @@ sfmla_status validate(const sfmla_params* pp) {
               p.head_blocks_per_group == 2 || p.head_blocks_per_group == 4 ||
               p.head_blocks_per_group == 8,
           "head_blocks_per_group must be 0, 1, 2, 4 or 8");
+  REQUIRE(p.merge_wait_us >= -1 && p.merge_wait_us <= 10000,
+          "merge_wait_us must be -1, 0 or 1..10000");
   REQUIRE(!(p.has_separate_v && p.kv_dtype != SFMLA_KV_BF16 && p.kv_dtype != SFMLA_KV_FP16),
           "a separate V is only supported for bf16 KV (packed V is the dequantised nope)");
   if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.ori_kv_s > 0, "BSND ori_kv needs ori_kv_s > 0");
@@ -227,6 +229,11 @@ size_t metadata_ints(const sfmla_params& p) {
   return (size_t)sfmla::kHeaderInts +
          (size_t)(sfmla::kRecInts + sfmla::kCounterInts) * (size_t)p.q_t;
 }
+
+// Longest wait (us) of a split that merges the partials of its row's other
+// splits for them (the splits of a row end within a few us of each other;
+// past this bound it hands the merge to the last split to arrive).
+constexpr int kMergeWaitUs = 40;
 
 // Workgroups below which a launch spreads a row's heads over several groups.
 constexpr int64_t kMinGroups = 256;
@@ -508,8 +515,11 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
   a.bpg = bpg;
   const int dqk = 512 + p.rope_head_dim;
   const int vmode = p.has_separate_v ? 1 : 0;
-  hipError_t e =
-      sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, (hipStream_t)stream, t0, t1);
+  // the owned split merge waits at most this long for the row's other
+  // splits (when the launch's workgroups are all resident at once)
+  const int merge_wait_us = p.merge_wait_us == 0 ? kMergeWaitUs : std::max(0, p.merge_wait_us);
+  hipError_t e = sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, merge_wait_us,
+                                       (hipStream_t)stream, t0, t1);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -58,6 +58,7 @@ struct FwdArgs {
   int32_t groups;                   // head groups of the launch
   int32_t bpg;                      // 16-head blocks per head group (<= waves; spare waves only load)
   int32_t split_rows;               // list positions per split of a short-query row
+  int32_t merge_wait_ticks;         // owned-merge wait bound (s_memrealtime ticks; 0: none)
   uint32_t fingerprint;
   float scale_log2;                 // softmax_scale * log2(e)
   const int32_t* meta;
@@ -100,8 +101,11 @@ struct CombineArgs {
 // Kernel launchers (defined in sfmla_kernels.hip).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // t0 / t1 (may be null): events the dispatch stamps at the kernel's start / end
+// merge_wait_us: the owned-merge wait bound when every workgroup of the launch
+// can be resident at once (0: never wait)
 hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
-                          hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+                          int merge_wait_us, hipStream_t s, hipEvent_t t0 = nullptr,
+                          hipEvent_t t1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_debug_resolve(const FwdArgs& a, hipStream_t s);
 // device address of the library-owned split workspace on the current device

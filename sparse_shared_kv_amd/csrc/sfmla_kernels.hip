@@ -382,6 +382,15 @@ __device__ __forceinline__ void dma16_s(uint64_t base, uint32_t voff, uint32_t l
                : "memory");
 }
 
+// The same with the agent-scope cache policy (sc1): data another workgroup
+// stored with sc1 stores (split partials).
+__device__ __forceinline__ void dma16_sc1(const void* g, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1"
+               :
+               : "v"(g), "{m0}"(lds_addr)
+               : "memory");
+}
+
 // 64-bit value held by lane j, as a uniform (SGPR) value.
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int j) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, j);
@@ -429,6 +438,12 @@ __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)"
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr(T* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)p;
+}
+// 16 bytes at an LDS byte address
+__device__ __forceinline__ uint4 lds_ld16(uint32_t addr) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u v = *(const __attribute__((address_space(3))) v4u*)(uintptr_t)addr;
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <int NW, int DQK, int VMODE>
@@ -613,6 +628,7 @@ __device__ __forceinline__ void decode_tile(const char* raw, char* kbf, float* s
 // touched only when the max jumps.
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kMergeSplits = 4;       // splits whose partials one merge round loads (8 waves)
+constexpr int kMaxOwnerSplits = 8;    // splits of a row whose partials an owning wave merges
 
 // HB head blocks of 16 heads per wave; FMT is the KV storage format.
 template <int NW, int HB, int DQK, int VMODE, int FMT>
@@ -643,12 +659,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   __shared__ uint32_t sRow[kMaxSplitRows + T];      // resolved positions of the split
   // bf16 / fp16 with a separate V: a merging wave stages its output in the
   // K / V stage buffers (two waves per buffer) once every wave of the
-  // workgroup is done with them (sOut counts the waves out)
+  // workgroup is done with them (sOut counts the waves out); owning waves
+  // (below) land the other splits' partials there
   constexpr bool STAGE = VMODE && !PK;
+  constexpr bool OUTCNT = !PK;
   constexpr int kStgRow = 1040;                      // staged output row (one head), padded
   static_assert(!STAGE || (NW == 8 && 2 * 16 * kStgRow <= T * RS && T * RS <= C::KBYTES),
                 "output staging: two waves' 16 heads per stage buffer");
   __shared__ int32_t sOut;
+  // V = K nope: two more landing slots for the owned merge (the separate-V
+  // kernel has its V stages for them)
+  __shared__ __align__(16) char sM[(VMODE || PK) ? 16 : 32768];
+  // owned merge: per owning wave, every split's weight and the normaliser
+  // per head, and a flag (1: landed and weighted, 2: handed off)
+  __shared__ float sWs[PK ? 1 : NW][PK ? 1 : kMaxOwnerSplits][16];
+  __shared__ float sInv[PK ? 1 : NW][16];
+  __shared__ int32_t sReady[NW];
 
   // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so XCD x = bid
   // mod 8 takes the query rows 8k + x, and within it slot bid / 8 runs over
@@ -688,12 +714,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // the resolve below reloads in those cases.  Every load is in bounds
   // (positions past the lists read the plan header instead).
   constexpr int PPT = (512 + T + NTHR - 1) / NTHR;   // positions per thread and batch
+  // Position of slot u of a resolve batch starting at i0.  bf16 rows: wave w
+  // resolves exactly the rows it gathers (row w*NR + l%NR of tile l/NR, then
+  // the next 64/NR tiles for u = 1), so it can issue its share of the first
+  // tiles as soon as its own entries are in, with no workgroup barrier.
+  // Packed rows (gathered in 16-byte chunks across rows): one position per
+  // thread in order.
+  auto posn = [&](int i0, int u) -> int {
+    if constexpr (PK) {
+      return i0 + tid + u * NTHR;
+    } else {
+      constexpr int NR = C::NR, TPB = 64 / NR;
+      static_assert(PPT * TPB * T == PPT * NTHR, "a batch covers PPT*NTHR positions");
+      return i0 + (u * TPB + l / NR) * T + w * NR + (l % NR);
+    }
+  };
   const int spec_cnt = a.ori_topk << a.ori_sbs_log2;
   const int spec_cap = a.ori_topk > 0 ? spec_cnt + (a.cmp_topk > 0 ? a.cmp_topk : 0) : 0;
   int vspec[PPT];
 #pragma unroll
   for (int u = 0; u < PPT; ++u) {
-    const int i = tid + u * NTHR;
+    const int i = posn(0, u);
     const int k = split * a.split_rows + i;
     const int32_t* ep = (const int32_t*)a.meta;
     if (i < a.split_rows && k < spec_cap)
@@ -739,7 +780,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // Q slices (B operand: k = d, n = head).  They are loaded right after the
   // table loads of the resolve below: loads complete in order, so waiting
   // for the table entries does not wait for Q, which travels while the
-  // entries go to LDS and the first tile's rows are requested.
+  // entries go to LDS.  Every load here is an ordinary one the compiler
+  // tracks: it places the waits for its results itself.
   bf16x8 qreg[HB][NKS];
   // ---- resolve every list position of this split once, into physical row
   //      entries in LDS (empty or masked slots: kNoRow).  Positions go in
@@ -761,7 +803,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         // join waits for them
 #pragma unroll
         for (int u = 0; u < PPT; ++u) {
-          const int i = i0 + tid + u * NTHR;
+          const int i = posn(i0, u);
           const int k = k0 + i;
           const int32_t* ep = (i < ntT && k < k1) ? slot_entry(a, ri, row, k) : nullptr;
           vv[u] = *(ep ? ep : rec);
@@ -771,7 +813,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
-        const int i = i0 + tid + u * NTHR;
+        const int i = posn(i0, u);
         const int k = k0 + i;
         sd[u] = 0;
         jj[u] = (i < ntT && k < k1) ? slot_row(a, ri, k, vv[u], &sd[u]) : -1;
@@ -787,8 +829,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
-        const int i = i0 + tid + u * NTHR;
-        if (i >= ntT) break;
+        const int i = posn(i0, u);
+        if (i >= ntT) continue;
         const int64_t phys = phys_row(a, ri, jj[u], sd[u], he[u], ee[u]);
         sRow[i] = phys >= 0 ? (uint32_t)phys | (sd[u] ? kCmpBit : 0u) : kNoRow;
       }
@@ -811,9 +853,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     });
     for (int i0 = PPT * NTHR; i0 < ntT; i0 += PPT * NTHR) batch(i0, false, [] {});
   }
-  if (STAGE && tid == 0) sOut = 0;
-  wait_lgkm0();
-  block_barrier();
+  if (OUTCNT && tid == 0) sOut = 0;
+  if (OUTCNT && tid < NW) sReady[tid] = 0;
+  if constexpr (PK) {
+    wait_lgkm0();
+    block_barrier();
+  }
 
   f32x4 o[HB][32];
 #pragma unroll
@@ -995,13 +1040,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(a, sRow, (tt + 2) * T, lds_addr(sKc), w, l);
       if (wave_on) pv(sVc);
     };
-    // K(0) and the Q slices land first; the explicit full wait also tells
-    // the compiler the Q loads are done, so no wait for them remains inside
-    // the loop (where it would wait for every gather in flight).
-    if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
-    wait_vmcnt<0>();
+    // Q lands before the first tiles go out: the compiler waits for the Q
+    // loads at their first use, which is here (settle), so that no wait it
+    // places inside the loop covers a gather in flight.  K(0), V(0) and K(1)
+    // then go out together; every wave issues the rows whose entries it
+    // resolved itself.
     settle(qreg);
     if (nt > 0) {
+      issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
       issue_v<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sV0), w, l);
       if (nt > 1) issue_k<NW, DQK, VMODE>(a, sRow, T, lds_addr(sK1), w, l);
     }
@@ -1021,9 +1067,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         pv(sKc);
       }
     };
-    if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
-    wait_vmcnt<0>();                                      // K(0) and the Q slices
+    // Q lands first (its first use is here), then K(0) and K(1) go out
     settle(qreg);
+    if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
     if (nt > 1) issue_k<NW, DQK, VMODE>(a, sRow, T, lds_addr(sK1), w, l);
     for (int tt = 0; tt < nt; tt += 3) {
       step(tt, sK0, sK2);
@@ -1032,7 +1078,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  if constexpr (STAGE) {
+  if constexpr (OUTCNT) {
     // this wave's last reads of the stage buffers have returned
     wait_lgkm0();
     if (l == 0) atomicAdd(&sOut, 1);
@@ -1075,10 +1121,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     return;
   }
 
-  // ---- split rows: every split stores its normalised partial (bf16, in the
-  // lanes' fragment order: instruction j of a wave writes 1 KB contiguously),
-  // then counts itself in; the last one to arrive merges all of them.
-  // loader-only waves hold no partial (their h0 lies in another group's heads)
+  // ---- split rows.  Loader-only waves hold no partial (their h0 lies in
+  // another group's heads).
   if (!wave_on) return;
   static_assert(NW * 8 <= kCounterInts, "arrival counters per row: head groups (<= 8) x waves");
   const int HP = a.groups * NW * HPW;              // heads per row, padded
@@ -1088,161 +1132,332 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const int64_t row_bytes = (int64_t)a.max_splits * a.groups * NW * WAVE_BYTES;
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc((char*)a.ws_ob + row * row_bytes, row_bytes);
   const int wave_off = ((split * a.groups + hg) * NW + w) * WAVE_BYTES;
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      uint4 pk;
-      pk.x = (uint32_t)to16<HALF>(o[hb][2 * j][0] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][1] * inv) << 16);
-      pk.y = (uint32_t)to16<HALF>(o[hb][2 * j][2] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][3] * inv) << 16);
-      pk.z = (uint32_t)to16<HALF>(o[hb][2 * j + 1][0] * inv) |
-             ((uint32_t)to16<HALF>(o[hb][2 * j + 1][1] * inv) << 16);
-      pk.w = (uint32_t)to16<HALF>(o[hb][2 * j + 1][2] * inv) |
-             ((uint32_t)to16<HALF>(o[hb][2 * j + 1][3] * inv) << 16);
-      const u32x4 d = {pk.x, pk.y, pk.z, pk.w};
-      __builtin_amdgcn_raw_buffer_store_b128(d, rs, wave_off + ((hb * 16 + j) * 64 + l) * 16, 0, kSc1);
-    }
-    if (g == 0)
-      st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
-  }
-  drain_vmem();                                     // this wave's partial is stored
-  // Arrival is counted per (row, head group, wave): the last of the splits'
-  // waves for these 16 heads merges them, so the merges of one row spread
-  // over the splits' workgroups and no workgroup barrier is needed.
+  // arrival counter of this (row, head group, wave) over the splits
   int32_t* ctr = a.counters + (int64_t)row * kCounterInts + hg * NW + w;
-  int last = 0;
-  if (l == 0)
-    last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
-  if (!__builtin_amdgcn_readfirstlane(last)) return;
-  if (l == 0)                                       // ready for the next call
-    __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // merge from the stored partials (this split's own included).  Round r
-  // loads column blocks [JB*(r / ns4), +JB) of MS splits (MS*JB loads of 16
-  // bytes per lane in flight: 16, or 32 where one wave per SIMD leaves the
-  // registers); the first round travels together with the loads of the
-  // LSEs, which give the max and the normaliser in one pass.
-  constexpr int MS = NW <= 4 ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = 16 / JB;
-  const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
-  const int R = NJ * ns4;                               // load rounds
-  const int split_bytes = a.groups * NW * WAVE_BYTES;
-  // Staged output: rounds write their results to LDS and the wave stores all
-  // 16 heads at the end.  Vector-memory stores count in vmcnt with the loads
-  // and complete in order, so stores between rounds would make each next
-  // round's wait include them.  Every wave of the workgroup counts itself
-  // out right after its main loop, so this wait ends.
-  char* stg = nullptr;
-  if constexpr (STAGE) {
-    stg = (w < 2 ? sK0 : w < 4 ? sK1 : w < 6 ? sV0 : sV1) + (w & 1) * 16 * kStgRow;
-    while (*(volatile int32_t*)&sOut < NW) __builtin_amdgcn_s_sleep(1);
-  }
+
+  // Owned merges (bf16 rows).  The partials of wave w's 16 heads are merged
+  // in the workgroup of split w % nsplit, their owner, when the launch lets it
+  // wait (every workgroup of the launch is resident at once, so the other
+  // splits make progress meanwhile):
+  //   - the owning wave writes its own partial to an LDS slot (the bits a
+  //     store would have written), waits until the other nsplit - 1 splits
+  //     have counted in, computes the split weights, lands their partials in
+  //     LDS slots with one round of DMA and raises a flag;
+  //   - every head-holding wave of the workgroup then merges a share of the
+  //     owned heads' 16 fragments from LDS (the merge runs on all SIMDs).
+  // The wait is bounded: past a.merge_wait_ticks the owner stores its partial
+  // and counts in like the others, and the last to arrive merges (below),
+  // which gives the same bits.  Non-owning waves store and count in, then
+  // help.  After the last split's loop the critical path is one store, one
+  // count, one load round and a merge spread over the workgroup.
+  constexpr int OSLOT = 8;                          // LDS slots of 16 KB
+  const int n_on = min(a.bpg, (a.qn - hg * a.bpg * HPW + HPW - 1) / HPW);   // waves with heads
+  const int n_own = split < n_on ? (n_on - 1 - split) / nsplit + 1 : 0;    // owned waves here
+  const bool own_mode = !PK && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
+                        n_own > 0 && n_own * nsplit <= OSLOT;
+  auto slot_addr = [&](int q) -> uint32_t {          // slot q: two per stage buffer
+    const int b = q >> 1;
+    const uint32_t base = VMODE ? (b == 0 ? lds_addr(sK0) : b == 1 ? lds_addr(sK1)
+                                   : b == 2 ? lds_addr(sV0) : lds_addr(sV1))
+                                : (b == 0 ? lds_addr(sK0) : b == 1 ? lds_addr(sK1)
+                                   : b == 2 ? lds_addr(sK2) : lds_addr(sM));
+    return __builtin_amdgcn_readfirstlane(base + (q & 1) * 16384);
+  };
+  // the last-arriver merge of this wave's heads (every split's partial from
+  // memory, this split's own included)
+  auto merge_last = [&]() __attribute__((always_inline)) {
+    // merge from the stored partials (this split's own included).  Round r
+    // loads column blocks [JB*(r / ns4), +JB) of MS splits (MS*JB loads of 16
+    // bytes per lane in flight: 16, or 32 where one wave per SIMD leaves the
+    // registers); the first round travels together with the loads of the
+    // LSEs, which give the max and the normaliser in one pass.
+    constexpr int MS = NW <= 4 ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = 16 / JB;
+    const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
+    const int R = NJ * ns4;                               // load rounds
+    const int split_bytes = a.groups * NW * WAVE_BYTES;
+    // Staged output: rounds write their results to LDS and the wave stores all
+    // 16 heads at the end.  Vector-memory stores count in vmcnt with the loads
+    // and complete in order, so stores between rounds would make each next
+    // round's wait include them.  Every wave of the workgroup counts itself
+    // out right after its main loop, so this wait ends.  Not while owning
+    // waves of this workgroup use the same buffers (owned merges): this
+    // merge is then the rare fallback after a time-out and stores directly.
+    char* stg = nullptr;
+    const bool stage = STAGE && !own_mode;
+    if (stage) {
+      stg = (w < 2 ? sK0 : w < 4 ? sK1 : w < 6 ? sV0 : sV1) + (w & 1) * 16 * kStgRow;
+      while (*(volatile int32_t*)&sOut < NW) __builtin_amdgcn_s_sleep(1);
+    }
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int h = h0 + 16 * hb + t;
-    const float* lp = a.ws_lse + (int64_t)row * a.max_splits * HP + h;
-    const int off0 = (hg * NW + w) * WAVE_BYTES + ((hb * 16) * 64 + l) * 16;   // split 0
-    u32x4 v[MS][JB];
-    float wl[MS];
-    auto issue = [&](int r) {
-      const int jr = r / ns4, s0 = (r - jr * ns4) * MS;
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = h0 + 16 * hb + t;
+      const float* lp = a.ws_lse + (int64_t)row * a.max_splits * HP + h;
+      const int off0 = (hg * NW + w) * WAVE_BYTES + ((hb * 16) * 64 + l) * 16;   // split 0
+      u32x4 v[MS][JB];
+      float wl[MS];
+      auto issue = [&](int r) {
+        const int jr = r / ns4, s0 = (r - jr * ns4) * MS;
 #pragma unroll
-      for (int q = 0; q < MS; ++q) {
-        const int s2 = min(s0 + q, nsplit - 1);
-        wl[q] = ld_agent(lp + (int64_t)s2 * HP);
+        for (int q = 0; q < MS; ++q) {
+          const int s2 = min(s0 + q, nsplit - 1);
+          wl[q] = ld_agent(lp + (int64_t)s2 * HP);
 #pragma unroll
-        for (int j = 0; j < JB; ++j)
-          v[q][j] = __builtin_amdgcn_raw_buffer_load_b128(
-              rs, off0 + s2 * split_bytes + (jr * JB + j) * 64 * 16, 0, kSc1);
-      }
-    };
-    issue(0);
-    // max and normaliser over every split's LSE (the first chunk is wl)
-    float M = kNegInf, tot = 0.f;
-#pragma unroll
-    for (int q = 0; q < MS; ++q)
-      if (q < nsplit) M = fmaxf(M, wl[q]);
-#pragma unroll 1
-    for (int s0 = MS; s0 < nsplit; s0 += MS) {
+          for (int j = 0; j < JB; ++j)
+            v[q][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, off0 + s2 * split_bytes + (jr * JB + j) * 64 * 16, 0, kSc1);
+        }
+      };
+      issue(0);
+      // max and normaliser over every split's LSE (the first chunk is wl)
+      float M = kNegInf, tot = 0.f;
 #pragma unroll
       for (int q = 0; q < MS; ++q)
-        if (s0 + q < nsplit) M = fmaxf(M, ld_agent(lp + (int64_t)(s0 + q) * HP));
-    }
-    const float Mu = M == kNegInf ? 0.f : M;
-#pragma unroll
-    for (int q = 0; q < MS; ++q)
-      if (q < nsplit) tot += __builtin_amdgcn_exp2f(wl[q] - Mu);
+        if (q < nsplit) M = fmaxf(M, wl[q]);
 #pragma unroll 1
-    for (int s0 = MS; s0 < nsplit; s0 += MS) {
+      for (int s0 = MS; s0 < nsplit; s0 += MS) {
+#pragma unroll
+        for (int q = 0; q < MS; ++q)
+          if (s0 + q < nsplit) M = fmaxf(M, ld_agent(lp + (int64_t)(s0 + q) * HP));
+      }
+      const float Mu = M == kNegInf ? 0.f : M;
 #pragma unroll
       for (int q = 0; q < MS; ++q)
-        if (s0 + q < nsplit) tot += __builtin_amdgcn_exp2f(ld_agent(lp + (int64_t)(s0 + q) * HP) - Mu);
-    }
-    float den = tot;
-    if (a.has_sinks && h < a.qn && tot > 0.f)
-      den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - Mu);
-    const float inv = tot > 0.f ? 1.f / den : 0.f;
-    const bool on = h < a.qn;
-    uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g;
-    float acc[JB][8];
-#pragma unroll
-    for (int j = 0; j < JB; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+        if (q < nsplit) tot += __builtin_amdgcn_exp2f(wl[q] - Mu);
 #pragma unroll 1
-    for (int r = 0; r < R; ++r) {
-      if (r > 0) issue(r);
-      const int jr = r / ns4, s0 = (r - jr * ns4) * MS;
+      for (int s0 = MS; s0 < nsplit; s0 += MS) {
 #pragma unroll
-      for (int q = 0; q < MS; ++q) {
-        const float ws = s0 + q < nsplit ? __builtin_amdgcn_exp2f(wl[q] - Mu) : 0.f;
-#pragma unroll
-        for (int j = 0; j < JB; ++j) {
-          const uint32_t u[4] = {v[q][j].x, v[q][j].y, v[q][j].z, v[q][j].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[j][2 * e] += ws * lo16<HALF>(u[e]);
-            acc[j][2 * e + 1] += ws * hi16<HALF>(u[e]);
-          }
-        }
+        for (int q = 0; q < MS; ++q)
+          if (s0 + q < nsplit) tot += __builtin_amdgcn_exp2f(ld_agent(lp + (int64_t)(s0 + q) * HP) - Mu);
       }
-      if (s0 + MS < nsplit) continue;                    // more splits for these columns
-      if (STAGE || on) {
-#pragma unroll
-        for (int j = 0; j < JB; ++j) {
-          const int jj = jr * JB + j;
-          uint2 p0, p1;
-          p0.x = (uint32_t)to16<HALF>(acc[j][0] * inv) | ((uint32_t)to16<HALF>(acc[j][1] * inv) << 16);
-          p0.y = (uint32_t)to16<HALF>(acc[j][2] * inv) | ((uint32_t)to16<HALF>(acc[j][3] * inv) << 16);
-          p1.x = (uint32_t)to16<HALF>(acc[j][4] * inv) | ((uint32_t)to16<HALF>(acc[j][5] * inv) << 16);
-          p1.y = (uint32_t)to16<HALF>(acc[j][6] * inv) | ((uint32_t)to16<HALF>(acc[j][7] * inv) << 16);
-          if constexpr (STAGE) {
-            char* sp = stg + (16 * hb + t) * kStgRow + 2 * (32 * jj + 4 * g);
-            *(uint2*)sp = p0;
-            *(uint2*)(sp + 32) = p1;
-          } else {
-            *(uint2*)(op + 16 * (2 * jj)) = p0;
-            *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
-          }
-        }
-      }
+      float den = tot;
+      if (a.has_sinks && h < a.qn && tot > 0.f)
+        den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - Mu);
+      const float inv = tot > 0.f ? 1.f / den : 0.f;
+      const bool on = h < a.qn;
+      uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g;
+      float acc[JB][8];
 #pragma unroll
       for (int j = 0; j < JB; ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+#pragma unroll 1
+      for (int r = 0; r < R; ++r) {
+        if (r > 0) issue(r);
+        const int jr = r / ns4, s0 = (r - jr * ns4) * MS;
+#pragma unroll
+        for (int q = 0; q < MS; ++q) {
+          const float ws = s0 + q < nsplit ? __builtin_amdgcn_exp2f(wl[q] - Mu) : 0.f;
+#pragma unroll
+          for (int j = 0; j < JB; ++j) {
+            const uint32_t u[4] = {v[q][j].x, v[q][j].y, v[q][j].z, v[q][j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[j][2 * e] = __builtin_fmaf(ws, lo16<HALF>(u[e]), acc[j][2 * e]);
+              acc[j][2 * e + 1] = __builtin_fmaf(ws, hi16<HALF>(u[e]), acc[j][2 * e + 1]);
+            }
+          }
+        }
+        if (s0 + MS < nsplit) continue;                    // more splits for these columns
+        if (stage || on) {
+#pragma unroll
+          for (int j = 0; j < JB; ++j) {
+            const int jj = jr * JB + j;
+            uint2 p0, p1;
+            p0.x = (uint32_t)to16<HALF>(acc[j][0] * inv) | ((uint32_t)to16<HALF>(acc[j][1] * inv) << 16);
+            p0.y = (uint32_t)to16<HALF>(acc[j][2] * inv) | ((uint32_t)to16<HALF>(acc[j][3] * inv) << 16);
+            p1.x = (uint32_t)to16<HALF>(acc[j][4] * inv) | ((uint32_t)to16<HALF>(acc[j][5] * inv) << 16);
+            p1.y = (uint32_t)to16<HALF>(acc[j][6] * inv) | ((uint32_t)to16<HALF>(acc[j][7] * inv) << 16);
+            if (stage) {
+              char* sp = stg + (16 * hb + t) * kStgRow + 2 * (32 * jj + 4 * g);
+              *(uint2*)sp = p0;
+              *(uint2*)(sp + 32) = p1;
+            } else {
+              *(uint2*)(op + 16 * (2 * jj)) = p0;
+              *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+      }
+      if (on && a.lse && g == 0)
+        a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;
     }
-    if (on && a.lse && g == 0)
-      a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;
+    if (stage) {
+      // the staged heads (1 KB each, contiguous in the output) go out 16 bytes
+      // a lane; heads past q_n are not written
+      wait_lgkm0();
+      // (heads past q_n are read and not written, so that every row read
+      // is one unconditional instruction)
+#pragma unroll
+      for (int i = 0; i < 16 * HB; ++i) {
+        const uint4 r = *(const uint4*)(stg + i * kStgRow + 16 * l);
+        if (h0 + i < a.qn) *(uint4*)(a.out + ((int64_t)row * a.qn + h0 + i) * 512 + 8 * l) = r;
+      }
+    }
+  };
+
+  bool owned_here = false;                          // this wave's heads are merged here
+  if constexpr (!PK) {
+    static_assert(HB == 1, "owned merge: one 16-head block per wave");
+    if (own_mode && w % nsplit == split) {
+      const int ow = w / nsplit;
+      // the stage buffers are free once every wave has counted out
+      while (*(volatile int32_t*)&sOut < NW) __builtin_amdgcn_s_sleep(1);
+      {
+        const float io = lt[0] > 0.f ? 1.f / lt[0] : 0.f;
+        const uint32_t dst = slot_addr(ow * nsplit + split) + 16 * l;
+        typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          v4u pk;
+          pk.x = (uint32_t)to16<HALF>(o[0][2 * j][0] * io) | ((uint32_t)to16<HALF>(o[0][2 * j][1] * io) << 16);
+          pk.y = (uint32_t)to16<HALF>(o[0][2 * j][2] * io) | ((uint32_t)to16<HALF>(o[0][2 * j][3] * io) << 16);
+          pk.z = (uint32_t)to16<HALF>(o[0][2 * j + 1][0] * io) |
+                 ((uint32_t)to16<HALF>(o[0][2 * j + 1][1] * io) << 16);
+          pk.w = (uint32_t)to16<HALF>(o[0][2 * j + 1][2] * io) |
+                 ((uint32_t)to16<HALF>(o[0][2 * j + 1][3] * io) << 16);
+          *(__attribute__((address_space(3))) v4u*)(uintptr_t)(dst + j * 1024) = pk;
+        }
+      }
+      int seen = 0;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seen >= nsplit - 1) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)a.merge_wait_ticks) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (__builtin_amdgcn_readfirstlane(seen) >= nsplit - 1) {
+        owned_here = true;
+        if (l == 0)                                   // ready for the next call
+          __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int h = h0 + t;
+        const float* lp0 = a.ws_lse + (int64_t)row * a.max_splits * HP + h;
+        float wl[kMaxOwnerSplits];
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxOwnerSplits; ++s2)
+          wl[s2] = s2 >= nsplit ? kNegInf : s2 == split ? lse2[0] : ld_agent(lp0 + (int64_t)s2 * HP);
+        const char* part0 = (const char*)a.ws_ob + row * row_bytes +
+                            (int64_t)(hg * NW + w) * WAVE_BYTES + 16 * l;   // split 0
+        const int split_bytes = a.groups * NW * WAVE_BYTES;
+#pragma unroll 1
+        for (int sp = 0; sp < nsplit; ++sp) {
+          if (sp == split) continue;
+          const uint32_t dst = slot_addr(ow * nsplit + sp);
+          wait_vmcnt<63 - 16>();                      // the 6-bit counter never overflows
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            dma16_sc1(part0 + (int64_t)sp * split_bytes + j * 1024, dst + j * 1024);
+        }
+        float M = kNegInf;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxOwnerSplits; ++s2) M = fmaxf(M, wl[s2]);
+        const float Mu = M == kNegInf ? 0.f : M;
+        float tot = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxOwnerSplits; ++s2)
+          if (s2 < nsplit) tot += __builtin_amdgcn_exp2f(wl[s2] - Mu);
+        float den = tot;
+        if (a.has_sinks && h < a.qn && tot > 0.f)
+          den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - Mu);
+        if (g == 0) {
+#pragma unroll
+          for (int s2 = 0; s2 < kMaxOwnerSplits; ++s2)
+            if (s2 < nsplit) sWs[ow][s2][t] = __builtin_amdgcn_exp2f(wl[s2] - Mu);
+          sInv[ow][t] = tot > 0.f ? 1.f / den : 0.f;
+          if (h < a.qn && a.lse)
+            a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;
+        }
+        wait_vmcnt<0>();                              // the partials have landed
+        wait_lgkm0();
+        if (l == 0) *(volatile int32_t*)&sReady[ow] = 1;
+      } else {
+        // timed out: hand these heads to the last split to arrive
+        if (l == 0) *(volatile int32_t*)&sReady[ow] = 2;
+      }
+    }
   }
-  if constexpr (STAGE) {
-    // the staged heads (1 KB each, contiguous in the output) go out 16 bytes
-    // a lane; heads past q_n are not written
-    wait_lgkm0();
-    uint4 rowv[16 * HB];
+
+  if (!owned_here) {
+    // store this split's partial (bf16, in the lanes' fragment order:
+    // instruction j of a wave writes 1 KB contiguously), count in; the last
+    // to arrive merges every split's partial of these heads
 #pragma unroll
-    for (int i = 0; i < 16 * HB; ++i) rowv[i] = *(const uint4*)(stg + i * kStgRow + 16 * l);
+    for (int hb = 0; hb < HB; ++hb) {
+      const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16 * HB; ++i)
-      if (h0 + i < a.qn) *(uint4*)(a.out + ((int64_t)row * a.qn + h0 + i) * 512 + 8 * l) = rowv[i];
+      for (int j = 0; j < 16; ++j) {
+        uint4 pk;
+        pk.x = (uint32_t)to16<HALF>(o[hb][2 * j][0] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][1] * inv) << 16);
+        pk.y = (uint32_t)to16<HALF>(o[hb][2 * j][2] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][3] * inv) << 16);
+        pk.z = (uint32_t)to16<HALF>(o[hb][2 * j + 1][0] * inv) |
+               ((uint32_t)to16<HALF>(o[hb][2 * j + 1][1] * inv) << 16);
+        pk.w = (uint32_t)to16<HALF>(o[hb][2 * j + 1][2] * inv) |
+               ((uint32_t)to16<HALF>(o[hb][2 * j + 1][3] * inv) << 16);
+        const u32x4 d = {pk.x, pk.y, pk.z, pk.w};
+        __builtin_amdgcn_raw_buffer_store_b128(d, rs, wave_off + ((hb * 16 + j) * 64 + l) * 16, 0, kSc1);
+      }
+      if (g == 0)
+        st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
+    }
+    drain_vmem();                                   // this wave's partial is stored
+    // Arrival is counted per (row, head group, wave): the last of the
+    // splits' waves for these 16 heads merges them (unless their owner
+    // does), so the merges of one row spread over the splits' workgroups
+    // and no workgroup barrier is needed.
+    int last = 0;
+    if (l == 0)
+      last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+    if (__builtin_amdgcn_readfirstlane(last)) {
+      if (l == 0)                                   // ready for the next call
+        __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merge_last();
+    }
+  }
+
+  if constexpr (!PK) {
+    if (own_mode) {
+      // share of the owned heads' merge: fragment j (head t, value columns
+      // [32 j, 32 j + 32)) of owned wave ow goes to head-holding wave
+      // j mod n_on; weights and normalisers come from the owner
+#pragma unroll 1
+      for (int ow = 0; ow < n_own; ++ow) {
+        int st;
+        while ((st = *(volatile int32_t*)&sReady[ow]) == 0) __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_readfirstlane(st) != 1) continue;   // handed off
+        const int wo = split + ow * nsplit;                      // the owned wave
+        const int ho = (hg * a.bpg + wo) * HPW + t;
+        const float inv = sInv[ow][t];
+        uint16_t* op = a.out + ((int64_t)row * a.qn + (ho < a.qn ? ho : 0)) * 512 + 4 * g;
+#pragma unroll 1
+        for (int j = w; j < 16; j += n_on) {
+          float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+          for (int sp = 0; sp < nsplit; ++sp) {
+            const float ws = sWs[ow][sp][t];
+            const uint4 v = lds_ld16(slot_addr(ow * nsplit + sp) + j * 1024 + 16 * l);
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[2 * e] = __builtin_fmaf(ws, lo16<HALF>(u[e]), acc[2 * e]);
+              acc[2 * e + 1] = __builtin_fmaf(ws, hi16<HALF>(u[e]), acc[2 * e + 1]);
+            }
+          }
+          if (ho < a.qn) {
+            uint2 p0, p1;
+            p0.x = (uint32_t)to16<HALF>(acc[0] * inv) | ((uint32_t)to16<HALF>(acc[1] * inv) << 16);
+            p0.y = (uint32_t)to16<HALF>(acc[2] * inv) | ((uint32_t)to16<HALF>(acc[3] * inv) << 16);
+            p1.x = (uint32_t)to16<HALF>(acc[4] * inv) | ((uint32_t)to16<HALF>(acc[5] * inv) << 16);
+            p1.y = (uint32_t)to16<HALF>(acc[6] * inv) | ((uint32_t)to16<HALF>(acc[7] * inv) << 16);
+            *(uint2*)(op + 16 * (2 * j)) = p0;
+            *(uint2*)(op + 16 * (2 * j + 1)) = p1;
+          }
+        }
+      }
+    }
   }
 }
 
@@ -1330,6 +1545,8 @@ __global__ __launch_bounds__(256) void resolve_kernel(FwdArgs a) {
 // launchers
 // ---------------------------------------------------------------------------
 
+constexpr int kMaxDevices = 64;
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   const int threads = 128;
   const int blocks = (a.p.q_t + threads - 1) / threads;
@@ -1337,14 +1554,40 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Workgroups of this kernel the current device holds at once (cached per
+// device and kernel; 0 if the runtime cannot tell).
 template <int NW, int DQK, int VMODE, int FMT>
-static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s, hipEvent_t t0,
-                               hipEvent_t t1) {
+static int64_t resident_capacity() {
+  static std::atomic<int64_t> cap[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int64_t c = cap[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&fwd_kernel<NW, 1, DQK, VMODE, FMT>), NW * 64,
+            0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    c = (int64_t)per_cu * cus;
+    cap[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+template <int NW, int DQK, int VMODE, int FMT>
+static hipError_t launch_fwd_t(const FwdArgs& a, int groups, int merge_wait_us, hipStream_t s,
+                               hipEvent_t t0, hipEvent_t t1) {
   FwdArgs b = a;
   b.groups = groups;
   if (b.bpg < 1 || b.bpg > NW) return hipErrorInvalidConfiguration;
   const int64_t blocks = (int64_t)(a.q_t + 7) / 8 * 8 * a.max_splits * groups;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // an owning wave may wait for the other splits of its row only when every
+  // workgroup of the launch is resident at once (s_memrealtime: 100 MHz)
+  b.merge_wait_ticks = 0;
+  if (merge_wait_us > 0 && blocks <= resident_capacity<NW, DQK, VMODE, FMT>())
+    b.merge_wait_ticks = merge_wait_us * 100;
   if (t0 || t1)   // events that the dispatch itself stamps at the kernel's start and end
     hipExtLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks),
                           dim3(NW * 64), 0, s, t0, t1, 0, b);
@@ -1357,28 +1600,28 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int groups, hipStream_t s, hipE
 // Eight waves per workgroup for bf16 rows; four for packed rows, whose
 // decode needs more registers per wave.
 hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
-                          hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+                          int mw, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   switch (fmt) {
     case SFMLA_KV_INT8_PACKED:
       if (nw != 4) return hipErrorInvalidConfiguration;
-      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1)
-                        : launch_fwd_t<4, 576, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1);
+      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_INT8_PACKED>(a, groups, mw, s, t0, t1)
+                        : launch_fwd_t<4, 576, 0, SFMLA_KV_INT8_PACKED>(a, groups, mw, s, t0, t1);
     case SFMLA_KV_FP8_E4M3_PACKED:
       if (nw != 4) return hipErrorInvalidConfiguration;
-      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1)
-                        : launch_fwd_t<4, 576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1);
+      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, mw, s, t0, t1)
+                        : launch_fwd_t<4, 576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, mw, s, t0, t1);
     case SFMLA_KV_FP16:
       if (nw != 8) return hipErrorInvalidConfiguration;
-      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
-                                   : launch_fwd_t<8, 512, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
-      return vmode ? launch_fwd_t<8, 576, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
-                   : launch_fwd_t<8, 576, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
+      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1)
+                                   : launch_fwd_t<8, 512, 0, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1);
+      return vmode ? launch_fwd_t<8, 576, 1, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1)
+                   : launch_fwd_t<8, 576, 0, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1);
     default:
       if (nw != 8) return hipErrorInvalidConfiguration;
-      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, 0>(a, groups, s, t0, t1)
-                                   : launch_fwd_t<8, 512, 0, 0>(a, groups, s, t0, t1);
-      return vmode ? launch_fwd_t<8, 576, 1, 0>(a, groups, s, t0, t1)
-                   : launch_fwd_t<8, 576, 0, 0>(a, groups, s, t0, t1);
+      if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, 0>(a, groups, mw, s, t0, t1)
+                                   : launch_fwd_t<8, 512, 0, 0>(a, groups, mw, s, t0, t1);
+      return vmode ? launch_fwd_t<8, 576, 1, 0>(a, groups, mw, s, t0, t1)
+                   : launch_fwd_t<8, 576, 0, 0>(a, groups, mw, s, t0, t1);
   }
 }
 
@@ -1393,7 +1636,6 @@ hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt,
 static __device__ __align__(256) char scratch[kStaticWorkspaceBytes];
 
 namespace {
-constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 }  // namespace
 

