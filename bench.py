@@ -88,6 +88,63 @@ def row_bytes(P) -> tuple:
     return b, 2 * (d_qk + 512)
 
 
+def recipe_rows(P):
+    """Rows each query row of a workload attends to, counted here from how
+    the workload is built (not by the library's resolver): queries sit at
+    the last positions of their sequence (query i of q_len at position
+    len - q_len + i); TopK entries count where they are >= 0 and (causal
+    mode) their token is at or before the position; windows are (win_left,
+    win_right) around the position clipped to the sequence; compressed rows
+    are the TopK entries a position has completed, or all it has completed
+    ((p + 1) // ratio).  The CPU tests check it against the oracle's lists
+    on every benchmark workload's recipe."""
+    import numpy as np
+    p = P.params
+    a = P.arrays
+    B = int(p["batch_size"])
+    if p["layout_q"] == "BSND":
+        q_lens = [int(p["q_s"])] * B
+    else:
+        q_lens = np.diff(a["cu_seqlens_q"]).astype(int).tolist()
+
+    def lens(side):
+        su = a.get("seqused_%s_kv" % side)
+        if su is not None:
+            return [int(x) for x in su]
+        cu = a.get("cu_seqlens_%s_kv" % side)
+        if cu is not None:
+            return np.diff(cu).astype(int).tolist()
+        return [int(p["%s_kv_s" % side])] * B
+
+    ori = lens("ori")
+    cmp_ = lens("cmp") if p["has_cmp_kv"] else [0] * B
+    out = []
+    row = 0
+    for b in range(B):
+        for i in range(q_lens[b]):
+            pos = ori[b] - q_lens[b] + i
+            if p["ori_topk"]:
+                sbs = int(p.get("sparse_block_size", 1))
+                ent = np.asarray(a["ori_sparse_indices"][row, 0])
+                ent = ent[ent >= 0].astype(np.int64)
+                tok = (ent[:, None] * sbs + np.arange(sbs)[None, :]).ravel()
+                n = int((tok <= pos).sum()) if p["ori_mask_mode"] == 3 else int((tok < ori[b]).sum())
+            else:
+                lo = 0 if p["ori_win_left"] < 0 else max(0, pos - p["ori_win_left"])
+                hi = ori[b] - 1 if p["ori_win_right"] < 0 else min(ori[b] - 1, pos + p["ori_win_right"])
+                n = max(0, hi - lo + 1)
+            if p["has_cmp_kv"]:
+                vis = min(cmp_[b], (pos + 1) // int(p["cmp_ratio"]))
+                if p["cmp_topk"]:
+                    ent = np.asarray(a["cmp_sparse_indices"][row, 0])
+                    n += int(((ent >= 0) & (ent < vis)).sum())
+                else:
+                    n += vis
+            out.append(n)
+            row += 1
+    return np.asarray(out, dtype=np.int64)
+
+
 def kernel_name(P) -> str:
     """The forward kernel (one template for every KV format)."""
     return "fwd_kernel"
@@ -156,8 +213,17 @@ def cpu_baseline(P, flops_per_row, bytes_per_row, budget_s=10.0):
     dt = time.perf_counter() - t0
     fl = float(np.sum([flops_per_row[r] for r in done]))
     by = float(np.sum([bytes_per_row[r] for r in done]))
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "nproc": os.cpu_count(), "cpu_model": model,
+            "threads": "numpy float64 oracle; %d BLAS threads (threadpoolctl)" % threads,
             "sample": "%d query-row calls over the %d query rows (all heads), %.1f s; "
                       "%.3f GB/s gathered KV" % (len(done), len(rows), dt, by / dt / 1e9)}
 
@@ -172,7 +238,7 @@ def profile_commands(outdir: str, workload: str) -> list:
     and one for the MFMA counters (rocprofv3's derived MfmaUtil, MFMA busy
     cycles over active cycles of all SIMDs, and MfmaFlopsBF16 / F16, the
     MFMA operations issued)."""
-    b = "python3 bench.py --workload %s --no-cpu-baseline" % workload
+    b = "python3 bench.py --workload %s --no-cpu-baseline --no-sub-configs" % workload
     return [
         "rocprofv3 --kernel-trace --stats --output-format csv -d %s/trace -o trace -- %s"
         % (outdir, b),
@@ -298,6 +364,8 @@ def main():
     ap.add_argument("--merge-wait-us", type=int, default=0,
                     help="sfmla_params.merge_wait_us (0: the library's rule; -1: the last "
                          "split to arrive merges)")
+    ap.add_argument("--no-sub-configs", action="store_true",
+                    help="time only --workload (by default the other configurations follow it)")
     ap.add_argument("--split-rows", type=int, default=0,
                     help="sfmla_params.split_rows (0: the library's rule)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -323,7 +391,6 @@ def main():
     import numpy as np
     import torch
 
-    import sparse_shared_kv_amd as s
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -332,32 +399,123 @@ def main():
 
     log("[bench] building workload", args.workload)
     P = synth.make_workload(args.workload)
+    m = measure(P, args, dev, args.steps, args.warmup, args.settle_ms, args.time_every,
+                args.replicas)
+    rb, fl_row = row_bytes(P)
+    qn = int(P.params["num_heads_q"])
+    kern = kernel_name(P)
+    traffic = read_traffic(kern, args.workload)
+    mfma = read_mfma(kern, args.workload)
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: %d MiB device copy" % args.copy_probe_mb)
+
+    rl = m["roofline"]
+    result = {
+        "metric": "decode TFLOP/s + gathered-KV HBM GB/s vs roofline, q_n=128 topk=2048",
+        "value": round(m["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "settle": {"ms": round(m["settle_ms"], 1), "steps": m["settle_steps"]},
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": P.params["kv_dtype"],
+        "data": "synthetic (seeded; %s)" % P.recipe,
+        "config": {"workload": args.workload, "description": DESCR[args.workload],
+                   "query_rows": int(P.query_rows), "q_n": qn,
+                   "d_qk": 512 + int(P.params["rope_head_dim"]), "d_v": 512,
+                   "rows_per_step": m["rows_per_step"][0], "index_replicas": m["nrep"],
+                   "rows_counted_by": "bench.recipe_rows (the workload's construction)"},
+        "gathered_kv_gbps": round(m["gbps"], 2),
+        "hbm_frac": round(m["gbps"] / HBM_PEAK_GBPS, 4),
+        "mfma_frac": round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernel_ms": {"plan": round(m["plan_ms"], 5), "forward": round(m["forward_ms"], 5),
+                      "empty_event_bracket": round(m["empty_ms"], 5)},
+        "roofline": dict(rl, kernel="sfmla::" + kern,
+                         traffic=None if traffic is None else round(traffic, 0),
+                         bytes_per_row=rb, flops_per_row_head=fl_row,
+                         # rocprofv3 MfmaUtil of the same kernel source (profiles/), or null
+                         mfma_util_pct=None if mfma is None else mfma["util_pct"],
+                         mfma_flops_issued=None if mfma is None else round(mfma["flops_issued"], 0)),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        c = m["counts"]
+        result["cpu_baseline"] = cpu_baseline(P, c * fl_row * qn, c * rb)
+    if not args.no_sub_configs:
+        # the other configurations, each timed the same way on fewer steps
+        subs = {}
+        for name in SUB_CONFIGS:
+            if name == args.workload:
+                continue
+            log("[bench] sub-config", name)
+            Q = synth.make_workload(name)
+            sm = measure(Q, args, dev, 100, 10, 100.0, 4, args.replicas)
+            subs[name] = {"what": SUB_CONFIGS[name], "description": DESCR[name],
+                          "forward_us": round(sm["forward_ms"] * 1e3, 2),
+                          "ms_per_step": round(sm["ms_per_step"], 5),
+                          "tflops_per_step": round(sm["tflops"], 3),
+                          "gathered_kv_gbps_per_step": round(sm["gbps"], 2),
+                          "rows_per_step": sm["rows_per_step"][0],
+                          "roofline": sm["roofline"]}
+            del Q
+            torch.cuda.empty_cache()
+        result["sub_configs"] = subs
+    print(json.dumps(result), flush=True)
+
+
+# The other configurations of the measured set (timed after the headline in
+# the same run), with what each stands for.
+SUB_CONFIGS = {
+    "swa_decode": "c1 SWA decode",
+    "csa_decode_paged": "c2 CSA paged decode",
+    "hca_varlen": "c3 HCA varlen decode",
+    "c8_packed_int8": "c5 packed INT8 KV",
+    "c8_packed_fp8": "c5 packed FP8-E4M3 KV",
+    "c8_packed_int8_q32": "c5 shapes, 32 query tokens per sequence (throughput mode)",
+    "hca_varlen_q32": "c3 shapes, 32 query tokens per sequence (throughput mode)",
+    "csa_prefill": "prefill: the SparseAttnSharedkv call example's shapes",
+}
+
+
+def measure(P, args, dev, steps, warmup, settle_ms, time_every, replicas):
+    """Time whole steps (plan + forward) of one workload; the forward of
+    every time_every-th step is stamped by its own dispatch.  Inputs are
+    resident on the device first; the TopK index set rotates through
+    `replicas` independently drawn sets."""
+    import numpy as np
+    import torch
+
+    import sparse_shared_kv_amd as s
+    import synth
+
     spec = dict(P.params, merge_wait_us=args.merge_wait_us, split_rows=args.split_rows)
     call = s.Call(spec, P.arrays, device=dev)
-    reps = synth.index_replicas(P, args.replicas - 1) if args.replicas > 1 else []
-    idx_sets = []
+    reps = synth.index_replicas(P, replicas - 1) if replicas > 1 else []
+    idx_sets, counts_all = [], [recipe_rows(P)]
     if reps:
         name = reps[0][0]
         idx_sets = [call.d[name]] + [torch.from_numpy(a).to(dev) for _, a in reps]
-    log("[bench] index replicas:", len(idx_sets) or 1)
+        for _, arr in reps:
+            counts_all.append(recipe_rows(synth.Problem(P.name, P.seed, P.params,
+                                                        dict(P.arrays, **{name: arr}))))
     idx_ptrs = [t.data_ptr() for t in idx_sets]
-
-    # algorithmic work: resolved rows per query row (from the library's resolver)
+    nrep = max(1, len(idx_sets))
     rb, fl_row = row_bytes(P)
     qn = int(P.params["num_heads_q"])
-    counts_all = []
-    for k in range(max(1, len(idx_sets))):
-        if idx_sets:
-            setattr(call.tensors, reps[0][0], idx_ptrs[k])
-        call.plan()
-        _, counts = call.resolve(1)
-        counts_all.append(counts.cpu().numpy().astype(np.int64))
-    torch.cuda.synchronize()
     rows_per_step = [int(c.sum()) for c in counts_all]
     flops_step = [n * fl_row * qn for n in rows_per_step]
     bytes_step = [n * rb for n in rows_per_step]
-    nrep = max(1, len(idx_sets))
-
     stream = torch.cuda.current_stream()
 
     def select(k):
@@ -367,7 +525,7 @@ def main():
     # clock settle: the first ~150 back-to-back steps on an idle GPU run
     # ~10 % slower than the steady state, whatever the warm-up count
     settle_steps, t_settle = 0, time.perf_counter()
-    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
         for k in range(25):
             select(k)
             call.plan(stream)
@@ -375,7 +533,7 @@ def main():
         settle_steps += 25
         torch.cuda.synchronize()
     settle_ms = (time.perf_counter() - t_settle) * 1e3
-    for k in range(args.warmup):
+    for k in range(warmup):
         select(k)
         call.plan(stream)
         call.forward(stream)
@@ -388,15 +546,15 @@ def main():
     # to the measured duration, and even the dispatch-stamped pair delays the
     # next kernel by ~6 us (rocprofv3 kernel trace), so only a sample of the
     # steps carries it.
-    every = max(1, args.time_every)
+    every = max(1, time_every)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(0, args.steps, every)]
+          for _ in range(0, steps, every)]
     for a, b in ev:                     # create the events (a first record)
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         select(k)
         call.plan(stream)
         if k % every == 0:
@@ -420,78 +578,32 @@ def main():
         e[2].record(stream)
         e[3].record(stream)
     torch.cuda.synchronize()
-    plan_ms = [e[0].elapsed_time(e[1]) for e in pe]
-    empty_ms = [e[2].elapsed_time(e[3]) for e in pe]
+    plan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pe]))
+    empty_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in pe]))
 
-    ms_per_step = wall * 1e3 / args.steps
-    tot_flops = sum(flops_step[k % nrep] for k in range(args.steps))
-    tot_bytes = sum(bytes_step[k % nrep] for k in range(args.steps))
-    tflops = tot_flops / wall / 1e12
-    gbps = tot_bytes / wall / 1e9
+    tot_flops = sum(flops_step[k % nrep] for k in range(steps))
+    tot_bytes = sum(bytes_step[k % nrep] for k in range(steps))
     fwd_avg_s = float(np.mean(fwd_ms)) / 1e3
-    fwd_bytes = float(np.mean([bytes_step[k % nrep] for k in range(0, args.steps, every)]))
-    fwd_flops = float(np.mean([flops_step[k % nrep] for k in range(0, args.steps, every)]))
-    intensity = fwd_flops / fwd_bytes
-    hbm_bound = intensity < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    fwd_bytes = float(np.mean([bytes_step[k % nrep] for k in range(0, steps, every)]))
+    fwd_flops = float(np.mean([flops_step[k % nrep] for k in range(0, steps, every)]))
+    hbm_bound = fwd_flops / fwd_bytes < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if hbm_bound:
         achieved, peak, unit = fwd_bytes / fwd_avg_s / 1e9, HBM_PEAK_GBPS, "GB/s"
     else:
         achieved, peak, unit = fwd_flops / fwd_avg_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    kern = kernel_name(P)
-    traffic = read_traffic(kern, args.workload)
-    mfma = read_mfma(kern, args.workload)
-
-    if args.copy_probe_mb:
-        n = args.copy_probe_mb * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log("[bench] copy probe: %d MiB device copy" % args.copy_probe_mb)
-
-    result = {
-        "metric": "decode TFLOP/s + gathered-KV HBM GB/s vs roofline, q_n=128 topk=2048",
-        "value": round(tflops, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps},
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": P.params["kv_dtype"],
-        "data": "synthetic (seeded; %s)" % P.recipe,
-        "config": {"workload": args.workload, "description": DESCR[args.workload],
-                   "query_rows": int(P.query_rows), "q_n": qn,
-                   "d_qk": 512 + int(P.params["rope_head_dim"]), "d_v": 512,
-                   "rows_per_step": rows_per_step[0], "index_replicas": nrep},
-        "gathered_kv_gbps": round(gbps, 2),
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "kernel_ms": {"plan": round(float(np.mean(plan_ms)), 5),
-                      "forward": round(float(np.mean(fwd_ms)), 5),
-                      "empty_event_bracket": round(float(np.mean(empty_ms)), 5)},
-        "roofline": {"kernel": "sfmla::" + kern,
-                     "bound": "hbm" if hbm_bound else "mfma",
-                     "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4),
-                     "traffic": None if traffic is None else round(traffic, 0),
+    del call
+    return {
+        "tflops": tot_flops / wall / 1e12, "gbps": tot_bytes / wall / 1e9,
+        "ms_per_step": wall * 1e3 / steps, "forward_ms": float(np.mean(fwd_ms)),
+        "plan_ms": plan_ms, "empty_ms": empty_ms, "settle_ms": settle_ms,
+        "settle_steps": settle_steps, "rows_per_step": rows_per_step, "nrep": nrep,
+        "counts": counts_all[0],
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic_bytes_per_launch": round(fwd_bytes, 0),
                      "algorithmic_flops_per_launch": round(fwd_flops, 0),
-                     "bytes_per_row": rb, "flops_per_row_head": fl_row,
-                     "timed_launches": len(fwd_ms),
-                     # rocprofv3 MfmaUtil of the same kernel source (profiles/), or null
-                     "mfma_util_pct": None if mfma is None else mfma["util_pct"],
-                     "mfma_flops_issued": None if mfma is None else round(mfma["flops_issued"], 0)},
+                     "timed_launches": len(fwd_ms)},
     }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle) ...")
-        c = counts_all[0]
-        result["cpu_baseline"] = cpu_baseline(P, c * fl_row * qn, c * rb)
-    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -71,6 +71,8 @@ uint32_t fingerprint(const sfmla_params& p) {
 
 int64_t max_list(const sfmla_params& p);
 int max_splits(const sfmla_params& p);
+// heads each wave holds (one 16-head MFMA block)
+int heads_per_wave(const sfmla_params&) { return 16; }
 void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg);
 
 sfmla_status validate(const sfmla_params* pp) {
@@ -165,7 +167,7 @@ sfmla_status validate(const sfmla_params* pp) {
           (long long)4096 * sfmla::kMaxSplitRows);
   int nw, groups, bpg;
   choose_groups(p, &nw, &groups, &bpg);
-  const int64_t part_bytes = (int64_t)max_splits(p) * groups * nw * 16 * 512 * 2;
+  const int64_t part_bytes = (int64_t)max_splits(p) * groups * nw * heads_per_wave(p) * 512 * 2;
   REQUIRE(part_bytes < ((int64_t)1 << 31),
           "split partials of one query row would take %lld bytes (limit 2^31)",
           (long long)part_bytes);
@@ -251,7 +253,7 @@ WsLayout workspace_layout(const sfmla_params& p) {
   if (s <= 1) return L;
   int nw, groups, bpg;
   choose_groups(p, &nw, &groups, &bpg);
-  L.heads = groups * nw * 16;
+  L.heads = groups * nw * heads_per_wave(p);
   const size_t slots = (size_t)p.q_t * s * L.heads;
   L.o_bytes = (slots * 512 * 2 + 255) / 256 * 256;
   L.lse_bytes = (slots * sizeof(float) + 255) / 256 * 256;
@@ -270,7 +272,8 @@ size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total
 // never changes a result: every head is computed the same way in any group.
 void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
   const int64_t units = (int64_t)p.q_t * max_splits(p);
-  const int blocks = (p.num_heads_q + 15) / 16;        // 16-head blocks
+  const int hpw = heads_per_wave(p);
+  const int blocks = (p.num_heads_q + hpw - 1) / hpw;  // head blocks of one wave each
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int wmax = packed ? 4 : 8;                     // packed rows: more registers per wave
   *nw = wmax;

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "sfmla_internal.h"
@@ -869,7 +870,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) { m_run[hb] = kNegInf; l_run[hb] = 0.f; }
   bf16x8 pb[HB];
-  bf16x8 pbt[PK ? 4 : 1][HB];     // packed: P times the rows' scales, per 128 value columns
+  // packed rows: the probabilities in fp32 (this lane's 8 rows), scaled by
+  // each 128-column tile's row scales just before that tile's PV products
+  float pj32[PK ? HB : 1][8];
 
   // ---- S^T = K Q^T, online softmax -> pb (M = 16 rows, N = 16 heads per MFMA).
   // The operands of the next PF k-steps are in flight while step ks
@@ -882,56 +885,73 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       valid[i] = sRow[tbase + 4 * g + i] != kNoRow;
       valid[4 + i] = sRow[tbase + 16 + 4 * g + i] != kNoRow;
     }
-    // packed: the scales of this lane's rows (4g+i and 16+4g+i), per tile
-    f32x4 sc[PK ? 4 : 1][2];
-    if constexpr (PK) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[j][0] = *(const f32x4*)(sScale + j * T + 4 * g);
-        sc[j][1] = *(const f32x4*)(sScale + j * T + 16 + 4 * g);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 s[HB][2], sp[HB][2];
+    f32x4 s[HB][2];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const char* kp0 = sK + t * RS + 16 * g;
-    const char* kp1 = kp0 + 16 * RS;
-    auto kload = [&](int ks, bf16x8& k0v, bf16x8& k1v) {
-      if (!C::ROPE || ks < 16) {
-        k0v = *(const bf16x8*)(kp0 + 64 * ks);
-        k1v = *(const bf16x8*)(kp1 + 64 * ks);
-      } else {
-        const int c = 4 * (ks - 16) + g;
-        k0v = *(const bf16x8*)(sR + t * 128 + 16 * (c ^ ((t >> 1) & 7)));
-        k1v = *(const bf16x8*)(sR + (16 + t) * 128 + 16 * (c ^ (((16 + t) >> 1) & 7)));
-      }
-    };
-    constexpr int PF = NW * HB >= 8 ? (C::ROPE ? 1 : 2) : 4;   // 2 waves/SIMD: fewer registers
-    bf16x8 kb[PF][2];
+    if constexpr (PK) {
+      // Packed rows: exact scaling, one partial product per 128-column scale
+      // tile, taken one 16-row half of the tile at a time (the partial sums,
+      // K operands and row scales of one half are live at once).
 #pragma unroll
-    for (int i = 0; i < PF; ++i) kload(i, kb[i][0], kb[i][1]);
+      for (int half = 0; half < 2; ++half) {
+        const char* kp = sK + (16 * half + t) * RS + 16 * g;
+        auto kload = [&](int ks) -> bf16x8 {
+          if (!C::ROPE || ks < 16) return *(const bf16x8*)(kp + 64 * ks);
+          const int c = 4 * (ks - 16) + g, r = 16 * half + t;
+          return *(const bf16x8*)(sR + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
+        };
+        constexpr int PF = NW * HB >= 8 ? (C::ROPE ? 1 : 2) : 4;
+        bf16x8 kb[PF];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 k0v = kb[ks % PF][0], k1v = kb[ks % PF][1];
+        for (int i = 0; i < PF; ++i) kb[i] = kload(i);
+        f32x4 sp[HB], scq;
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        if (PK && ks < 16) {
-          // exact scaling: one partial product per 128-column scale tile
-          const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-          sp[hb][0] = mfma16<HALF>(k0v, qreg[hb][ks], ks % 4 ? sp[hb][0] : z);
-          sp[hb][1] = mfma16<HALF>(k1v, qreg[hb][ks], ks % 4 ? sp[hb][1] : z);
-          if (ks % 4 == 3) {
-            s[hb][0] += sp[hb][0] * sc[PK ? ks / 4 : 0][0];
-            s[hb][1] += sp[hb][1] * sc[PK ? ks / 4 : 0][1];
+        for (int ks = 0; ks < NKS; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 kv = kb[ks % PF];
+          if (ks < 16 && ks % 4 == 0)   // this lane's rows' scales of the tile
+            scq = *(const f32x4*)(sScale + (ks / 4) * T + 16 * half + 4 * g);
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            if (ks < 16) {
+              const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+              sp[hb] = mfma16<HALF>(kv, qreg[hb][ks], ks % 4 ? sp[hb] : z);
+              if (ks % 4 == 3) s[hb][half] += sp[hb] * scq;
+            } else {
+              s[hb][half] = mfma16<HALF>(kv, qreg[hb][ks], s[hb][half]);
+            }
           }
+          if (ks + PF < NKS) kb[ks % PF] = kload(ks + PF);
+        }
+      }
+    } else {
+      const char* kp0 = sK + t * RS + 16 * g;
+      const char* kp1 = kp0 + 16 * RS;
+      auto kload = [&](int ks, bf16x8& k0v, bf16x8& k1v) {
+        if (!C::ROPE || ks < 16) {
+          k0v = *(const bf16x8*)(kp0 + 64 * ks);
+          k1v = *(const bf16x8*)(kp1 + 64 * ks);
         } else {
+          const int c = 4 * (ks - 16) + g;
+          k0v = *(const bf16x8*)(sR + t * 128 + 16 * (c ^ ((t >> 1) & 7)));
+          k1v = *(const bf16x8*)(sR + (16 + t) * 128 + 16 * (c ^ (((16 + t) >> 1) & 7)));
+        }
+      };
+      constexpr int PF = NW * HB >= 8 ? (C::ROPE ? 1 : 2) : 4;   // 2 waves/SIMD: fewer registers
+      bf16x8 kb[PF][2];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) kload(i, kb[i][0], kb[i][1]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 k0v = kb[ks % PF][0], k1v = kb[ks % PF][1];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
           s[hb][0] = mfma16<HALF>(k0v, qreg[hb][ks], s[hb][0]);
           s[hb][1] = mfma16<HALF>(k1v, qreg[hb][ks], s[hb][1]);
         }
+        if (ks + PF < NKS) kload(ks + PF, kb[ks % PF][0], kb[ks % PF][1]);
       }
-      if (ks + PF < NKS) kload(ks + PF, kb[ks % PF][0], kb[ks % PF][1]);
     }
     __builtin_amdgcn_sched_barrier(0);
     // lane holds head t of each block and rows {4g+i, 16+4g+i}
@@ -959,12 +979,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       for (int j = 0; j < 8; ++j) {
         const float pj = __builtin_amdgcn_exp2f(x[j] - m_use);
         psum += pj;
-        if constexpr (PK) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) pbt[u][hb][j] = elem16<HALF>(pj * sc[PK ? u : 0][j >> 2][j & 3]);
-        } else {
-          pb[hb][j] = elem16<HALF>(pj);
-        }
+        if constexpr (PK) pj32[PK ? hb : 0][j] = pj;
+        else pb[hb][j] = elem16<HALF>(pj);
       }
       l_run[hb] = l_run[hb] * alpha[hb] + psum;
     }
@@ -989,14 +1005,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     };
 #pragma unroll
     for (int i = 0; i < PV; ++i) vload(i, vb[i][0], vb[i][1]);
+    bf16x8 pbt[HB];                // packed: P times the rows' scales of tile mb / 8
 #pragma unroll
     for (int mb = 0; mb < 32; ++mb) {
+      if (PK && mb % 8 == 0) {
+        const f32x4 c0 = *(const f32x4*)(sScale + (mb / 8) * T + 4 * g);
+        const f32x4 c1 = *(const f32x4*)(sScale + (mb / 8) * T + 16 + 4 * g);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            pbt[hb][j] = elem16<HALF>(pj32[PK ? hb : 0][j] * (j < 4 ? c0[j] : c1[j - 4]));
+      }
       __builtin_amdgcn_sched_barrier(0);
       const bf16x8 va = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(vb[mb % PV][0], vb[mb % PV][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
-        o[hb][mb] = mfma16<HALF>(va, PK ? pbt[PK ? mb >> 3 : 0][hb] : pb[hb], o[hb][mb]);
+        o[hb][mb] = mfma16<HALF>(va, PK ? pbt[hb] : pb[hb], o[hb][mb]);
       if (mb + PV < 32) vload(mb + PV, vb[mb % PV][0], vb[mb % PV][1]);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1153,8 +1179,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   constexpr int OSLOT = 8;                          // LDS slots of 16 KB
   const int n_on = min(a.bpg, (a.qn - hg * a.bpg * HPW + HPW - 1) / HPW);   // waves with heads
   const int n_own = split < n_on ? (n_on - 1 - split) / nsplit + 1 : 0;    // owned waves here
+  // (only where every wave of the workgroup holds heads, so the shared
+  // merge runs on all SIMDs: with fewer head waves the last split to
+  // arrive merges sooner, measured)
   const bool own_mode = !PK && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
-                        n_own > 0 && n_own * nsplit <= OSLOT;
+                        n_on == NW && n_own > 0 && n_own * nsplit <= OSLOT;
   auto slot_addr = [&](int q) -> uint32_t {          // slot q: two per stage buffer
     const int b = q >> 1;
     const uint32_t base = VMODE ? (b == 0 ? lds_addr(sK0) : b == 1 ? lds_addr(sK1)
@@ -1556,6 +1585,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 
 // Workgroups of this kernel the current device holds at once (cached per
 // device and kernel; 0 if the runtime cannot tell).
+// 16-head blocks each wave holds
+template <int NW, int FMT>
+constexpr int kHeadBlocks = 1;
+
 template <int NW, int DQK, int VMODE, int FMT>
 static int64_t resident_capacity() {
   static std::atomic<int64_t> cap[kMaxDevices];
@@ -1563,16 +1596,22 @@ static int64_t resident_capacity() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   int64_t c = cap[dev].load(std::memory_order_relaxed);
   if (c == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&fwd_kernel<NW, 1, DQK, VMODE, FMT>), NW * 64,
-            0) != hipSuccess ||
+    // the runtime's occupancy, bounded by what the LDS holds (the larger
+    // of the two was seen to over-count for workgroups of ~147 KB of LDS)
+    const void* fn = reinterpret_cast<const void*>(&fwd_kernel<NW, kHeadBlocks<NW, FMT>, DQK, VMODE, FMT>);
+    int per_cu = 0, cus = 0, lds_cu = 0;
+    hipFuncAttributes fa;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NW * 64, 0) != hipSuccess ||
+        hipFuncGetAttributes(&fa, fn) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    c = (int64_t)per_cu * cus;
-    cap[dev].store(c, std::memory_order_relaxed);
+    if (fa.sharedSizeBytes > 0) per_cu = std::min<int>(per_cu, lds_cu / (int)fa.sharedSizeBytes);
+    c = (int64_t)std::max(per_cu, 0) * cus;
+    cap[dev].store(c > 0 ? c : -1, std::memory_order_relaxed);
   }
-  return c;
+  return c > 0 ? c : 0;
 }
 
 template <int NW, int DQK, int VMODE, int FMT>
@@ -1589,10 +1628,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int groups, int merge_wait_us, 
   if (merge_wait_us > 0 && blocks <= resident_capacity<NW, DQK, VMODE, FMT>())
     b.merge_wait_ticks = merge_wait_us * 100;
   if (t0 || t1)   // events that the dispatch itself stamps at the kernel's start and end
-    hipExtLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks),
+    hipExtLaunchKernelGGL((fwd_kernel<NW, kHeadBlocks<NW, FMT>, DQK, VMODE, FMT>), dim3((unsigned)blocks),
                           dim3(NW * 64), 0, s, t0, t1, 0, b);
   else
-    hipLaunchKernelGGL((fwd_kernel<NW, 1, DQK, VMODE, FMT>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((fwd_kernel<NW, kHeadBlocks<NW, FMT>, DQK, VMODE, FMT>), dim3((unsigned)blocks),
                        dim3(NW * 64), 0, s, b);
   return hipGetLastError();
 }

@@ -558,3 +558,4 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
                            else gs.standard_normal(qn)).astype(np.float32)
     return Problem("tiny_%s_%d" % (family, seed), seed, params, arrays,
                    "random tiny %s" % family)
+

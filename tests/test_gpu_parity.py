@@ -515,22 +515,26 @@ def test_lse_off_matches_lse_on_bitwise():
 # ---------------------------------------------------------------------------
 
 MERGE_CASES = [
-    # 4 splits of 512 rows (rope, separate V: the headline's kernel)
+    # owned merges need every wave of the workgroup to hold heads: 128 heads
+    # in one group of 8 head blocks.  4 splits of 512 rows (rope, separate V:
+    # the headline's kernel)
     dict(seed=930, family="sfa", max_kv=4000, topk=2048, num_heads_q=128, rope_head_dim=64,
          separate_v=True, layout_q="TND", layout_kv="PA_BSND", block_size=64, q_lens=[2, 1],
-         batch=2),
-    # 2 and 8 splits; V = K nope (the extra landing buffer), a partial head block
-    dict(seed=931, family="sfa", max_kv=3000, topk=1000, num_heads_q=100, rope_head_dim=0,
-         separate_v=False, split_rows=512),
-    dict(seed=932, family="sfa", max_kv=3000, topk=2000, num_heads_q=64, rope_head_dim=64,
-         separate_v=False, split_rows=256),
-    # 4 splits over 4 head groups of 32 heads (owned waves per workgroup: 1 of 2)
+         batch=2, head_blocks_per_group=8),
+    # 2 and 8 splits with V = K nope (the extra landing buffer)
+    dict(seed=931, family="sfa", max_kv=3000, topk=1000, num_heads_q=128, rope_head_dim=0,
+         separate_v=False, split_rows=512, head_blocks_per_group=8),
+    dict(seed=932, family="sfa", max_kv=3000, topk=2000, num_heads_q=128, rope_head_dim=64,
+         separate_v=False, split_rows=256, head_blocks_per_group=8),
+    # 3 splits: splits 0 and 1 own too many waves for the landing slots (the
+    # last to arrive merges those heads), split 2 owns its two; float16, sinks
+    dict(seed=933, family="csa", max_kv=2000, topk=700, num_heads_q=128, cmp_ratio=1,
+         kv_dtype="fp16", sinks=True, head_blocks_per_group=8),
+    # not owned: 4 head groups of 32 heads; a partial last head block
     dict(seed=934, family="sfa", max_kv=3000, topk=2048, num_heads_q=128, rope_head_dim=64,
          separate_v=True, head_blocks_per_group=2),
-    # 3 splits (owners hold too few landing slots: the last to arrive merges),
-    # sinks, float16
-    dict(seed=933, family="csa", max_kv=2000, topk=700, num_heads_q=128, cmp_ratio=1,
-         kv_dtype="fp16", sinks=True),
+    dict(seed=935, family="sfa", max_kv=3000, topk=1000, num_heads_q=100, rope_head_dim=0,
+         separate_v=False, split_rows=512, head_blocks_per_group=8),
 ]
 
 
