@@ -368,6 +368,8 @@ def main():
                     help="time only --workload (by default the other configurations follow it)")
     ap.add_argument("--split-rows", type=int, default=0,
                     help="sfmla_params.split_rows (0: the library's rule)")
+    ap.add_argument("--query-tile", type=int, default=0,
+                    help="sfmla_params.query_tile (0: the library's rule; 1: no query tiles)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--profile-commands", metavar="OUTDIR",
@@ -485,6 +487,9 @@ SUB_CONFIGS = {
     "c8_packed_int8_q32": "c5 shapes, 32 query tokens per sequence (throughput mode)",
     "hca_varlen_q32": "c3 shapes, 32 query tokens per sequence (throughput mode)",
     "csa_prefill": "prefill: the SparseAttnSharedkv call example's shapes",
+    "swa_prefill": "prefill, window only (query tiles of 2 rows at 64 heads)",
+    "swa_prefill_h16": "prefill, window only, 16 heads (query tiles of 8 rows)",
+    "hca_prefill": "prefill, window and every visible compressed row (query tiles of 2 rows)",
 }
 
 
@@ -499,7 +504,8 @@ def measure(P, args, dev, steps, warmup, settle_ms, time_every, replicas):
     import sparse_shared_kv_amd as s
     import synth
 
-    spec = dict(P.params, merge_wait_us=args.merge_wait_us, split_rows=args.split_rows)
+    spec = dict(P.params, merge_wait_us=args.merge_wait_us, split_rows=args.split_rows,
+                query_tile=args.query_tile)
     call = s.Call(spec, P.arrays, device=dev)
     reps = synth.index_replicas(P, replicas - 1) if replicas > 1 else []
     idx_sets, counts_all = [], [recipe_rows(P)]

@@ -163,6 +163,26 @@ typedef struct sfmla_params {
    * (used only when every workgroup of the launch is resident at once; on
    * time-out the last to arrive merges).  Every setting gives the same bits. */
   int32_t merge_wait_us;
+  /* Query tiles (0 = the library's rule).  Consecutive query rows of one
+   * sequence share a workgroup: their lists are merged into one union list
+   * that is gathered once, and each row masks the union positions that its
+   * own list does not hold (SparseAttnSharedkv README, 调用说明: prefill with
+   * s1 query tokens per sequence).  Tiles are used where every list is a
+   * rule (window and / or every visible compressed row: ori_topk = cmp_topk
+   * = 0), KV is bf16 or float16, at most 64 heads, and the parameters bound
+   * a tile's union to one split of 2048 rows (window: win_left + win_right +
+   * rows per tile, else max_seqlen_ori_kv; plus max_seqlen_cmp_kv).
+   * The rule tiles 8 / (16-head blocks rounded up to a power of two) rows,
+   * i.e. 2 rows at 64 heads, 8 at 16, when max_seqlen_q >= 16.
+   *   1        never tile;
+   *   2, 4, 8  that many rows per tile (refused where the parameters do not
+   *            allow tiles of that size).
+   * Tiles start at each sequence's first query row, so a row's tile depends
+   * on its own sequence only.  Tiling changes the rounding order (results
+   * stay within the stated tolerances); split_rows, head_blocks_per_group
+   * and merge_wait_us have no effect on a tiled call, which needs no
+   * workspace. */
+  int32_t query_tile;
 } sfmla_params;
 
 /*
@@ -236,7 +256,10 @@ sfmla_status sfmla_metadata_size(const sfmla_params* params, size_t* n_ints);
 /*
  * Build the split plan (sparse_flash_mla_metadata on the API page): per query
  * row its batch, position, resolved window / list extents and split count,
- * plus a fingerprint of `params`.  Reads the length tensors on the device.
+ * plus a fingerprint of `params`; with query tiles (sfmla_params.query_tile)
+ * also the tiles, numbered sequence by sequence with no gaps, each as its
+ * first query row and row count.  Reads the length tensors on the device
+ * (cu_seqlens_q must start at 0, be non-decreasing and end at q_t).
  * `metadata` holds at least sfmla_metadata_size() int32, 16-byte aligned.
  */
 sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* lengths,

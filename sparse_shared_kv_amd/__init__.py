@@ -192,6 +192,7 @@ def make_params(spec: dict, arrays: dict) -> Params:
     p.split_rows = int(g("split_rows", 0))
     p.head_blocks_per_group = int(g("head_blocks_per_group", 0))
     p.merge_wait_us = int(g("merge_wait_us", 0))
+    p.query_tile = int(g("query_tile", 0))
     return p
 
 

@@ -62,7 +62,7 @@ uint32_t fingerprint(const sfmla_params& p) {
       p.cmp_mask_mode, p.ori_win_left, p.ori_win_right, p.has_ori_kv, p.has_cmp_kv,
       p.kv_dtype, p.has_separate_v, p.has_sinks, p.return_softmax_lse, p.has_seqused_q,
       p.has_seqused_ori_kv, p.has_seqused_cmp_kv, p.has_cmp_residual_kv, p.split_rows,
-      p.head_blocks_per_group, p.merge_wait_us};
+      p.head_blocks_per_group, p.merge_wait_us, p.query_tile};
   for (int32_t v : f32) mix(v);
   mix(p.ori_kv_rows);
   mix(p.cmp_kv_rows);
@@ -71,6 +71,8 @@ uint32_t fingerprint(const sfmla_params& p) {
 
 int64_t max_list(const sfmla_params& p);
 int max_splits(const sfmla_params& p);
+int tile_limit(const sfmla_params& p);
+bool tile_eligible(const sfmla_params& p);
 // heads each wave holds (one 16-head MFMA block)
 int heads_per_wave(const sfmla_params&) { return 16; }
 void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg);
@@ -132,6 +134,15 @@ sfmla_status validate(const sfmla_params* pp) {
           "head_blocks_per_group must be 0, 1, 2, 4 or 8");
   REQUIRE(p.merge_wait_us >= -1 && p.merge_wait_us <= 10000,
           "merge_wait_us must be -1, 0 or 1..10000");
+  REQUIRE(p.query_tile == 0 || p.query_tile == 1 || p.query_tile == 2 || p.query_tile == 4 ||
+              p.query_tile == 8,
+          "query_tile must be 0, 1, 2, 4 or 8");
+  if (p.query_tile > 1) {
+    REQUIRE(tile_eligible(p) && p.query_tile <= tile_limit(p),
+            "query_tile %d needs rule lists (ori_topk = cmp_topk = 0), bf16 or float16 KV "
+            "and %d rows x 16-head blocks <= 8",
+            p.query_tile, p.query_tile);
+  }
   REQUIRE(!(p.has_separate_v && p.kv_dtype != SFMLA_KV_BF16 && p.kv_dtype != SFMLA_KV_FP16),
           "a separate V is only supported for bf16 KV (packed V is the dequantised nope)");
   if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.ori_kv_s > 0, "BSND ori_kv needs ori_kv_s > 0");
@@ -227,9 +238,55 @@ int max_splits(const sfmla_params& p) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, 4096));
 }
 
-size_t metadata_ints(const sfmla_params& p) {
+// Query tiles.  Rows per tile that the waves of one workgroup hold: the 16-head
+// blocks of a row, rounded up to a power of two, times the rows fill the 8
+// waves (1: a row's heads need every wave).
+int tile_limit(const sfmla_params& p) {
+  const int blocks = (p.num_heads_q + 15) / 16;
+  int pw = 1;
+  while (pw < blocks) pw *= 2;
+  return 8 / pw;
+}
+
+// Tiles need rule lists (a tile's rows then share most of their rows: the
+// windows of consecutive rows overlap, the visible compressed rows of one
+// row include the earlier row's) and 16-bit rows (the eight-wave kernel).
+bool tile_eligible(const sfmla_params& p) {
+  return (p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_FP16) && p.ori_topk == 0 &&
+         p.cmp_topk == 0 && tile_limit(p) >= 2;
+}
+
+// Query rows per tile of this call (1: no tiles).  By rule: the most the
+// waves hold, where a sequence may be long enough to be a prefill.  Which
+// sequences are tiled is decided on the device from each sequence's own
+// lengths (at least kMinTileQueries valid queries by rule, any number when
+// forced, and a tile's union list within one split).
+int query_tile(const sfmla_params& p) {
+  if (p.query_tile == 1) return 1;
+  if (p.query_tile > 1) return p.query_tile;        // validated
+  if (!tile_eligible(p) || p.max_seqlen_q < sfmla::kMinTileQueries) return 1;
+  return tile_limit(p);
+}
+
+// Tile descriptors of a tiled call: at least the tiles any batch of these
+// parameters has (sum over sequences of ceil(len / tq) <= (q_t + b (tq - 1)) / tq,
+// and at most one per query row), rounded up to a multiple of 8 so that the
+// rows of untiled sequences that follow the tiles in the grid start on XCD 0.
+int64_t tile_bound(const sfmla_params& p) {
+  const int tq = query_tile(p);
+  if (tq <= 1) return 0;
+  const int64_t n = std::min<int64_t>(((int64_t)p.q_t + (int64_t)p.batch_size * (tq - 1)) / tq,
+                                      p.q_t);
+  return (n + 7) / 8 * 8;
+}
+
+size_t tile_off(const sfmla_params& p) {
   return (size_t)sfmla::kHeaderInts +
          (size_t)(sfmla::kRecInts + sfmla::kCounterInts) * (size_t)p.q_t;
+}
+
+size_t metadata_ints(const sfmla_params& p) {
+  return tile_off(p) + (size_t)sfmla::kTileDescInts * (size_t)tile_bound(p);
 }
 
 // Longest wait (us) of a split that merges the partials of its row's other
@@ -271,6 +328,14 @@ size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total
 // more groups, each re-gathering the row's KV (mostly from L2).  The shape
 // never changes a result: every head is computed the same way in any group.
 void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
+  if (query_tile(p) > 1) {
+    // with query tiles, an untiled sequence's rows take every head in one
+    // workgroup (tiles keep the grid full)
+    *nw = 8;
+    *groups = 1;
+    *bpg = 8;
+    return;
+  }
   const int64_t units = (int64_t)p.q_t * max_splits(p);
   const int hpw = heads_per_wave(p);
   const int blocks = (p.num_heads_q + hpw - 1) / hpw;  // head blocks of one wave each
@@ -465,6 +530,10 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
   a.max_splits = max_splits(p);
   a.split_rows = split_rows(p);
   a.split_rows_long = std::max(a.split_rows, sfmla::kMaxSplitRows);
+  a.tq = query_tile(p);
+  a.tile_min_queries = p.query_tile > 1 ? 1 : sfmla::kMinTileQueries;
+  a.tile_bound = (int32_t)tile_bound(p);
+  a.tile_off = (int64_t)tile_off(p);
   hipError_t e = sfmla::launch_plan(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "plan launch: %s", hipGetErrorString(e));
   return ok();
@@ -513,11 +582,22 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
     a.ws_lse = (float*)((char*)workspace + L.o_bytes);
   }
   a.counters = metadata + sfmla::kHeaderInts + (size_t)sfmla::kRecInts * p.q_t;
+  const int dqk = 512 + p.rope_head_dim;
+  const int vmode = p.has_separate_v ? 1 : 0;
+  const int tq = query_tile(p);
+  if (tq > 1) {
+    a.tq = tq;
+    a.nb = (p.num_heads_q + 15) / 16;
+    a.tile_off = (int64_t)tile_off(p);
+    a.tile_units = (int32_t)tile_bound(p);
+    hipError_t e = sfmla::launch_forward_tiled(a, dqk, vmode, p.kv_dtype, (hipStream_t)stream,
+                                               t0, t1);
+    if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   int nw, groups, bpg;
   choose_groups(p, &nw, &groups, &bpg);
   a.bpg = bpg;
-  const int dqk = 512 + p.rope_head_dim;
-  const int vmode = p.has_separate_v ? 1 : 0;
   // the owned split merge waits at most this long for the row's other
   // splits (when the launch's workgroups are all resident at once)
   const int merge_wait_us = p.merge_wait_us == 0 ? kMergeWaitUs : std::max(0, p.merge_wait_us);

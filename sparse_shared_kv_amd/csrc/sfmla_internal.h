@@ -14,6 +14,8 @@ constexpr int kQueriesPerStep = 16;   // queries of a sequence per step of longe
 constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
 constexpr int kCounterInts = 64;   // arrival counters per query row (one per head group x wave)
+constexpr int kMinTileQueries = 16;   // query tiles by rule from this max_seqlen_q on
+constexpr int kTileDescInts = 2;      // per query tile: first query row, row count
 constexpr int32_t kMagic = 0x534d4c41;
 // size of the library-owned split workspace (one static device array per GPU)
 constexpr size_t kStaticWorkspaceBytes = SFMLA_STATIC_WORKSPACE_BYTES;
@@ -22,7 +24,8 @@ constexpr size_t kStaticWorkspaceBytes = SFMLA_STATIC_WORKSPACE_BYTES;
 enum RecField {
   R_B = 0,       // batch index
   R_I,           // index of the query row inside its batch
-  R_VALID,       // 1 if i < seqused_q (else the row attends to nothing)
+  R_VALID,       // bit 0: i < seqused_q (else the row attends to nothing);
+                 // bit 1: the row's sequence goes in query tiles
   R_P,           // original-KV position p = ori_len - q_used + i
   R_PC,          // compressed-side position cmp_len*ratio + residual - q_used + i
   R_ORI_LO,      // first row of the window rule
@@ -46,6 +49,10 @@ struct PlanArgs {
   int32_t max_splits;
   int32_t split_rows;               // KV rows per split (multiple of the tile, <= kMaxSplitRows)
   int32_t split_rows_long;          // the longest split of a row of a sequence with many queries
+  int32_t tq;                       // query rows per tile (1: no tiles)
+  int32_t tile_min_queries;         // valid queries from which a sequence is tiled
+  int32_t tile_bound;               // tile descriptors written
+  int64_t tile_off;                 // int offset of the descriptors in meta
 };
 
 struct FwdArgs {
@@ -59,6 +66,11 @@ struct FwdArgs {
   int32_t bpg;                      // 16-head blocks per head group (<= waves; spare waves only load)
   int32_t split_rows;               // list positions per split of a short-query row
   int32_t merge_wait_ticks;         // owned-merge wait bound (s_memrealtime ticks; 0: none)
+  int32_t tq;                       // query rows per tile (tiled launch)
+  int32_t nb;                       // 16-head blocks per query row (tiled launch)
+  int32_t tile_units;               // tiled launch: workgroups of the tiles (a multiple of 8);
+                                    // the rows of untiled sequences follow
+  int64_t tile_off;                 // int offset of the tile descriptors in meta
   uint32_t fingerprint;
   float scale_log2;                 // softmax_scale * log2(e)
   const int32_t* meta;
@@ -106,6 +118,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
                           int merge_wait_us, hipStream_t s, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);
+// launch with query tiles: a.tile_units workgroups for the tiles (one each,
+// a.tq rows), then one per (split, row) of the rows of untiled sequences
+hipError_t launch_forward_tiled(const FwdArgs& a, int dqk, int vmode, int fmt, hipStream_t s,
+                                hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_debug_resolve(const FwdArgs& a, hipStream_t s);
 // device address of the library-owned split workspace on the current device

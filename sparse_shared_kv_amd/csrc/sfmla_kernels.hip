@@ -146,9 +146,123 @@ __device__ __forceinline__ int64_t resolve_pos(const FwdArgs& a, const int32_t* 
 // planner
 // ---------------------------------------------------------------------------
 
-__global__ void plan_kernel(PlanArgs a) {
+constexpr int kPlanThreads = 128;
+
+// Lengths of sequence b, read from the length tensors.
+struct SeqLens {
+  int q_len, q_used, ori_len, ori_base, cmp_len, cmp_base, res;
+};
+__device__ __forceinline__ SeqLens seq_lens(const PlanArgs& a, int b) {
+  const sfmla_params& p = a.p;
+  SeqLens s;
+  s.q_len = p.layout_q == SFMLA_LAYOUT_BSND ? p.q_s
+                                            : a.len.cu_seqlens_q[b + 1] - a.len.cu_seqlens_q[b];
+  const int qu = a.len.seqused_q ? a.len.seqused_q[b] : s.q_len;
+  s.q_used = qu < 0 ? 0 : (qu > s.q_len ? s.q_len : qu);
+  s.ori_base = 0;
+  if (a.len.seqused_ori_kv) s.ori_len = a.len.seqused_ori_kv[b];
+  else if (p.layout_kv == SFMLA_LAYOUT_TND)
+    s.ori_len = a.len.cu_seqlens_ori_kv[b + 1] - a.len.cu_seqlens_ori_kv[b];
+  else s.ori_len = p.ori_kv_s;
+  if (p.layout_kv == SFMLA_LAYOUT_TND) s.ori_base = a.len.cu_seqlens_ori_kv[b];
+  else if (p.layout_kv == SFMLA_LAYOUT_BSND) s.ori_base = b * p.ori_kv_s;
+  s.cmp_len = 0, s.cmp_base = 0, s.res = 0;
+  if (p.has_cmp_kv) {
+    if (a.len.seqused_cmp_kv) s.cmp_len = a.len.seqused_cmp_kv[b];
+    else if (p.layout_kv == SFMLA_LAYOUT_TND)
+      s.cmp_len = a.len.cu_seqlens_cmp_kv[b + 1] - a.len.cu_seqlens_cmp_kv[b];
+    else s.cmp_len = p.cmp_kv_s;
+    if (p.layout_kv == SFMLA_LAYOUT_TND) s.cmp_base = a.len.cu_seqlens_cmp_kv[b];
+    else if (p.layout_kv == SFMLA_LAYOUT_BSND) s.cmp_base = b * p.cmp_kv_s;
+    if (a.len.cmp_residual_kv) s.res = a.len.cmp_residual_kv[b];
+  }
+  return s;
+}
+
+// Whether the rows of a sequence go in query tiles: a decision from the
+// sequence's own lengths (so a sequence is tiled the same way in any batch),
+// taken where tiles are possible at all (a.tq > 1): enough valid queries,
+// and a bound on the union of a tile's lists within one split.  The union
+// of tq consecutive rows' windows spans at most win_left + win_right + tq
+// positions (each row's window is its predecessor's moved by one), every
+// rule list lies within the sequence's ori rows, and the visible compressed
+// rows of any row lie within the sequence's compressed rows.
+__device__ __forceinline__ bool seq_tiled(const PlanArgs& a, const SeqLens& s) {
+  const sfmla_params& p = a.p;
+  if (a.tq < 2 || s.q_used < a.tile_min_queries) return false;
+  int64_t n = max(s.ori_len, 0);
+  if (p.ori_mask_mode == SFMLA_MASK_BAND && p.ori_win_left >= 0 && p.ori_win_right >= 0)
+    n = min(n, (int64_t)p.ori_win_left + p.ori_win_right + a.tq);
+  if (p.has_cmp_kv) n += max(s.cmp_len, 0);
+  return n <= kMaxSplitRows;
+}
+
+// Query tiles of a.tq consecutive rows of the tiled sequences, numbered
+// sequence by sequence with no gaps, so that the workgroups of the tiled
+// launch that find no tile all come after the real ones.  One workgroup:
+// sequences go in chunks of kPlanThreads, an LDS scan of their tile counts
+// gives each chunk's numbers, then every thread writes descriptors (first
+// row, row count), finding a tile's sequence by binary search over the
+// chunk's scan.  Descriptors past the last tile read (-1, 0).  Only rows
+// < q_t belong to a sequence's tiles.
+__device__ void plan_tiles(const PlanArgs& a) {
+  const sfmla_params& p = a.p;
+  __shared__ int32_t s_scan[kPlanThreads], s_first[kPlanThreads], s_row0[kPlanThreads],
+      s_len[kPlanThreads];
+  const int tid = threadIdx.x, tq = a.tq;
+  int32_t* desc = a.meta + a.tile_off;
+  int64_t base = 0;                              // tiles of the chunks before
+  for (int b0 = 0; b0 < p.batch_size; b0 += kPlanThreads) {
+    const int b = b0 + tid;
+    int r0 = 0, len = 0;
+    if (b < p.batch_size) {
+      const SeqLens sl = seq_lens(a, b);
+      r0 = p.layout_q == SFMLA_LAYOUT_BSND ? b * p.q_s : a.len.cu_seqlens_q[b];
+      len = seq_tiled(a, sl) ? sl.q_len : 0;
+      if (r0 < 0 || r0 >= p.q_t) len = 0;
+      len = max(0, min(len, p.q_t - max(r0, 0)));
+    }
+    const int cnt = (len + tq - 1) / tq;
+    int v = cnt;                                  // inclusive scan over the chunk
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const int add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      v += add;
+      s_scan[tid] = v;
+      __syncthreads();
+    }
+    s_first[tid] = v - cnt;
+    s_row0[tid] = r0;
+    s_len[tid] = len;
+    __syncthreads();
+    const int total = s_scan[kPlanThreads - 1];
+    const int last = min(kPlanThreads, p.batch_size - b0) - 1;
+    for (int u = tid; u < total; u += kPlanThreads) {
+      // the last sequence whose first tile is <= u holds tile u
+      int lo = 0, hi = last;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_first[mid] <= u) lo = mid; else hi = mid - 1;
+      }
+      const int k = u - s_first[lo];
+      const int64_t gu = base + u;
+      if (gu < a.tile_bound)
+        *(int2*)(desc + kTileDescInts * gu) =
+            make_int2(s_row0[lo] + tq * k, min(tq, s_len[lo] - tq * k));
+    }
+    base += total;
+    __syncthreads();                              // before the next chunk reuses LDS
+  }
+  for (int64_t u = base + tid; u < a.tile_bound; u += kPlanThreads)
+    *(int2*)(desc + kTileDescInts * u) = make_int2(-1, 0);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const sfmla_params& p = a.p;
   const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (a.tq > 1 && blockIdx.x == 0) plan_tiles(a);
   if (row == 0) {
     a.meta[0] = kMagic;
     a.meta[1] = (int32_t)a.fingerprint;
@@ -164,11 +278,10 @@ __global__ void plan_kernel(PlanArgs a) {
     for (int64_t k = row; k < n4; k += (int64_t)gridDim.x * blockDim.x) cnt[k] = make_uint4(0, 0, 0, 0);
   }
   if (row >= p.q_t) return;
-  int b, i, q_len;
+  int b, i;
   if (p.layout_q == SFMLA_LAYOUT_BSND) {
     b = row / p.q_s;
     i = row - b * p.q_s;
-    q_len = p.q_s;
   } else {
     int lo = 0, hi = p.batch_size - 1;  // last b with cu[b] <= row
     while (lo < hi) {
@@ -177,29 +290,11 @@ __global__ void plan_kernel(PlanArgs a) {
     }
     b = lo;
     i = row - a.len.cu_seqlens_q[b];
-    q_len = a.len.cu_seqlens_q[b + 1] - a.len.cu_seqlens_q[b];
   }
-  int q_used = a.len.seqused_q ? a.len.seqused_q[b] : q_len;
-  q_used = q_used < 0 ? 0 : (q_used > q_len ? q_len : q_used);
-
-  int ori_len, ori_base = 0;
-  if (a.len.seqused_ori_kv) ori_len = a.len.seqused_ori_kv[b];
-  else if (p.layout_kv == SFMLA_LAYOUT_TND)
-    ori_len = a.len.cu_seqlens_ori_kv[b + 1] - a.len.cu_seqlens_ori_kv[b];
-  else ori_len = p.ori_kv_s;
-  if (p.layout_kv == SFMLA_LAYOUT_TND) ori_base = a.len.cu_seqlens_ori_kv[b];
-  else if (p.layout_kv == SFMLA_LAYOUT_BSND) ori_base = b * p.ori_kv_s;
-
-  int cmp_len = 0, cmp_base = 0, res = 0;
-  if (p.has_cmp_kv) {
-    if (a.len.seqused_cmp_kv) cmp_len = a.len.seqused_cmp_kv[b];
-    else if (p.layout_kv == SFMLA_LAYOUT_TND)
-      cmp_len = a.len.cu_seqlens_cmp_kv[b + 1] - a.len.cu_seqlens_cmp_kv[b];
-    else cmp_len = p.cmp_kv_s;
-    if (p.layout_kv == SFMLA_LAYOUT_TND) cmp_base = a.len.cu_seqlens_cmp_kv[b];
-    else if (p.layout_kv == SFMLA_LAYOUT_BSND) cmp_base = b * p.cmp_kv_s;
-    if (a.len.cmp_residual_kv) res = a.len.cmp_residual_kv[b];
-  }
+  const SeqLens sl = seq_lens(a, b);
+  const int q_used = sl.q_used, ori_len = sl.ori_len, ori_base = sl.ori_base;
+  const int cmp_len = sl.cmp_len, cmp_base = sl.cmp_base, res = sl.res;
+  const int tiled = seq_tiled(a, sl);
 
   const int valid = i < q_used;
   const int pos = ori_len - q_used + i;
@@ -209,7 +304,7 @@ __global__ void plan_kernel(PlanArgs a) {
   if (p.ori_topk > 0) {
     ori_cnt = p.ori_topk * p.ori_sparse_block_size;   // list positions (tokens)
   } else {
-    int lo = 0, hi = ori_len - 1;
+  int lo = 0, hi = ori_len - 1;
     if (p.ori_mask_mode == SFMLA_MASK_CAUSAL) {
       hi = pos < hi ? pos : hi;
     } else if (p.ori_mask_mode == SFMLA_MASK_BAND) {
@@ -245,7 +340,7 @@ __global__ void plan_kernel(PlanArgs a) {
     chunk = (chunk + kTile - 1) / kTile * kTile;
   }
   int32_t* r = a.meta + kHeaderInts + (int64_t)row * kRecInts;
-  r[R_B] = b; r[R_I] = i; r[R_VALID] = valid; r[R_P] = pos; r[R_PC] = pos_c;
+  r[R_B] = b; r[R_I] = i; r[R_VALID] = valid | (tiled << 1); r[R_P] = pos; r[R_PC] = pos_c;
   r[R_ORI_LO] = ori_lo; r[R_ORI_CNT] = ori_cnt; r[R_CMP_CNT] = cmp_cnt;
   r[R_ORI_BASE] = ori_base; r[R_CMP_BASE] = cmp_base; r[R_ORI_LEN] = ori_len;
   r[R_CMP_LEN] = cmp_len; r[R_NSPLIT] = nsplit; r[R_CHUNK] = chunk;
@@ -631,14 +726,36 @@ constexpr float kRescaleThreshold = 8.0f;
 constexpr int kMergeSplits = 4;       // splits whose partials one merge round loads (8 waves)
 constexpr int kMaxOwnerSplits = 8;    // splits of a row whose partials an owning wave merges
 
+// Position of slot u of a resolve batch starting at i0 (PPT slots per thread).
+// bf16 rows: wave w resolves exactly the rows it gathers (row w*NR + l%NR of
+// tile l/NR, then the next 64/NR tiles for u = 1).  Packed rows (gathered in
+// 16-byte chunks across rows): one position per thread in order.
+template <int NW, int DQK, int VMODE, bool PK, int PPT>
+__device__ __forceinline__ int posn_of(int i0, int u, int tid, int w, int l) {
+  if constexpr (PK) {
+    return i0 + tid + u * NW * 64;
+  } else {
+    constexpr int NR = Pipe<NW, DQK, VMODE>::NR, TPB = 64 / NR;
+    static_assert(PPT * TPB * kTile == PPT * NW * 64, "a batch covers PPT*NTHR positions");
+    return i0 + (u * TPB + l / NR) * kTile + w * NR + (l % NR);
+  }
+}
+
 // HB head blocks of 16 heads per wave; FMT is the KV storage format.
-template <int NW, int HB, int DQK, int VMODE, int FMT>
+// TILED: the launch starts with a.tile_units workgroups, one per query tile
+// (a.tq consecutive rows of a sequence, a.nb head blocks each): the tile's
+// union list is resolved and gathered once, wave w computes row w / a.nb's
+// head block w % a.nb and masks the union positions its row's list does not
+// hold.  The rows of sequences that are not tiled follow, one workgroup per
+// (split, row) with every head (one head group), as without tiles.
+template <int NW, int HB, int DQK, int VMODE, int FMT, bool TILED = false>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   using C = Pipe<NW, DQK, VMODE>;
   using PP = PackedPipe<NW, DQK>;
   constexpr bool HALF = FMT == SFMLA_KV_FP16;     // float16 q / kv / P / output
   constexpr bool PK = FMT != SFMLA_KV_BF16 && !HALF;   // packed rows (V = decoded nope)
   static_assert(!PK || VMODE == 0, "packed KV has no separate V");
+  static_assert(!TILED || (!PK && NW == 8 && HB == 1), "query tiles: 16-bit rows, 8 waves");
   static_assert(FMT == SFMLA_KV_BF16 || FMT == SFMLA_KV_INT8_PACKED ||
                 FMT == SFMLA_KV_FP8_E4M3_PACKED || FMT == SFMLA_KV_FP16, "KV format");
   constexpr int T = C::T;
@@ -669,111 +786,166 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
                 "output staging: two waves' 16 heads per stage buffer");
   __shared__ int32_t sOut;
   // V = K nope: two more landing slots for the owned merge (the separate-V
-  // kernel has its V stages for them)
-  __shared__ __align__(16) char sM[(VMODE || PK) ? 16 : 32768];
+  // kernel has its V stages for them; the tiled kernel merges splits of its
+  // untiled rows with the last split to arrive)
+  __shared__ __align__(16) char sM[(VMODE || PK || TILED) ? 16 : 32768];
   // owned merge: per owning wave, every split's weight and the normaliser
   // per head, and a flag (1: landed and weighted, 2: handed off)
-  __shared__ float sWs[PK ? 1 : NW][PK ? 1 : kMaxOwnerSplits][16];
-  __shared__ float sInv[PK ? 1 : NW][16];
+  __shared__ float sWs[(PK || TILED) ? 1 : NW][(PK || TILED) ? 1 : kMaxOwnerSplits][16];
+  __shared__ float sInv[(PK || TILED) ? 1 : NW][16];
   __shared__ int32_t sReady[NW];
 
-  // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so XCD x = bid
-  // mod 8 takes the query rows 8k + x, and within it slot bid / 8 runs over
-  // (split, k, head group), split slowest: every split and head group of a
-  // row is on one XCD, so the groups' repeated gathers and the merger's reads
-  // of the other splits' partials stay within that XCD's L2.  Split-major
-  // order puts the workgroups of splits a row does not have (its list is
-  // shorter than the longest) after all the real ones; interleaved between
-  // them they were measured to slow a one-split launch by a third.
-  const int G = a.groups;
-  const int K8 = (a.q_t + 7) >> 3;
-  const int bid = blockIdx.x;
-  const int slot = bid >> 3;
-  const int hg = slot % G;
-  const int split = slot / G / K8;
-  const int row = ((slot / G) % K8) * 8 + (bid & 7);
-  if (row >= a.q_t) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g = l >> 4, t = l & 15;
-  // a head group holds a.bpg 16-head blocks; waves past them only gather
-  const int h0 = (hg * a.bpg + w) * HPW;           // first head of this wave
-  const bool wave_on = w < a.bpg && h0 < a.qn;
-
-  // The row's plan record is read together with the plan header (the buffer
-  // always holds both; its size is checked on the host), so the two reads
-  // cost one round trip; the record is only used once the header matches.
-  const int4 hdr = *(const int4*)a.meta;
-  const int32_t* rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
-  const int nsplit = rec[R_NSPLIT];
-  const int n = rec[R_NTOTAL];
-  const int chunk = rec[R_CHUNK];
-  const RowInfo ri = row_info(rec);
-  // Index loads of the first resolve batch, issued in the same round trip:
-  // where the original-KV list is a TopK list its length is fixed by the
-  // parameters, so a position's entry does not depend on the plan record
-  // unless the row is empty or split in other chunks (a long-query row);
-  // the resolve below reloads in those cases.  Every load is in bounds
-  // (positions past the lists read the plan header instead).
-  constexpr int PPT = (512 + T + NTHR - 1) / NTHR;   // positions per thread and batch
-  // Position of slot u of a resolve batch starting at i0.  bf16 rows: wave w
-  // resolves exactly the rows it gathers (row w*NR + l%NR of tile l/NR, then
-  // the next 64/NR tiles for u = 1), so it can issue its share of the first
-  // tiles as soon as its own entries are in, with no workgroup barrier.
-  // Packed rows (gathered in 16-byte chunks across rows): one position per
-  // thread in order.
-  auto posn = [&](int i0, int u) -> int {
-    if constexpr (PK) {
-      return i0 + tid + u * NTHR;
-    } else {
-      constexpr int NR = C::NR, TPB = 64 / NR;
-      static_assert(PPT * TPB * T == PPT * NTHR, "a batch covers PPT*NTHR positions");
-      return i0 + (u * TPB + l / NR) * T + w * NR + (l % NR);
+  // NaN outputs of query row r for this wave's heads (a plan that does not
+  // match, or a list longer than the parameters allow)
+  auto fail_row = [&](int r, int hfirst, bool on) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = hfirst + 16 * hb + t;
+      if (!on || h >= a.qn) continue;
+      uint16_t* op = a.out + ((int64_t)r * a.qn + h) * 512;
+      for (int c = g; c < 512; c += 4) op[c] = to16<HALF>(__builtin_nanf(""));
+      if (a.lse && g == 0) a.lse[(int64_t)r * a.qn + h] = __builtin_nanf("");
     }
   };
-  const int spec_cnt = a.ori_topk << a.ori_sbs_log2;
-  const int spec_cap = a.ori_topk > 0 ? spec_cnt + (a.cmp_topk > 0 ? a.cmp_topk : 0) : 0;
+  int row;            // the query row whose plan record gives the list's sequence
+  int orow;           // the query row this wave computes
+  int split, hg, h0, nsplit, n, chunk;
+  bool wave_on;
+  const int32_t* rec;
+  RowInfo ri;
+  constexpr int PPT = (512 + T + NTHR - 1) / NTHR;   // positions per thread and batch
   int vspec[PPT];
+  // tiles: the union positions this wave's row holds are [m_a0, m_a0 + m_cnt)
+  // (original KV) and [m_ucnt, m_ucnt + m_cc) (compressed KV); a row's own
+  // list holds every position
+  int m_a0 = 0, m_cnt = 0x7fffffff, m_ucnt = 0, m_cc = 0;
+  if (TILED && (int)blockIdx.x < a.tile_units) {
+    // Tiles are numbered without gaps (descriptor: first row, row count), so
+    // the workgroups past the last tile, which exit at once, all come after
+    // the real ones.  Tile u is dealt to XCD u mod 8.
+    const int unit = blockIdx.x;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int tau = wu / a.nb;                      // this wave's row in the tile
+    split = 0;
+    hg = 0;
+    h0 = (wu - tau * a.nb) * HPW;
+    const int4 hdr = *(const int4*)a.meta;
+    const int2 ud = *(const int2*)(a.meta + a.tile_off + (int64_t)kTileDescInts * unit);
+    // a plan of other parameters: the rows' workgroups that follow the tiles
+    // (split 0 of every row) write the NaN outputs and the status
+    if (!plan_matches(a, hdr)) return;
+    const int ntok = ud.y;
+    if (ud.x < 0 || ntok < 1 || ntok > a.tq || ud.x > a.q_t - ntok) return;   // no tile
+    row = ud.x;
+    orow = row + min(tau, ntok - 1);
+    wave_on = tau < ntok && h0 < a.qn;
+    rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
+    ri = row_info(rec);
+    // every row's list extents: lane j reads row min(j, ntok - 1) of the tile
+    const int32_t* rj = a.meta + kHeaderInts + (int64_t)(row + min(l & 7, ntok - 1)) * kRecInts;
+    const int olo = rj[R_ORI_LO], ocnt = rj[R_ORI_CNT], occ = rj[R_CMP_CNT];
+    // union: the window rows from the first row's start to the last row's end
+    // (consecutive rows' windows overlap or touch, and a position of the
+    // union outside a row's own window is masked for it anyway), and the
+    // visible compressed rows of the row that sees the most
+    int ulo = 0x7fffffff, uhi = -0x7fffffff - 1, ucc = 0;
 #pragma unroll
-  for (int u = 0; u < PPT; ++u) {
-    const int i = posn(0, u);
-    const int k = split * a.split_rows + i;
-    const int32_t* ep = (const int32_t*)a.meta;
-    if (i < a.split_rows && k < spec_cap)
-      ep = k < spec_cnt ? a.ori_idx + (int64_t)row * a.ori_topk + (k >> a.ori_sbs_log2)
-                        : a.cmp_idx + (int64_t)row * a.cmp_topk + (k - spec_cnt);
-    vspec[u] = *ep;
-  }
-  if (!plan_matches(a, hdr)) {
-    if (split == 0) {
-      const float nan = __builtin_nanf("");
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const int h = h0 + 16 * hb + t;
-        if (!wave_on || h >= a.qn) continue;
-        uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
-        for (int c = g; c < 512; c += 4) op[c] = to16<HALF>(nan);
-        if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = nan;
+    for (int j = 0; j < 8; ++j) {
+      const int c = __builtin_amdgcn_readlane(ocnt, j), lo = __builtin_amdgcn_readlane(olo, j);
+      if (c > 0) {
+        ulo = min(ulo, lo);
+        uhi = max(uhi, lo + c);
       }
-      if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_METADATA_MISMATCH);
+      ucc = max(ucc, __builtin_amdgcn_readlane(occ, j));
     }
-    return;
+    const int ucnt = uhi > ulo ? uhi - ulo : 0;
+    if (ucnt == 0) ulo = 0;
+    const int me = min(tau, ntok - 1);
+    const int my_cnt = __builtin_amdgcn_readlane(ocnt, me);
+    m_a0 = my_cnt > 0 ? __builtin_amdgcn_readlane(olo, me) - ulo : 0;
+    m_cnt = my_cnt;
+    m_ucnt = ucnt;
+    m_cc = __builtin_amdgcn_readlane(occ, me);
+    ri.ori_lo = ulo;
+    ri.ori_cnt = ucnt;
+    ri.cmp_limit = ucc;
+    n = ucnt + ucc;
+    nsplit = 1;
+    chunk = n;
+  } else {
+    // 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so XCD x = bid
+    // mod 8 takes the query rows 8k + x, and within it slot bid / 8 runs over
+    // (split, k, head group), split slowest: every split and head group of a
+    // row is on one XCD, so the groups' repeated gathers and the merger's reads
+    // of the other splits' partials stay within that XCD's L2.  Split-major
+    // order puts the workgroups of splits a row does not have (its list is
+    // shorter than the longest) after all the real ones; interleaved between
+    // them they were measured to slow a one-split launch by a third.
+    const int G = a.groups;
+    const int K8 = (a.q_t + 7) >> 3;
+    const int bid = (int)blockIdx.x - (TILED ? a.tile_units : 0);   // a multiple of 8
+    const int slot = bid >> 3;
+    hg = slot % G;
+    split = slot / G / K8;
+    row = ((slot / G) % K8) * 8 + (bid & 7);
+    if (row >= a.q_t) return;
+    orow = row;
+    // a head group holds a.bpg 16-head blocks; waves past them only gather
+    h0 = (hg * a.bpg + w) * HPW;                    // first head of this wave
+    wave_on = w < a.bpg && h0 < a.qn;
+
+    // The row's plan record is read together with the plan header (the buffer
+    // always holds both; its size is checked on the host), so the two reads
+    // cost one round trip; the record is only used once the header matches.
+    const int4 hdr = *(const int4*)a.meta;
+    rec = a.meta + kHeaderInts + (int64_t)row * kRecInts;
+    nsplit = rec[R_NSPLIT];
+    n = rec[R_NTOTAL];
+    chunk = rec[R_CHUNK];
+    ri = row_info(rec);
+    // Index loads of the first resolve batch, issued in the same round trip:
+    // where the original-KV list is a TopK list its length is fixed by the
+    // parameters, so a position's entry does not depend on the plan record
+    // unless the row is empty or split in other chunks (a long-query row);
+    // the resolve below reloads in those cases.  Every load is in bounds
+    // (positions past the lists read the plan header instead).
+    const int spec_cnt0 = a.ori_topk << a.ori_sbs_log2;
+    const int spec_cap = a.ori_topk > 0 ? spec_cnt0 + (a.cmp_topk > 0 ? a.cmp_topk : 0) : 0;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = posn_of<NW, DQK, VMODE, PK, PPT>(0, u, tid, w, l);
+      const int k = split * a.split_rows + i;
+      const int32_t* ep = (const int32_t*)a.meta;
+      if (i < a.split_rows && k < spec_cap)
+        ep = k < spec_cnt0 ? a.ori_idx + (int64_t)row * a.ori_topk + (k >> a.ori_sbs_log2)
+                           : a.cmp_idx + (int64_t)row * a.cmp_topk + (k - spec_cnt0);
+      vspec[u] = *ep;
+    }
+    if (!plan_matches(a, hdr)) {
+      if (split == 0) {
+        fail_row(row, h0, wave_on);
+        if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_METADATA_MISMATCH);
+      }
+      return;
+    }
+    if (split >= nsplit) return;
+    if (TILED && (rec[R_VALID] & 2)) return;        // the row is in a tile
   }
-  if (split >= nsplit) return;
   if (chunk > kMaxSplitRows) {
     // a list longer than the parameters' maxima allow: refuse the row
     if (split == 0) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const int h = h0 + 16 * hb + t;
-        if (!wave_on || h >= a.qn) continue;
-        uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512;
-        for (int c = g; c < 512; c += 4) op[c] = to16<HALF>(__builtin_nanf(""));
-        if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = __builtin_nanf("");
-      }
+      fail_row(orow, h0, wave_on);
       if (a.status && tid == 0) atomicOr(a.status, SFMLA_STATUS_LIST_TOO_LONG);
     }
     return;
   }
+  const int spec_cnt = a.ori_topk << a.ori_sbs_log2;
+  // bf16 rows: each wave resolves the rows it gathers, so it can issue its
+  // share of the first tiles as soon as its own entries are in, with no
+  // workgroup barrier
+  auto posn = [&](int i0, int u) -> int { return posn_of<NW, DQK, VMODE, PK, PPT>(i0, u, tid, w, l); };
   const int k0 = split * chunk;
   const int k1 = min(n, k0 + chunk);
   const int nt = (k1 - k0 + T - 1) / T;
@@ -791,7 +963,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   //      512-row split, the Q loads follow its table loads.
   {
     const int ntT = nt * T;
-    const bool spec = a.ori_topk > 0 && chunk == a.split_rows && ri.ori_cnt == spec_cnt;
+    const bool spec = !TILED && a.ori_topk > 0 && chunk == a.split_rows && ri.ori_cnt == spec_cnt;
     auto batch = [&](int i0, bool use_spec, auto&& between) {
       int vv[PPT], jj[PPT], sd[PPT], ee[PPT];
       bool he[PPT];
@@ -845,7 +1017,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         // (row * q_n + head < 2^31, checked on the host; a 32-bit index
         // here also keeps it from being held until the epilogue)
         const int h = h0 + 16 * hb + t;
-        const int qi = row * a.qn + (h < a.qn ? h : 0);
+        const int qi = orow * a.qn + (h < a.qn ? h : 0);
         const uint16_t* qp = a.q + (uint32_t)qi * (uint64_t)DQK + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
@@ -884,6 +1056,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       valid[i] = sRow[tbase + 4 * g + i] != kNoRow;
       valid[4 + i] = sRow[tbase + 16 + 4 * g + i] != kNoRow;
+    }
+    if constexpr (TILED) {
+      // union positions outside this wave's row's own list
+      auto mine = [&](int k) {
+        return (uint32_t)(k - m_a0) < (uint32_t)m_cnt || (uint32_t)(k - m_ucnt) < (uint32_t)m_cc;
+      };
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        valid[i] = valid[i] && mine(tbase + 4 * g + i);
+        valid[4 + i] = valid[4 + i] && mine(tbase + 16 + 4 * g + i);
+      }
     }
     f32x4 s[HB][2];
 #pragma unroll
@@ -1123,7 +1306,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     const int h = h0 + 16 * hb + t;
     if (h >= a.qn) return;
     const float inv = den > 0.f ? scale / den : 0.f;
-    uint16_t* op = a.out + ((int64_t)row * a.qn + h) * 512 + 4 * g;
+    uint16_t* op = a.out + ((int64_t)orow * a.qn + h) * 512 + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < 32; ++mb) {
       uint2 pk;
@@ -1131,7 +1314,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       pk.y = (uint32_t)to16<HALF>(o[hb][mb][2] * inv) | ((uint32_t)to16<HALF>(o[hb][mb][3] * inv) << 16);
       *(uint2*)(op + 16 * mb) = pk;
     }
-    if (a.lse && g == 0) a.lse[(int64_t)row * a.qn + h] = den > 0.f ? l2 * kLn2 : kNegInf;
+    if (a.lse && g == 0) a.lse[(int64_t)orow * a.qn + h] = den > 0.f ? l2 * kLn2 : kNegInf;
   };
 
   if (nsplit == 1) {
@@ -1182,7 +1365,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // (only where every wave of the workgroup holds heads, so the shared
   // merge runs on all SIMDs: with fewer head waves the last split to
   // arrive merges sooner, measured)
-  const bool own_mode = !PK && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
+  const bool own_mode = !PK && !TILED && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
                         n_on == NW && n_own > 0 && n_own * nsplit <= OSLOT;
   auto slot_addr = [&](int q) -> uint32_t {          // slot q: two per stage buffer
     const int b = q >> 1;
@@ -1577,7 +1760,7 @@ __global__ __launch_bounds__(256) void resolve_kernel(FwdArgs a) {
 constexpr int kMaxDevices = 64;
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  const int threads = 128;
+  const int threads = kPlanThreads;
   const int blocks = (a.p.q_t + threads - 1) / threads;
   hipLaunchKernelGGL(plan_kernel, dim3(blocks > 0 ? blocks : 1), dim3(threads), 0, s, a);
   return hipGetLastError();
@@ -1661,6 +1844,45 @@ hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt,
                                    : launch_fwd_t<8, 512, 0, 0>(a, groups, mw, s, t0, t1);
       return vmode ? launch_fwd_t<8, 576, 1, 0>(a, groups, mw, s, t0, t1)
                    : launch_fwd_t<8, 576, 0, 0>(a, groups, mw, s, t0, t1);
+  }
+}
+
+template <int DQK, int VMODE, int FMT>
+static hipError_t launch_tiled_t(const FwdArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  // a tile's rows and head blocks fill at most the 8 waves; the tiles'
+  // workgroups are a multiple of 8 (the rows' XCD mapping follows them)
+  if (a.tq < 2 || a.tq > 8 || a.nb < 1 || a.tq * a.nb > 8 || a.tile_units < 8 ||
+      a.tile_units % 8)
+    return hipErrorInvalidConfiguration;
+  FwdArgs b = a;
+  b.groups = 1;
+  b.bpg = 8;
+  b.merge_wait_ticks = 0;
+  const int64_t blocks = (int64_t)a.tile_units + (int64_t)(a.q_t + 7) / 8 * 8 * a.max_splits;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (t0 || t1)
+    hipExtLaunchKernelGGL((fwd_kernel<8, 1, DQK, VMODE, FMT, true>), dim3((unsigned)blocks),
+                          dim3(512), 0, s, t0, t1, 0, b);
+  else
+    hipLaunchKernelGGL((fwd_kernel<8, 1, DQK, VMODE, FMT, true>), dim3((unsigned)blocks),
+                       dim3(512), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_tiled(const FwdArgs& a, int dqk, int vmode, int fmt, hipStream_t s,
+                                hipEvent_t t0, hipEvent_t t1) {
+  switch (fmt) {
+    case SFMLA_KV_BF16:
+      if (dqk == 512) return vmode ? launch_tiled_t<512, 1, 0>(a, s, t0, t1)
+                                   : launch_tiled_t<512, 0, 0>(a, s, t0, t1);
+      return vmode ? launch_tiled_t<576, 1, 0>(a, s, t0, t1) : launch_tiled_t<576, 0, 0>(a, s, t0, t1);
+    case SFMLA_KV_FP16:
+      if (dqk == 512) return vmode ? launch_tiled_t<512, 1, SFMLA_KV_FP16>(a, s, t0, t1)
+                                   : launch_tiled_t<512, 0, SFMLA_KV_FP16>(a, s, t0, t1);
+      return vmode ? launch_tiled_t<576, 1, SFMLA_KV_FP16>(a, s, t0, t1)
+                   : launch_tiled_t<576, 0, SFMLA_KV_FP16>(a, s, t0, t1);
+    default:
+      return hipErrorInvalidConfiguration;   // packed rows are not tiled
   }
 }
 

@@ -310,3 +310,64 @@ def test_partials_of_one_row_beyond_32_bit_offsets_are_rejected():
     assert b"2^31" in lib.sfmla_last_error()
     p.head_blocks_per_group = 0
     assert lib.sfmla_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+
+
+# ---------------------------------------------------------------------------
+# query tiles: host rule, metadata size and workspace
+# ---------------------------------------------------------------------------
+
+def _meta_ints(P, **over):
+    return s.sfmla_metadata_size(s.make_params(dict(P.params, **over), P.arrays))
+
+
+def test_query_tile_rule_sizes_the_tile_descriptors():
+    """Tiles by rule need rule lists, 16-bit rows, at most 64 heads and
+    max_seqlen_q >= 16; the plan then holds one (first row, row count) pair
+    per possible tile: ceil((q_t + b (tq - 1)) / tq), at most q_t, rounded up
+    to a multiple of 8."""
+    base_ints = lambda P: 16 + (16 + 64) * P.params["q_t"]
+    up8 = lambda n: (n + 7) // 8 * 8
+    for name, tq in (("swa_prefill", 2), ("hca_prefill", 2), ("swa_prefill_h16", 8)):
+        P = synth.make_workload(name)
+        q_t, B = P.params["q_t"], P.params["batch_size"]
+        assert _meta_ints(P) == base_ints(P) + 2 * up8(min(q_t, (q_t + B * (tq - 1)) // tq)), name
+        assert _meta_ints(P, query_tile=1) == base_ints(P), name      # tiles off
+    # TopK lists (csa), packed rows and 128 heads are never tiled
+    for name in ("csa_prefill", "c8_packed_int8_q32", "hca_varlen_q32", "swa_decode"):
+        P = synth.make_workload(name)
+        assert _meta_ints(P) == base_ints(P), name
+    # forced tiles of 4 rows at 16 heads on a decode-sized batch
+    P = synth.make_workload("swa_decode")                 # 2 sequences of one query, 16 heads
+    assert _meta_ints(P, query_tile=4) == base_ints(P) + 2 * 8
+
+
+def test_query_tile_override_is_validated_and_fingerprinted():
+    P = synth.make_workload("swa_prefill")                # 64 heads: at most 2 rows per tile
+    for bad in (3, 16, -1):
+        with pytest.raises(s.SfmlaError, match="query_tile"):
+            _meta_ints(P, query_tile=bad)
+    for bad in (4, 8):                                    # 4 head blocks x 4 rows > 8 waves
+        with pytest.raises(s.SfmlaError, match="query_tile"):
+            _meta_ints(P, query_tile=bad)
+    C = synth.make_workload("csa_prefill")                # TopK compressed rows
+    with pytest.raises(s.SfmlaError, match="query_tile"):
+        _meta_ints(C, query_tile=2)
+    K = synth.make_workload("c8_packed_int8")             # packed rows
+    with pytest.raises(s.SfmlaError, match="query_tile"):
+        _meta_ints(K, query_tile=2)
+
+
+def test_tiled_call_lays_out_split_rows_with_every_head_in_one_group():
+    """Rows of sequences that are not tiled (too few queries, or a union too
+    long for one split) are split as without tiles, with every head in one
+    workgroup: the workspace is that of one head group of 8 waves."""
+    P = synth.make_workload("hca_prefill")
+    q = s.make_params(dict(P.params, max_seqlen_cmp_kv=4096), P.arrays)
+    ws = s.sfmla_workspace_size(q)
+    splits = -(-(128 + 4096) // 256)                     # all-visible rows: 256-row splits
+    slots = P.params["q_t"] * splits * 128                # 8 waves x 16 heads
+    up = lambda n: (n + 255) // 256 * 256
+    assert ws == up(slots * 1024) + up(slots * 4)
+    # without tiles the 64 heads take 4 waves per group of the same size
+    assert s.sfmla_workspace_size(s.make_params(dict(P.params, max_seqlen_cmp_kv=4096,
+                                                     query_tile=1), P.arrays)) > 0

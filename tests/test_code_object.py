@@ -102,11 +102,12 @@ def kernels():
 
 
 def _fwd(kernels):
-    """fwd_kernel instantiations as (waves, d_qk, separate V, format) -> fields."""
+    """fwd_kernel instantiations as (waves, d_qk, separate V, format, query
+    tiles) -> fields."""
     res = {}
     for name, f in kernels.items():
-        m = re.fullmatch(r"_ZN5sfmla10fwd_kernelILi(\d+)ELi1ELi(\d+)ELi(\d)ELi(\d)EEEvNS_7FwdArgsE",
-                         name)
+        m = re.fullmatch(r"_ZN5sfmla10fwd_kernelILi(\d+)ELi1ELi(\d+)ELi(\d)ELi(\d)ELb(\d)EEEv"
+                         r"NS_7FwdArgsE", name)
         if m:
             res[tuple(int(x) for x in m.groups())] = f
     return res
@@ -114,15 +115,18 @@ def _fwd(kernels):
 
 def test_every_forward_variant_is_built(kernels):
     fwd = _fwd(kernels)
-    # bf16 / float16 rows: d_qk 512 or 576, V shared or separate
+    # bf16 / float16 rows: d_qk 512 or 576, V shared or separate, one query
+    # row per workgroup or query tiles
     for fmt in (0, 3):
         for dqk in (512, 576):
             for vmode in (0, 1):
-                assert (8, dqk, vmode, fmt) in fwd
-    # packed INT8 / FP8 rows, with and without rope
+                for tiled in (0, 1):
+                    assert (8, dqk, vmode, fmt, tiled) in fwd
+    # packed INT8 / FP8 rows, with and without rope (never tiled)
     for fmt in (1, 2):
         for dqk in (512, 576):
-            assert (4, dqk, 0, fmt) in fwd
+            assert (4, dqk, 0, fmt, 0) in fwd
+            assert (4, dqk, 0, fmt, 1) not in fwd
     assert any("plan_kernel" in k for k in kernels)
     assert any("combine_kernel" in k for k in kernels)
 
@@ -143,14 +147,13 @@ def test_forward_kernels_use_no_scratch_in_the_main_loop(kernels, disasm):
     instantiation (bf16, rope, separate V) has none at all."""
     fwd = _fwd(kernels)
     for key, f in fwd.items():
-        waves, dqk, vmode, fmt = key
-        if key == (8, 576, 1, 0):
+        if key == (8, 576, 1, 0, 0):
             assert f["vgpr_spill_count"] == 0 and f["private_segment_fixed_size"] == 0, (key, f)
         assert f["vgpr_spill_count"] <= 16 and f["private_segment_fixed_size"] <= 64, (key, f)
     found = 0
     for name, body in disasm.items():
-        m = re.fullmatch(r"_ZN5sfmla10fwd_kernelILi(\d+)ELi1ELi(\d+)ELi(\d)ELi(\d)EEEvNS_7FwdArgsE",
-                         name)
+        m = re.fullmatch(r"_ZN5sfmla10fwd_kernelILi(\d+)ELi1ELi(\d+)ELi(\d)ELi(\d)ELb(\d)EEEv"
+                         r"NS_7FwdArgsE", name)
         if not m:
             continue
         found += 1

@@ -331,13 +331,17 @@ GRAPH_CASES = [dict(),                                        # bf16, separate V
 
 @pytest.mark.parametrize("kw", GRAPH_CASES, ids=["separate_v", "packed", "shared_v"])
 def test_graph_replay_matches_eager(kw):
-    """plan + forward + combine captured in one HIP graph: every replay,
-    with other eager work and synchronisations in between, reproduces the
-    eager result bit for bit (split rows merged in the launch: the arrival
-    counters must come back to zero on every replay)."""
-    import sparse_shared_kv_amd as s
+    """plan + forward captured in one HIP graph: every replay, with other
+    eager work and synchronisations in between, reproduces the eager result
+    bit for bit (split rows merged in the launch: the arrival counters must
+    come back to zero on every replay)."""
     P = synth.random_tiny(602, family="sfa", max_kv=3000, topk=1500, num_heads_q=128, lse=True,
                           **kw)
+    _graph_replay(P)
+
+
+def _graph_replay(P):
+    import sparse_shared_kv_amd as s
     other = synth.random_tiny(603, family="csa", num_heads_q=64, max_kv=900)
     call = s.Call(P.params, P.arrays)
     eager = [t.clone() for t in call.run() if t is not None]
@@ -565,3 +569,118 @@ def test_owned_merge_matches_last_arriver_bitwise(kw):
     rows = sorted({0, P.query_rows - 1})
     res = dict(O=outs[0][0].float().cpu().numpy(), lse=outs[0][1].cpu().numpy(), status=0)
     check_outputs(P, res, oracle.forward(P, rows=rows), rows)
+
+
+# ---------------------------------------------------------------------------
+# query tiles: consecutive query rows of a sequence share one gathered list
+# ---------------------------------------------------------------------------
+
+def _tiny_tiled(kw):
+    kw = dict(kw)
+    tq = kw.pop("query_tile")
+    P = synth.random_tiny(**kw)
+    P.params["query_tile"] = tq
+    return P
+
+
+TILE_CASES = (
+    [dict(seed=700 + i, family=["swa", "hca"][i % 2], query_tile=[2, 4, 8][i % 3], max_q=20,
+          max_kv=300) for i in range(12)]
+    + [dict(seed=720 + i, family=["swa", "hca"][i % 2], query_tile=2, num_heads_q=64, dist="p4",
+            max_q=9, max_kv=400) for i in range(2)]
+    + [dict(seed=730, family="hca", query_tile=4, num_heads_q=20, max_q=13),
+       dict(seed=731, family="swa", query_tile=4, num_heads_q=32, max_q=13, kv_dtype="fp16"),
+       dict(seed=732, family="hca", query_tile=8, kv_dtype="fp16", max_q=20),
+       dict(seed=733, family="swa", query_tile=2, separate_v=True, rope_head_dim=64,
+            num_heads_q=48, max_q=11, max_kv=200),
+       dict(seed=734, family="hca", query_tile=8, rope_head_dim=64, max_q=17, max_kv=200),
+       dict(seed=735, family="hca", query_tile=4, layout_q="TND", batch=3, q_lens=[5, 0, 9],
+            ori_lens=[40, 10, 60]),
+       dict(seed=736, family="swa", query_tile=2, layout_q="BSND", batch=2, q_lens=[7, 3],
+            ori_lens=[30, 50], seqused_q=True)]
+)
+
+
+@pytest.mark.parametrize("kw", TILE_CASES, ids=lambda k: "-".join(str(v) for v in k.values()))
+def test_tiny_tiled_parity(kw):
+    """Tiles forced on small problems (every layout, window and mask rule,
+    ragged and empty sequences, rows past seqused_q, tiles cut short by the
+    sequence's end, 1 to 4 head blocks per row, rope and a separate V,
+    float16): every row against the oracle."""
+    P = _tiny_tiled(kw)
+    say("[tiles] case", kw)
+    ref = oracle.forward(P)
+    res = run_gpu(P)
+    check_lists(P, res["call"], ref)
+    check_outputs(P, res, ref)
+
+
+def _mixed_tile_batch():
+    """Sequences by rule: 20 queries with a short union (tiled), 3 queries
+    (too few: one workgroup per row), 18 queries whose visible compressed
+    rows exceed one split (rows split in 256-row chunks and merged)."""
+    return logical(41, q_lens=[20, 3, 18], ori_lens=[600, 900, 9000], qn=16, ratio=4, cmp_topk=0,
+                   win=(127, 0))
+
+
+def test_tiled_batch_matches_oracle_and_is_batch_invariant_bitwise():
+    L = _mixed_tile_batch()
+    full = place(L, "TND", "PA_BSND", bs=16, seed=1)
+    say("[tiles] mixed batch: gpu")
+    res = run_gpu(full)
+    say("[tiles] mixed batch: oracle")
+    ref = oracle.forward(full)
+    check_lists(full, res["call"], ref)
+    check_outputs(full, res, ref)
+    per_b = unplace_o(full, res["O"], L)
+    for b in range(3):
+        Lb = {k: ([v[b]] if isinstance(v, list) and len(v) == 3 else v) for k, v in L.items()}
+        one = place(Lb, "TND", "PA_BSND", bs=16, seed=2)
+        got = run_gpu(one)["O"]                   # b = 1 alone: no tiles in the launch at all
+        assert np.array_equal(got, per_b[b]), b
+
+
+def test_untiled_rows_of_a_tiled_launch_equal_the_untiled_launch_bitwise():
+    """The rows that are not tiled give the same bits with tiles off for the
+    whole call; the tiled rows agree with the oracle either way."""
+    import sparse_shared_kv_amd as s
+    L = _mixed_tile_batch()
+    P = place(L, "TND", "PA_BSND", bs=16, seed=1)
+    on = run_gpu(P)
+    off = run_gpu(P, s.Call(dict(P.params, query_tile=1), P.arrays))
+    assert np.array_equal(on["O"][20:], off["O"][20:])
+    assert np.array_equal(on["lse"][20:], off["lse"][20:])
+    assert not np.array_equal(on["O"][:20], off["O"][:20])   # the tiled rows took another order
+    ref = oracle.forward(P, rows=list(range(20)))
+    check_outputs(P, off, ref, list(range(20)))
+
+
+def test_tiled_metadata_from_other_params_is_rejected():
+    import sparse_shared_kv_amd as s
+    P = synth.make_workload("swa_prefill")
+    call = s.Call(P.params, P.arrays)
+    other = dict(P.params, ori_win_left=63)
+    call_b = s.Call(other, P.arrays)
+    call_b.plan()
+    call.metadata.copy_(call_b.metadata)       # plan of different parameters (same size)
+    call.status.zero_()
+    call.forward()
+    torch.cuda.synchronize()
+    assert torch.isnan(call.out.float()).all()
+    assert int(call.status.item()) & 1
+    # a plan made with tiles off does not serve a call with tiles
+    call_c = s.Call(dict(P.params, query_tile=1), P.arrays)
+    call_c.plan()
+    call.metadata.zero_()
+    call.metadata[:call_c.metadata.numel()].copy_(call_c.metadata)
+    call.status.zero_()
+    call.out.zero_()
+    call.forward()
+    torch.cuda.synchronize()
+    assert torch.isnan(call.out.float()).all()
+    assert int(call.status.item()) & 1
+
+
+def test_tiled_graph_replay_matches_eager():
+    L = _mixed_tile_batch()
+    _graph_replay(place(L, "TND", "PA_BSND", bs=16, seed=1))
