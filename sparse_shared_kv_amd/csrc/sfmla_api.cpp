@@ -256,11 +256,12 @@ bool tile_eligible(const sfmla_params& p) {
          p.cmp_topk == 0 && tile_limit(p) >= 2;
 }
 
-// Query rows per tile of this call (1: no tiles).  By rule: the most the
-// waves hold, where a sequence may be long enough to be a prefill.  Which
-// sequences are tiled is decided on the device from each sequence's own
-// lengths (at least kMinTileQueries valid queries by rule, any number when
-// forced, and a tile's union list within one split).
+// Most query rows per tile of this call (1: no tiles).  By rule: the most
+// the waves hold, where a sequence may be long enough to be a prefill.
+// Which sequences are tiled, and by rule with how many rows, is decided on
+// the device from each sequence's own lengths (at least kMinTileQueries
+// valid queries by rule, any number when forced, and a tile's union list
+// within one split).
 int query_tile(const sfmla_params& p) {
   if (p.query_tile == 1) return 1;
   if (p.query_tile > 1) return p.query_tile;        // validated
@@ -269,12 +270,13 @@ int query_tile(const sfmla_params& p) {
 }
 
 // Tile descriptors of a tiled call: at least the tiles any batch of these
-// parameters has (sum over sequences of ceil(len / tq) <= (q_t + b (tq - 1)) / tq,
-// and at most one per query row), rounded up to a multiple of 8 so that the
-// rows of untiled sequences that follow the tiles in the grid start on XCD 0.
+// parameters has (sum over sequences of ceil(len / tq) <= (q_t + b (tq - 1)) / tq
+// with the fewest rows per tile, and at most one per query row), rounded up
+// to a multiple of 8 so that the rows of untiled sequences that follow the
+// tiles in the grid start on XCD 0.
 int64_t tile_bound(const sfmla_params& p) {
-  const int tq = query_tile(p);
-  if (tq <= 1) return 0;
+  if (query_tile(p) <= 1) return 0;
+  const int tq = p.query_tile > 1 ? p.query_tile : 2;
   const int64_t n = std::min<int64_t>(((int64_t)p.q_t + (int64_t)p.batch_size * (tq - 1)) / tq,
                                       p.q_t);
   return (n + 7) / 8 * 8;
@@ -531,6 +533,7 @@ sfmla_status sfmla_metadata(const sfmla_params* params, const sfmla_lengths* len
   a.split_rows = split_rows(p);
   a.split_rows_long = std::max(a.split_rows, sfmla::kMaxSplitRows);
   a.tq = query_tile(p);
+  a.tile_auto = p.query_tile > 1 ? 0 : 1;
   a.tile_min_queries = p.query_tile > 1 ? 1 : sfmla::kMinTileQueries;
   a.tile_bound = (int32_t)tile_bound(p);
   a.tile_off = (int64_t)tile_off(p);

@@ -49,7 +49,8 @@ struct PlanArgs {
   int32_t max_splits;
   int32_t split_rows;               // KV rows per split (multiple of the tile, <= kMaxSplitRows)
   int32_t split_rows_long;          // the longest split of a row of a sequence with many queries
-  int32_t tq;                       // query rows per tile (1: no tiles)
+  int32_t tq;                       // most query rows per tile (1: no tiles)
+  int32_t tile_auto;                // rows per tile by each sequence's valid queries (else tq)
   int32_t tile_min_queries;         // valid queries from which a sequence is tiled
   int32_t tile_bound;               // tile descriptors written
   int64_t tile_off;                 // int offset of the descriptors in meta
@@ -66,7 +67,7 @@ struct FwdArgs {
   int32_t bpg;                      // 16-head blocks per head group (<= waves; spare waves only load)
   int32_t split_rows;               // list positions per split of a short-query row
   int32_t merge_wait_ticks;         // owned-merge wait bound (s_memrealtime ticks; 0: none)
-  int32_t tq;                       // query rows per tile (tiled launch)
+  int32_t tq;                       // most query rows per tile (tiled launch)
   int32_t nb;                       // 16-head blocks per query row (tiled launch)
   int32_t tile_units;               // tiled launch: workgroups of the tiles (a multiple of 8);
                                     // the rows of untiled sequences follow

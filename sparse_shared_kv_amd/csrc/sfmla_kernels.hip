@@ -179,25 +179,34 @@ __device__ __forceinline__ SeqLens seq_lens(const PlanArgs& a, int b) {
   return s;
 }
 
-// Whether the rows of a sequence go in query tiles: a decision from the
-// sequence's own lengths (so a sequence is tiled the same way in any batch),
-// taken where tiles are possible at all (a.tq > 1): enough valid queries,
-// and a bound on the union of a tile's lists within one split.  The union
-// of tq consecutive rows' windows spans at most win_left + win_right + tq
-// positions (each row's window is its predecessor's moved by one), every
-// rule list lies within the sequence's ori rows, and the visible compressed
-// rows of any row lie within the sequence's compressed rows.
-__device__ __forceinline__ bool seq_tiled(const PlanArgs& a, const SeqLens& s) {
+// Query rows per tile of a sequence (0: its rows are not tiled): a decision
+// from the sequence's own lengths, so a sequence is tiled the same way in any
+// batch, taken where tiles are possible at all (a.tq > 1).  It needs enough
+// valid queries and a bound on the union of a tile's lists within one split:
+// the union of tq consecutive rows' windows spans at most win_left +
+// win_right + tq positions (each row's window is its predecessor's moved by
+// one), every rule list lies within the sequence's ori rows, and the visible
+// compressed rows of any row lie within the sequence's compressed rows.  By
+// rule (a.tile_auto) the tile grows from 2 rows up to a.tq while the
+// sequence still has 128 valid queries per 2 rows of tile (about 64 tiles
+// per sequence, so that short prefills still fill the chip); otherwise every
+// tiled sequence takes a.tq.
+__device__ __forceinline__ int seq_tile_rows(const PlanArgs& a, const SeqLens& s) {
   const sfmla_params& p = a.p;
-  if (a.tq < 2 || s.q_used < a.tile_min_queries) return false;
+  if (a.tq < 2 || s.q_used < a.tile_min_queries) return 0;
+  int tq = a.tq;
+  if (a.tile_auto) {
+    tq = 2;
+    while (tq < a.tq && tq * 2 * 64 <= s.q_used) tq *= 2;
+  }
   int64_t n = max(s.ori_len, 0);
   if (p.ori_mask_mode == SFMLA_MASK_BAND && p.ori_win_left >= 0 && p.ori_win_right >= 0)
-    n = min(n, (int64_t)p.ori_win_left + p.ori_win_right + a.tq);
+    n = min(n, (int64_t)p.ori_win_left + p.ori_win_right + tq);
   if (p.has_cmp_kv) n += max(s.cmp_len, 0);
-  return n <= kMaxSplitRows;
+  return n <= kMaxSplitRows ? tq : 0;
 }
 
-// Query tiles of a.tq consecutive rows of the tiled sequences, numbered
+// Query tiles of consecutive rows of the tiled sequences, numbered
 // sequence by sequence with no gaps, so that the workgroups of the tiled
 // launch that find no tile all come after the real ones.  One workgroup:
 // sequences go in chunks of kPlanThreads, an LDS scan of their tile counts
@@ -208,17 +217,19 @@ __device__ __forceinline__ bool seq_tiled(const PlanArgs& a, const SeqLens& s) {
 __device__ void plan_tiles(const PlanArgs& a) {
   const sfmla_params& p = a.p;
   __shared__ int32_t s_scan[kPlanThreads], s_first[kPlanThreads], s_row0[kPlanThreads],
-      s_len[kPlanThreads];
-  const int tid = threadIdx.x, tq = a.tq;
+      s_len[kPlanThreads], s_tq[kPlanThreads];
+  const int tid = threadIdx.x;
   int32_t* desc = a.meta + a.tile_off;
   int64_t base = 0;                              // tiles of the chunks before
   for (int b0 = 0; b0 < p.batch_size; b0 += kPlanThreads) {
     const int b = b0 + tid;
-    int r0 = 0, len = 0;
+    int r0 = 0, len = 0, tq = 1;
     if (b < p.batch_size) {
       const SeqLens sl = seq_lens(a, b);
       r0 = p.layout_q == SFMLA_LAYOUT_BSND ? b * p.q_s : a.len.cu_seqlens_q[b];
-      len = seq_tiled(a, sl) ? sl.q_len : 0;
+      tq = seq_tile_rows(a, sl);
+      len = tq > 0 ? sl.q_len : 0;
+      tq = max(tq, 1);
       if (r0 < 0 || r0 >= p.q_t) len = 0;
       len = max(0, min(len, p.q_t - max(r0, 0)));
     }
@@ -236,6 +247,7 @@ __device__ void plan_tiles(const PlanArgs& a) {
     s_first[tid] = v - cnt;
     s_row0[tid] = r0;
     s_len[tid] = len;
+    s_tq[tid] = tq;
     __syncthreads();
     const int total = s_scan[kPlanThreads - 1];
     const int last = min(kPlanThreads, p.batch_size - b0) - 1;
@@ -246,7 +258,7 @@ __device__ void plan_tiles(const PlanArgs& a) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_first[mid] <= u) lo = mid; else hi = mid - 1;
       }
-      const int k = u - s_first[lo];
+      const int k = u - s_first[lo], tq = s_tq[lo];
       const int64_t gu = base + u;
       if (gu < a.tile_bound)
         *(int2*)(desc + kTileDescInts * gu) =
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const SeqLens sl = seq_lens(a, b);
   const int q_used = sl.q_used, ori_len = sl.ori_len, ori_base = sl.ori_base;
   const int cmp_len = sl.cmp_len, cmp_base = sl.cmp_base, res = sl.res;
-  const int tiled = seq_tiled(a, sl);
+  const int tiled = seq_tile_rows(a, sl) > 0;
 
   const int valid = i < q_used;
   const int pos = ori_len - q_used + i;

@@ -323,15 +323,19 @@ def _meta_ints(P, **over):
 def test_query_tile_rule_sizes_the_tile_descriptors():
     """Tiles by rule need rule lists, 16-bit rows, at most 64 heads and
     max_seqlen_q >= 16; the plan then holds one (first row, row count) pair
-    per possible tile: ceil((q_t + b (tq - 1)) / tq), at most q_t, rounded up
-    to a multiple of 8."""
+    per possible tile of the fewest rows (2 by rule, the forced count
+    otherwise): (q_t + b (tq - 1)) / tq, at most q_t, rounded up to a
+    multiple of 8."""
     base_ints = lambda P: 16 + (16 + 64) * P.params["q_t"]
     up8 = lambda n: (n + 7) // 8 * 8
-    for name, tq in (("swa_prefill", 2), ("hca_prefill", 2), ("swa_prefill_h16", 8)):
+    bound = lambda P, tq: up8(min(P.params["q_t"], (P.params["q_t"] + P.params["batch_size"] *
+                                                    (tq - 1)) // tq))
+    for name in ("swa_prefill", "hca_prefill", "swa_prefill_h16"):
         P = synth.make_workload(name)
-        q_t, B = P.params["q_t"], P.params["batch_size"]
-        assert _meta_ints(P) == base_ints(P) + 2 * up8(min(q_t, (q_t + B * (tq - 1)) // tq)), name
+        assert _meta_ints(P) == base_ints(P) + 2 * bound(P, 2), name
         assert _meta_ints(P, query_tile=1) == base_ints(P), name      # tiles off
+    P = synth.make_workload("swa_prefill_h16")
+    assert _meta_ints(P, query_tile=8) == base_ints(P) + 2 * bound(P, 8)
     # TopK lists (csa), packed rows and 128 heads are never tiled
     for name in ("csa_prefill", "c8_packed_int8_q32", "hca_varlen_q32", "swa_decode"):
         P = synth.make_workload(name)
