@@ -215,8 +215,12 @@ typedef struct sfmla_lengths {
  * non-contiguous rows with inter-row padding are allowed).
  *
  *   q            bf16 (float16 for SFMLA_KV_FP16), contiguous
- *                (q_t, num_heads_q, 512 + rope); "bf16" below reads float16
- *                for that format
+ *                (q_t, num_heads_q, 512 + rope), or (q_t, num_heads_q, 512)
+ *                when q_rope is given; "bf16" below reads float16 for that
+ *                format
+ *   q_rope       the query's rope part stored apart (SparseFlashAttention
+ *                README, 参数说明 query_rope): bf16, contiguous
+ *                (q_t, num_heads_q, 64), rope_head_dim 64 only; else NULL
  *   ori_kv       bf16 rows: 512 nope values, then (if rope_head_dim = 64 and
  *                ori_rope is NULL) 64 rope values; packed rows: 512 codes,
  *                2*rope bytes of bf16 rope, 16 bytes of fp32 scales
@@ -248,6 +252,7 @@ typedef struct sfmla_tensors {
   void* attention_out;
   float* softmax_lse;
   int32_t* status;
+  const void* q_rope;
 } sfmla_tensors;
 
 /* Number of int32 the plan of these parameters occupies (host only). */

@@ -245,11 +245,21 @@ class Call:
         contiguous with their pages' dtypes; KV pools with contiguous rows."""
         d = self.d
         half = torch.float16 if self.spec.get("kv_dtype") == "fp16" else torch.bfloat16
-        for name in ("q",):
+        rope = int(self.params.rope_head_dim)
+        q_rope = d.get("q_rope")
+        q_t, qn = int(self.params.q_t), int(self.params.num_heads_q)
+        for name in ("q", "q_rope"):
+            if d.get(name) is None:
+                continue
             if d[name].dtype not in (half, torch.int16):
-                raise SfmlaError(1, "q must be %s (or its int16 bits)" % half)
+                raise SfmlaError(1, "%s must be %s (or its int16 bits)" % (name, half))
             if not d[name].is_contiguous():
-                raise SfmlaError(1, "q must be contiguous")
+                raise SfmlaError(1, "%s must be contiguous" % name)
+        want = (q_t, qn, 512 if q_rope is not None else 512 + rope)
+        if tuple(d["q"].shape) != want:
+            raise SfmlaError(1, "q must have shape %s, got %s" % (want, tuple(d["q"].shape)))
+        if q_rope is not None and tuple(q_rope.shape) != (q_t, qn, rope):
+            raise SfmlaError(1, "q_rope must have shape %s" % ((q_t, qn, rope),))
         for name in ("ori_block_table", "cmp_block_table", "ori_sparse_indices",
                      "cmp_sparse_indices") + tuple(n for n, _ in Lengths._fields_):
             _require(d.get(name), name, torch.int32)
@@ -270,6 +280,8 @@ class Call:
             return x.stride(0) * x.element_size() if x is not None else 0
 
         t.q = d["q"].data_ptr()
+        if d.get("q_rope") is not None:
+            t.q_rope = d["q_rope"].data_ptr()
         t.ori_kv = d["ori_kv"].data_ptr()
         t.ori_kv_stride = row_bytes(d["ori_kv"])
         if d.get("ori_v") is not None:

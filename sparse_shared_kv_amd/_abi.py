@@ -63,6 +63,7 @@ class Tensors(ctypes.Structure):
         ("ori_block_table", _vp), ("cmp_block_table", _vp),
         ("ori_sparse_indices", _vp), ("cmp_sparse_indices", _vp),
         ("sinks", _vp), ("attention_out", _vp), ("softmax_lse", _vp), ("status", _vp),
+        ("q_rope", _vp),
     ]
 
 

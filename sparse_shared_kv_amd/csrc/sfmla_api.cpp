@@ -369,6 +369,8 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
                 metadata_ints(p));
   REQUIRE(std::isfinite(scale), "softmax_scale must be finite");
   REQUIRE(t->q && aligned16(t->q), "q must be a 16-byte aligned device pointer");
+  REQUIRE(!t->q_rope || (p.rope_head_dim == 64 && aligned16(t->q_rope)),
+          "q_rope needs rope_head_dim 64 and a 16-byte aligned device pointer");
   REQUIRE(t->ori_kv && aligned16(t->ori_kv), "ori_kv must be a 16-byte aligned device pointer");
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int64_t need_row = packed ? 512 + 2 * p.rope_head_dim + 16
@@ -442,6 +444,8 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
   f.scale_log2 = scale * 1.4426950408889634f;
   f.meta = meta;
   f.q = (const uint16_t*)t->q;
+  f.q_rope = (const uint16_t*)t->q_rope;
+  f.q_stride = t->q_rope ? 512u : (uint32_t)(512 + p.rope_head_dim);
   f.ori_kv = (const char*)t->ori_kv;
   f.ori_stride = (uint32_t)t->ori_kv_stride;
   f.ori_rope = (const char*)t->ori_rope;

@@ -76,6 +76,8 @@ struct FwdArgs {
   float scale_log2;                 // softmax_scale * log2(e)
   const int32_t* meta;
   const uint16_t* q;
+  const uint16_t* q_rope;           // rope part of the query stored apart (else null)
+  uint32_t q_stride;                // elements per (row, head) of q: 512 + rope, or 512
   // row strides in bytes (< 2^31, so a row's offset is one 32 x 32 -> 64 multiply-add)
   const char* ori_kv;   uint32_t ori_stride;
   const char* ori_rope; uint32_t ori_rope_stride;

@@ -1030,10 +1030,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         // here also keeps it from being held until the epilogue)
         const int h = h0 + 16 * hb + t;
         const int qi = orow * a.qn + (h < a.qn ? h : 0);
-        const uint16_t* qp = a.q + (uint32_t)qi * (uint64_t)DQK + 8 * g;
+        const uint16_t* qp = a.q + (uint32_t)qi * (uint64_t)a.q_stride + 8 * g;
+        // the rope k-steps (16, 17) read q_rope when it is stored apart
+        const uint16_t* qr = a.q_rope ? a.q_rope + (uint32_t)qi * (uint64_t)64 + 8 * g - 512 : qp;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
+          qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)((ks < 16 ? qp : qr) + 32 * ks));
       }
     });
     for (int i0 = PPT * NTHR; i0 < ntT; i0 += PPT * NTHR) batch(i0, false, [] {});

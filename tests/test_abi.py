@@ -375,3 +375,31 @@ def test_tiled_call_lays_out_split_rows_with_every_head_in_one_group():
     # without tiles the 64 heads take 4 waves per group of the same size
     assert s.sfmla_workspace_size(s.make_params(dict(P.params, max_seqlen_cmp_kv=4096,
                                                      query_tile=1), P.arrays)) > 0
+
+
+def test_q_rope_apart_is_validated():
+    """query_rope stored apart (SparseFlashAttention README, 参数说明):
+    only with rope 64; the binding checks both shapes."""
+    import torch
+    P = synth.random_tiny(41, family="sfa", rope_head_dim=64, num_heads_q=4)
+    q = P.arrays["q"]
+    split = dict(P.arrays, q=np.ascontiguousarray(q[..., :512]),
+                 q_rope=np.ascontiguousarray(q[..., 512:]))
+    s.Call(P.params, split, device="cpu")                       # accepted
+    with pytest.raises(s.SfmlaError, match="q must have shape"):
+        s.Call(P.params, dict(P.arrays, q_rope=split["q_rope"]), device="cpu")
+    with pytest.raises(s.SfmlaError, match="q_rope must have shape"):
+        s.Call(P.params, dict(split, q_rope=np.ascontiguousarray(q[..., 512:544])), device="cpu")
+    # the library refuses q_rope without rope before anything is launched
+    lib = s._abi.load()
+    P0 = synth.random_tiny(42, family="sfa", rope_head_dim=0, num_heads_q=4)
+    p = s.make_params(P0.params, P0.arrays)
+    t = s._abi.Tensors()
+    t.q = t.ori_kv = t.attention_out = t.q_rope = 4096
+    t.ori_kv_stride = 1024
+    t.ori_sparse_indices = 4096
+    n = ctypes.c_size_t()
+    assert lib.sfmla_metadata_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    st = lib.sfmla_forward(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(4096), n.value,
+                           ctypes.c_float(0.05), None, 0, None)
+    assert st == 1 and b"q_rope" in lib.sfmla_last_error()

@@ -684,3 +684,29 @@ def test_tiled_metadata_from_other_params_is_rejected():
 def test_tiled_graph_replay_matches_eager():
     L = _mixed_tile_batch()
     _graph_replay(place(L, "TND", "PA_BSND", bs=16, seed=1))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(seed=801, family="sfa", separate_v=True, num_heads_q=128, max_kv=3000, topk=1100),
+    dict(seed=802, family="sfa", kv_dtype="int8_packed", num_heads_q=20, max_kv=900),
+    dict(seed=803, family="sfa", kv_dtype="fp16", num_heads_q=16, separate_v=False),
+    dict(seed=804, family="hca", num_heads_q=32, max_q=20, max_kv=300, query_tile=4),
+], ids=["bf16_separate_v", "int8_packed", "fp16", "tiles"])
+def test_q_rope_apart_matches_concatenated_bitwise(kw):
+    """The query's rope part passed as its own tensor (SparseFlashAttention
+    README, 参数说明 query_rope) gives the same bits as one 576-wide q."""
+    import sparse_shared_kv_amd as s
+    kw = dict(kw, rope_head_dim=64, lse=True)
+    tq = kw.pop("query_tile", 0)
+    P = synth.random_tiny(**kw)
+    spec = dict(P.params, query_tile=tq)
+    q = P.arrays["q"]
+    split = dict(P.arrays, q=np.ascontiguousarray(q[..., :512]),
+                 q_rope=np.ascontiguousarray(q[..., 512:]))
+    one = run_gpu(P, s.Call(spec, P.arrays))
+    two = run_gpu(P, s.Call(spec, split))
+    assert one["status"] == 0 and two["status"] == 0
+    assert np.array_equal(one["O"], two["O"])
+    assert np.array_equal(one["lse"], two["lse"])
+    rows = list(range(min(4, P.query_rows)))
+    check_outputs(P, two, oracle.forward(P, rows=rows), rows)
