@@ -342,7 +342,15 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
   const int hpw = heads_per_wave(p);
   const int blocks = (p.num_heads_q + hpw - 1) / hpw;  // head blocks of one wave each
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
-  const int wmax = packed ? 4 : 8;                     // packed rows: more registers per wave
+  // Packed rows: four waves (one per SIMD, the whole register file for the
+  // decode), or eight where a row has eight head blocks and the launch keeps
+  // kMinGroups workgroups with all of them in one group: each row is then
+  // gathered and decoded once instead of once per head group (throughput
+  // mode: c8_packed_int8_q32 475 -> 372 us; at the packed configuration's
+  // 8 rows four waves stay faster, 40 vs 49 us).  The two kernels give the
+  // same bits (same per-wave arithmetic; the merge adds splits in order).
+  int wmax = 8;
+  if (packed && !(blocks >= 8 && units >= kMinGroups) && p.head_blocks_per_group != 8) wmax = 4;
   *nw = wmax;
   // params.head_blocks_per_group, when nonzero, overrides the rule
   if (p.head_blocks_per_group) {

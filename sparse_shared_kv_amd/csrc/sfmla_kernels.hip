@@ -967,7 +967,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // for the table entries does not wait for Q, which travels while the
   // entries go to LDS.  Every load here is an ordinary one the compiler
   // tracks: it places the waits for its results itself.
-  bf16x8 qreg[HB][NKS];
+  // Q slices held in registers: every k-step, except on the eight-wave packed
+  // kernel with rope, whose two waves per SIMD keep the two rope k-steps in
+  // LDS (16 KB; loaded two MFMA steps ahead of their use)
+  constexpr int NQR = (PK && NW == 8 && C::ROPE) ? 16 : NKS;
+  __shared__ __align__(16) bf16x8 sQr[NQR < NKS ? NW : 1][NQR < NKS ? NKS - NQR : 1][64];
+  bf16x8 qreg[HB][NQR];
+  bf16x8 qrt[NQR < NKS ? NKS - NQR : 1];
   // ---- resolve every list position of this split once, into physical row
   //      entries in LDS (empty or masked slots: kNoRow).  Positions go in
   //      batches of PPT per thread: the index loads of a batch, then its
@@ -1034,12 +1040,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         // the rope k-steps (16, 17) read q_rope when it is stored apart
         const uint16_t* qr = a.q_rope ? a.q_rope + (uint32_t)qi * (uint64_t)64 + 8 * g - 512 : qp;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          qreg[hb][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)((ks < 16 ? qp : qr) + 32 * ks));
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 v = __builtin_bit_cast(bf16x8, *(const uint4*)((ks < 16 ? qp : qr) + 32 * ks));
+          if (ks < NQR) qreg[hb][ks < NQR ? ks : 0] = v;
+          else qrt[ks - NQR] = v;
+        }
       }
     });
     for (int i0 = PPT * NTHR; i0 < ntT; i0 += PPT * NTHR) batch(i0, false, [] {});
   }
+  // one more tile of empty entries after the resolved positions: a read of
+  // the row table past them finds the zero row, never stale LDS
+  if (tid < T) sRow[nt * T + tid] = kNoRow;
   if (OUTCNT && tid == 0) sOut = 0;
   if (OUTCNT && tid < NW) sReady[tid] = 0;
   if constexpr (PK) {
@@ -1102,9 +1114,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) kb[i] = kload(i);
         f32x4 sp[HB], scq;
+        bf16x8 qlds[NQR < NKS ? NKS - NQR : 1];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (NQR < NKS) {
+            if (ks + 2 >= NQR && ks + 2 < NKS) qlds[ks + 2 - NQR] = sQr[w][ks + 2 - NQR][l];
+          }
           const bf16x8 kv = kb[ks % PF];
           if (ks < 16 && ks % 4 == 0)   // this lane's rows' scales of the tile
             scq = *(const f32x4*)(sScale + (ks / 4) * T + 16 * half + 4 * g);
@@ -1112,10 +1128,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           for (int hb = 0; hb < HB; ++hb) {
             if (ks < 16) {
               const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-              sp[hb] = mfma16<HALF>(kv, qreg[hb][ks], ks % 4 ? sp[hb] : z);
+              sp[hb] = mfma16<HALF>(kv, qreg[hb][ks < NQR ? ks : 0], ks % 4 ? sp[hb] : z);
               if (ks % 4 == 3) s[hb][half] += sp[hb] * scq;
             } else {
-              s[hb][half] = mfma16<HALF>(kv, qreg[hb][ks], s[hb][half]);
+              const bf16x8 qv = ks < NQR ? qreg[hb][ks < NQR ? ks : 0] : qlds[ks >= NQR ? ks - NQR : 0];
+              s[hb][half] = mfma16<HALF>(kv, qv, s[hb][half]);
             }
           }
           if (ks + PF < NKS) kb[ks % PF] = kload(ks + PF);
@@ -1144,8 +1161,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         const bf16x8 k0v = kb[ks % PF][0], k1v = kb[ks % PF][1];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-          s[hb][0] = mfma16<HALF>(k0v, qreg[hb][ks], s[hb][0]);
-          s[hb][1] = mfma16<HALF>(k1v, qreg[hb][ks], s[hb][1]);
+          s[hb][0] = mfma16<HALF>(k0v, qreg[hb][ks < NQR ? ks : 0], s[hb][0]);
+          s[hb][1] = mfma16<HALF>(k1v, qreg[hb][ks < NQR ? ks : 0], s[hb][1]);
         }
         if (ks + PF < NKS) kload(ks + PF, kb[ks % PF][0], kb[ks % PF][1]);
       }
@@ -1243,6 +1260,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     if (nt > 0) issue_raw<NW, DQK>(a, sRow, 0, lds_addr(sW0), w, l);
     wait_vmcnt<0>();                            // raw(0) and the Q slices
     settle(qreg);
+    if constexpr (NQR < NKS) {                  // the rope slices to this wave's LDS rows
+#pragma unroll
+      for (int i = 0; i < NKS - NQR; ++i) sQr[w][i][l] = qrt[i];
+    }
     if (nt > 1) issue_raw<NW, DQK>(a, sRow, T, lds_addr(sW1), w, l);
     for (int tt = 0; tt < nt; tt += 3) {
       step(tt, sW0, sW2);
@@ -1833,19 +1854,29 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int groups, int merge_wait_us, 
   return hipGetLastError();
 }
 
-// Eight waves per workgroup for bf16 rows; four for packed rows, whose
-// decode needs more registers per wave.
+// Eight waves per workgroup for bf16 rows; four or eight for packed rows
+// (four: one wave per SIMD with the whole register file for the decode;
+// eight: every head of a row in one workgroup, each row gathered and
+// decoded once).  Both give the same bits.
+template <int FMT>
+static hipError_t launch_packed(const FwdArgs& a, int nw, int dqk, int groups, int mw,
+                                hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (nw == 8)
+    return dqk == 512 ? launch_fwd_t<8, 512, 0, FMT>(a, groups, mw, s, t0, t1)
+                      : launch_fwd_t<8, 576, 0, FMT>(a, groups, mw, s, t0, t1);
+  if (nw == 4)
+    return dqk == 512 ? launch_fwd_t<4, 512, 0, FMT>(a, groups, mw, s, t0, t1)
+                      : launch_fwd_t<4, 576, 0, FMT>(a, groups, mw, s, t0, t1);
+  return hipErrorInvalidConfiguration;
+}
+
 hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
                           int mw, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   switch (fmt) {
     case SFMLA_KV_INT8_PACKED:
-      if (nw != 4) return hipErrorInvalidConfiguration;
-      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_INT8_PACKED>(a, groups, mw, s, t0, t1)
-                        : launch_fwd_t<4, 576, 0, SFMLA_KV_INT8_PACKED>(a, groups, mw, s, t0, t1);
+      return launch_packed<SFMLA_KV_INT8_PACKED>(a, nw, dqk, groups, mw, s, t0, t1);
     case SFMLA_KV_FP8_E4M3_PACKED:
-      if (nw != 4) return hipErrorInvalidConfiguration;
-      return dqk == 512 ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, mw, s, t0, t1)
-                        : launch_fwd_t<4, 576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, mw, s, t0, t1);
+      return launch_packed<SFMLA_KV_FP8_E4M3_PACKED>(a, nw, dqk, groups, mw, s, t0, t1);
     case SFMLA_KV_FP16:
       if (nw != 8) return hipErrorInvalidConfiguration;
       if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1)
