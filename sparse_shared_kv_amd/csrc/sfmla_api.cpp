@@ -346,8 +346,8 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
   // decode), or eight where a row has eight head blocks and the launch keeps
   // kMinGroups workgroups with all of them in one group: each row is then
   // gathered and decoded once instead of once per head group (throughput
-  // mode: c8_packed_int8_q32 475 -> 372 us; at the packed configuration's
-  // 8 rows four waves stay faster, 40 vs 49 us).  The two kernels give the
+  // mode: c8_packed_int8_q32 470 -> 280 us; at the packed configuration's
+  // 8 rows four waves stay faster, 40 vs 54 us).  The two kernels give the
   // same bits (same per-wave arithmetic; the merge adds splits in order).
   int wmax = 8;
   if (packed && !(blocks >= 8 && units >= kMinGroups) && p.head_blocks_per_group != 8) wmax = 4;

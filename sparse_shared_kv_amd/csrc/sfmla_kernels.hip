@@ -650,6 +650,17 @@ __device__ __forceinline__ void issue_v(const FwdArgs& a, const uint32_t* sRow, 
 // moving 64 consecutive 16-byte chunks, which may span several rows.  Padding
 // lanes (past the tile) read the zero row into the stage's tail so that every
 // wave issues the same number of loads.
+// A lane value the compiler cannot prove loop-invariant (an empty asm that
+// takes it and gives it back, in a register): per-lane addresses derived
+// from it are recomputed where they are used instead of being hoisted out
+// of the tile loop and held in registers (on the eight-wave packed kernel
+// they were spilled to scratch and reloaded every tile; the four-wave one
+// has the registers and keeps them).
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int NW, int DQK>
 struct PackedPipe {
   static constexpr int ROPE = DQK - 512;                     // rope values per row
@@ -663,6 +674,7 @@ template <int NW, int DQK>
 __device__ __forceinline__ void issue_raw(const FwdArgs& a, const uint32_t* sRow, int tbase,
                                           uint32_t ldsRaw, int w, int l) {
   using P = PackedPipe<NW, DQK>;
+  if constexpr (NW == 8) l = fresh(l);   // two waves per SIMD: no room for hoisted addresses
   const uint32_t base = __builtin_amdgcn_readfirstlane(ldsRaw + w * P::PER * 1024);
   // every row entry first (one LDS round trip for all), then branch-free
   // addresses: a slot without a row, and chunks past the tile (the last
@@ -697,6 +709,7 @@ __device__ __forceinline__ void decode_tile(const char* raw, char* kbf, float* s
   constexpr int NIT = kTile * 32 / NTHR;          // 16-code chunks per thread
   constexpr int U = NIT < 4 ? NIT : 4;            // chunks read before any is converted
   static_assert(kTile * 32 % NTHR == 0 && NIT % U == 0, "decode split");
+  if constexpr (NW == 8) tid = fresh(tid);
 #pragma unroll
   for (int i0 = 0; i0 < NIT; i0 += U) {
     uint4 c[U];
