@@ -10,7 +10,7 @@ namespace sfmla {
 
 constexpr int kTile = 32;          // KV rows staged in LDS per step
 constexpr int kMaxSplitRows = 2048;   // most KV rows per split of one query row (LDS row table)
-constexpr int kQueriesPerStep = 16;   // queries of a sequence per step of longer splits
+constexpr int kQueriesPerStep = 8;    // queries of a sequence per step of longer splits
 constexpr int kHeaderInts = 16;
 constexpr int kRecInts = 16;
 constexpr int kCounterInts = 64;   // arrival counters per query row (one per head group x wave)

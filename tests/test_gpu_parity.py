@@ -219,9 +219,10 @@ def test_batch_invariance_with_long_query_sequences_bitwise():
 
 
 def test_split_steps_by_query_count_bitwise():
-    """Sequences of 17, 33 and 48 queries take 1, 2 and 3 steps of the split
-    length (one per 16 queries); each sequence gives the same bits alone and
-    inside a batch, and matches the oracle."""
+    """Sequences of 17, 33 and 48 queries take 2, 4 and 6 steps of the split
+    length (one per 8 queries), the 2-query one the base length; each
+    sequence gives the same bits alone and inside a batch, and matches the
+    oracle."""
     L = logical(27, q_lens=[33, 17, 48, 2], ori_lens=[2600, 2200, 3000, 900], qn=32, ratio=2,
                 cmp_topk=900, win=(127, 0))
     full = place(L, "TND", "PA_BSND", bs=16, seed=1)
