@@ -692,15 +692,18 @@ def test_tiled_graph_replay_matches_eager():
     dict(seed=802, family="sfa", kv_dtype="int8_packed", num_heads_q=20, max_kv=900),
     dict(seed=803, family="sfa", kv_dtype="fp16", num_heads_q=16, separate_v=False),
     dict(seed=804, family="hca", num_heads_q=32, max_q=20, max_kv=300, query_tile=4),
-], ids=["bf16_separate_v", "int8_packed", "fp16", "tiles"])
+    dict(seed=805, family="sfa", kv_dtype="int8_packed", num_heads_q=128, max_kv=1500,
+         topk=900, head_blocks_per_group=8),
+], ids=["bf16_separate_v", "int8_packed", "fp16", "tiles", "int8_packed_eight_waves"])
 def test_q_rope_apart_matches_concatenated_bitwise(kw):
     """The query's rope part passed as its own tensor (SparseFlashAttention
     README, 参数说明 query_rope) gives the same bits as one 576-wide q."""
     import sparse_shared_kv_amd as s
     kw = dict(kw, rope_head_dim=64, lse=True)
     tq = kw.pop("query_tile", 0)
+    bpg = kw.pop("head_blocks_per_group", 0)
     P = synth.random_tiny(**kw)
-    spec = dict(P.params, query_tile=tq)
+    spec = dict(P.params, query_tile=tq, head_blocks_per_group=bpg)
     q = P.arrays["q"]
     split = dict(P.arrays, q=np.ascontiguousarray(q[..., :512]),
                  q_rope=np.ascontiguousarray(q[..., 512:]))
