@@ -193,6 +193,7 @@ def make_params(spec: dict, arrays: dict) -> Params:
     p.head_blocks_per_group = int(g("head_blocks_per_group", 0))
     p.merge_wait_us = int(g("merge_wait_us", 0))
     p.query_tile = int(g("query_tile", 0))
+    p.wave_pairs = int(g("wave_pairs", 0))
     return p
 
 

@@ -43,6 +43,7 @@ class Params(ctypes.Structure):
         ("has_seqused_ori_kv", _i32), ("has_seqused_cmp_kv", _i32),
         ("has_cmp_residual_kv", _i32), ("split_rows", _i32),
         ("head_blocks_per_group", _i32), ("merge_wait_us", _i32), ("query_tile", _i32),
+        ("wave_pairs", _i32),
     ]
 
 

@@ -62,7 +62,7 @@ uint32_t fingerprint(const sfmla_params& p) {
       p.cmp_mask_mode, p.ori_win_left, p.ori_win_right, p.has_ori_kv, p.has_cmp_kv,
       p.kv_dtype, p.has_separate_v, p.has_sinks, p.return_softmax_lse, p.has_seqused_q,
       p.has_seqused_ori_kv, p.has_seqused_cmp_kv, p.has_cmp_residual_kv, p.split_rows,
-      p.head_blocks_per_group, p.merge_wait_us, p.query_tile};
+      p.head_blocks_per_group, p.merge_wait_us, p.query_tile, p.wave_pairs};
   for (int32_t v : f32) mix(v);
   mix(p.ori_kv_rows);
   mix(p.cmp_kv_rows);
@@ -74,8 +74,17 @@ int max_splits(const sfmla_params& p);
 int tile_limit(const sfmla_params& p);
 bool tile_eligible(const sfmla_params& p);
 // heads each wave holds (one 16-head MFMA block)
-int heads_per_wave(const sfmla_params&) { return 16; }
-void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg);
+void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg, bool* pair = nullptr);
+
+// Heads of split partial per wave, in units of 512 columns: 16, or 8 where
+// wave pairs split the columns (16 heads x 256 columns per wave).
+int heads_per_wave(const sfmla_params& p) {
+  int nw, groups, bpg;
+  bool pair = false;
+  choose_groups(p, &nw, &groups, &bpg, &pair);
+  return pair ? 8 : 16;
+}
+bool pair_eligible(const sfmla_params& p);
 
 sfmla_status validate(const sfmla_params* pp) {
   REQUIRE(pp != nullptr, "params is NULL");
@@ -137,6 +146,10 @@ sfmla_status validate(const sfmla_params* pp) {
   REQUIRE(p.query_tile == 0 || p.query_tile == 1 || p.query_tile == 2 || p.query_tile == 4 ||
               p.query_tile == 8,
           "query_tile must be 0, 1, 2, 4 or 8");
+  REQUIRE(p.wave_pairs >= 0 && p.wave_pairs <= 2, "wave_pairs must be 0, 1 or 2");
+  if (p.wave_pairs == 2)
+    REQUIRE(pair_eligible(p),
+            "wave_pairs 2 needs bf16 or float16 KV and no query tiles");
   if (p.query_tile > 1) {
     REQUIRE(tile_eligible(p) && p.query_tile <= tile_limit(p),
             "query_tile %d needs rule lists (ori_topk = cmp_topk = 0), bf16 or float16 KV "
@@ -322,6 +335,11 @@ WsLayout workspace_layout(const sfmla_params& p) {
 
 size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total; }
 
+// Wave pairs: 16-bit rows in a call without query tiles.
+bool pair_eligible(const sfmla_params& p) {
+  return (p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_FP16) && query_tile(p) <= 1;
+}
+
 // Workgroup shape: nw waves; the heads of a query row are cut into `groups`
 // head groups of bpg 16-head blocks (bpg <= nw), one block per wave, and the
 // waves past bpg only help gather.  All heads of a query row share one
@@ -329,7 +347,8 @@ size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total
 // few workgroups to spread over the chip; then the heads are spread over
 // more groups, each re-gathering the row's KV (mostly from L2).  The shape
 // never changes a result: every head is computed the same way in any group.
-void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
+void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg, bool* pair) {
+  if (pair) *pair = false;
   if (query_tile(p) > 1) {
     // with query tiles, an untiled sequence's rows take every head in one
     // workgroup (tiles keep the grid full)
@@ -339,8 +358,25 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg) {
     return;
   }
   const int64_t units = (int64_t)p.q_t * max_splits(p);
-  const int hpw = heads_per_wave(p);
-  const int blocks = (p.num_heads_q + hpw - 1) / hpw;  // head blocks of one wave each
+  // Wave pairs: eight waves, bpg pairs of 16 heads per head group (every
+  // wave's partial is 16 heads x 256 columns)
+  const bool pairs = p.wave_pairs == 2 ||
+                     (p.wave_pairs == 0 && pair_eligible(p) && p.head_blocks_per_group == 0 &&
+                      units < kMinGroups);
+  if (pairs) {
+    if (pair) *pair = true;
+    *nw = 8;
+    const int pblocks = (p.num_heads_q + 15) / 16;
+    int per = p.head_blocks_per_group ? std::min(p.head_blocks_per_group, 4) : 4;
+    per = std::min(per, pblocks);
+    if (per == 3) per = 2;
+    if (!p.head_blocks_per_group)
+      while (per > 1 && units * ((pblocks + per - 1) / per) < kMinGroups) per /= 2;
+    *bpg = per;
+    *groups = (pblocks + per - 1) / per;
+    return;
+  }
+  const int blocks = (p.num_heads_q + 15) / 16;       // 16-head blocks of one wave each
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   // Packed rows: four waves (one per SIMD, the whole register file for the
   // decode), or eight where a row has eight head blocks and the launch keeps
@@ -611,13 +647,14 @@ sfmla_status sfmla_forward(const sfmla_params* params, const sfmla_tensors* t,
     return ok();
   }
   int nw, groups, bpg;
-  choose_groups(p, &nw, &groups, &bpg);
+  bool pair = false;
+  choose_groups(p, &nw, &groups, &bpg, &pair);
   a.bpg = bpg;
   // the owned split merge waits at most this long for the row's other
   // splits (when the launch's workgroups are all resident at once)
   const int merge_wait_us = p.merge_wait_us == 0 ? kMergeWaitUs : std::max(0, p.merge_wait_us);
-  hipError_t e = sfmla::launch_forward(a, nw, dqk, vmode, p.kv_dtype, groups, merge_wait_us,
-                                       (hipStream_t)stream, t0, t1);
+  hipError_t e = sfmla::launch_forward(a, nw, pair, dqk, vmode, p.kv_dtype, groups,
+                                       merge_wait_us, (hipStream_t)stream, t0, t1);
   if (e != hipSuccess) return fail(SFMLA_ERR_LAUNCH, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -117,9 +117,10 @@ struct CombineArgs {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // t0 / t1 (may be null): events the dispatch stamps at the kernel's start / end
 // merge_wait_us: the owned-merge wait bound when every workgroup of the launch
-// can be resident at once (0: never wait)
-hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
-                          int merge_wait_us, hipStream_t s, hipEvent_t t0 = nullptr,
+// can be resident at once (0: never wait); pair: the eight-wave kernel whose
+// wave pairs share 16 heads (16-bit rows, a.bpg pairs per head group)
+hipError_t launch_forward(const FwdArgs& a, int nw, bool pair, int dqk, int vmode, int fmt,
+                          int groups, int merge_wait_us, hipStream_t s, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);
 // launch with query tiles: a.tile_units workgroups for the tiles (one each,
 // a.tq rows), then one per (split, row) of the rows of untiled sequences

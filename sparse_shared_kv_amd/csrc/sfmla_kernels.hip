@@ -773,7 +773,14 @@ __device__ __forceinline__ int posn_of(int i0, int u, int tid, int w, int l) {
 // head block w % a.nb and masks the union positions its row's list does not
 // hold.  The rows of sequences that are not tiled follow, one workgroup per
 // (split, row) with every head (one head group), as without tiles.
-template <int NW, int HB, int DQK, int VMODE, int FMT, bool TILED = false>
+// PAIR: two waves share 16 heads.  Each computes the scores of one 16-row
+// half of every tile, the pair swaps its raw scores through LDS, both run the
+// same softmax over all 32 rows, and each accumulates half of the value
+// columns (16 heads x 256 columns of accumulators): a row of at most 64
+// heads keeps all eight waves, two per SIMD, in the products.  Every MFMA
+// and every softmax step is the one a single wave holding those heads would
+// take, so the results are the same bits.
+template <int NW, int HB, int DQK, int VMODE, int FMT, bool TILED = false, bool PAIR = false>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   using C = Pipe<NW, DQK, VMODE>;
   using PP = PackedPipe<NW, DQK>;
@@ -781,12 +788,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   constexpr bool PK = FMT != SFMLA_KV_BF16 && !HALF;   // packed rows (V = decoded nope)
   static_assert(!PK || VMODE == 0, "packed KV has no separate V");
   static_assert(!TILED || (!PK && NW == 8 && HB == 1), "query tiles: 16-bit rows, 8 waves");
+  static_assert(!PAIR || (!PK && !TILED && NW == 8 && HB == 1), "wave pairs: 16-bit rows, 8 waves");
   static_assert(FMT == SFMLA_KV_BF16 || FMT == SFMLA_KV_INT8_PACKED ||
                 FMT == SFMLA_KV_FP8_E4M3_PACKED || FMT == SFMLA_KV_FP16, "KV format");
   constexpr int T = C::T;
   constexpr int NKS = DQK / 32;
   constexpr int NTHR = NW * 64;
-  constexpr int HPW = 16 * HB;                     // heads per wave
+  constexpr int HPW = 16 * HB;                     // heads per wave (per pair)
+  constexpr int NMB = PAIR ? 16 : 32;              // 16-column blocks of O per wave
+  constexpr int NPW = PAIR ? NW / 2 : NW;          // head-holding units (waves or pairs)
   constexpr int RS = C::RSTR;
   // bf16, separate V: two K stages and two V stages; bf16, aliased V: three K
   // stages; packed: three raw stages and one decoded K tile (sK0)
@@ -804,7 +814,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // K / V stage buffers (two waves per buffer) once every wave of the
   // workgroup is done with them (sOut counts the waves out); owning waves
   // (below) land the other splits' partials there
-  constexpr bool STAGE = VMODE && !PK;
+  constexpr bool STAGE = VMODE && !PK && !PAIR;
   constexpr bool OUTCNT = !PK;
   constexpr int kStgRow = 1040;                      // staged output row (one head), padded
   static_assert(!STAGE || (NW == 8 && 2 * 16 * kStgRow <= T * RS && T * RS <= C::KBYTES),
@@ -813,15 +823,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // V = K nope: two more landing slots for the owned merge (the separate-V
   // kernel has its V stages for them; the tiled kernel merges splits of its
   // untiled rows with the last split to arrive)
-  __shared__ __align__(16) char sM[(VMODE || PK || TILED) ? 16 : 32768];
+  __shared__ __align__(16) char sM[(VMODE || PK || TILED || PAIR) ? 16 : 32768];
   // owned merge: per owning wave, every split's weight and the normaliser
   // per head, and a flag (1: landed and weighted, 2: handed off)
-  __shared__ float sWs[(PK || TILED) ? 1 : NW][(PK || TILED) ? 1 : kMaxOwnerSplits][16];
-  __shared__ float sInv[(PK || TILED) ? 1 : NW][16];
+  __shared__ float sWs[(PK || TILED || PAIR) ? 1 : NW][(PK || TILED || PAIR) ? 1 : kMaxOwnerSplits][16];
+  __shared__ float sInv[(PK || TILED || PAIR) ? 1 : NW][16];
+  // wave pairs: each wave's raw scores of its 16 tile rows, per head block
+  __shared__ __align__(16) f32x4 sSx[PAIR ? NW : 1][PAIR ? HB : 1][64];
   __shared__ int32_t sReady[NW];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g = l >> 4, t = l & 15;
+  const int hf = PAIR ? (w & 1) : 0;                // wave pairs: this wave's half
+  const int wp = PAIR ? (w >> 1) : w;               // head-holding unit
   // NaN outputs of query row r for this wave's heads (a plan that does not
   // match, or a list longer than the parameters allow)
   auto fail_row = [&](int r, int hfirst, bool on) {
@@ -918,8 +932,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     if (row >= a.q_t) return;
     orow = row;
     // a head group holds a.bpg 16-head blocks; waves past them only gather
-    h0 = (hg * a.bpg + w) * HPW;                    // first head of this wave
-    wave_on = w < a.bpg && h0 < a.qn;
+    h0 = (hg * a.bpg + wp) * HPW;                   // first head of this wave
+    wave_on = wp < a.bpg && h0 < a.qn;
 
     // The row's plan record is read together with the plan header (the buffer
     // always holds both; its size is checked on the host), so the two reads
@@ -1072,11 +1086,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     block_barrier();
   }
 
-  f32x4 o[HB][32];
+  f32x4 o[HB][NMB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) o[hb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < NMB; ++mb) o[hb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[HB], l_run[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) { m_run[hb] = kNegInf; l_run[hb] = 0.f; }
@@ -1151,6 +1165,45 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           if (ks + PF < NKS) kb[ks % PF] = kload(ks + PF);
         }
       }
+    } else if constexpr (PAIR) {
+      // this wave's 16 rows of the tile; the partner's scores come through LDS
+      f32x4 sm[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) sm[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (wave_on) {
+        const int r = 16 * hf + t;
+        const char* kp = sK + r * RS + 16 * g;
+        auto kload = [&](int ks) -> bf16x8 {
+          if (!C::ROPE || ks < 16) return *(const bf16x8*)(kp + 64 * ks);
+          const int c = 4 * (ks - 16) + g;
+          return *(const bf16x8*)(sR + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
+        };
+        constexpr int PF = 4;
+        bf16x8 kb[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) kb[i] = kload(i);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 kv = kb[ks % PF];
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) sm[hb] = mfma16<HALF>(kv, qreg[hb][ks], sm[hb]);
+          if (ks + PF < NKS) kb[ks % PF] = kload(ks + PF);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) sSx[w][hb][l] = sm[hb];
+      }
+      wait_lgkm0();
+      block_barrier();                              // both halves' scores are in
+      if (wave_on) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const f32x4 so = sSx[w ^ 1][hb][l];
+          s[hb][0] = hf ? so : sm[hb];
+          s[hb][1] = hf ? sm[hb] : so;
+        }
+      }
     } else {
       const char* kp0 = sK + t * RS + 16 * g;
       const char* kp1 = kp0 + 16 * RS;
@@ -1215,7 +1268,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int mb = 0; mb < 32; ++mb) o[hb][mb] *= alpha[hb];
+        for (int mb = 0; mb < NMB; ++mb) o[hb][mb] *= alpha[hb];
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -1223,7 +1276,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // ---- O^T += V^T P^T (M = 16 value columns, N = 16 heads, K = 32 rows with
   //      k = 8g+i <-> row (i < 4 ? 4g+i : 16+4g+i-4), the S^T lane layout)
   auto pv = [&](const char* sV) {
-    const char* vp = sV + (4 * g + (t >> 2)) * RS + 8 * (t & 3);
+    // (wave pairs: this wave's 256 value columns)
+    const char* vp = sV + (4 * g + (t >> 2)) * RS + 8 * (t & 3) + 512 * hf;
     constexpr int PV = NW * HB >= 8 ? 2 : 4;
     s16x4 vb[PV][2];
     auto vload = [&](int mb, s16x4& lo, s16x4& hi) {
@@ -1234,7 +1288,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     for (int i = 0; i < PV; ++i) vload(i, vb[i][0], vb[i][1]);
     bf16x8 pbt[HB];                // packed: P times the rows' scales of tile mb / 8
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
       if (PK && mb % 8 == 0) {
         const f32x4 c0 = *(const f32x4*)(sScale + (mb / 8) * T + 4 * g);
         const f32x4 c1 = *(const f32x4*)(sScale + (mb / 8) * T + 16 + 4 * g);
@@ -1250,7 +1304,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
         o[hb][mb] = mfma16<HALF>(va, PK ? pbt[hb] : pb[hb], o[hb][mb]);
-      if (mb + PV < 32) vload(mb + PV, vb[mb % PV][0], vb[mb % PV][1]);
+      if (mb + PV < NMB) vload(mb + PV, vb[mb % PV][0], vb[mb % PV][1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -1290,7 +1344,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       wait_lgkm0();
       block_barrier();                                    // ... and V(tt-1) reads are done
       if (tt + 1 < nt) issue_v<NW, DQK, VMODE>(a, sRow, (tt + 1) * T, lds_addr(sVn), w, l);
-      if (wave_on) qk_softmax(sKc, tt * T);
+      if (PAIR || wave_on) qk_softmax(sKc, tt * T);   // (pairs: a barrier inside)
       if (tt + 1 < nt) wait_vmcnt<C::NK + C::NV>(); else wait_vmcnt<0>();        // V(tt) landed
       wait_lgkm0();
       block_barrier();                                    // ... and K(tt) reads are done
@@ -1313,13 +1367,37 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       if (tt + 1 < nt) step(tt + 1, sK1, sV1, sV0);
     }
   } else {
-    // V aliases K: a ring of three K stages, two tiles in flight.
+    // V aliases K: a ring of three K stages, two tiles in flight.  Where at
+    // most four waves hold heads, waves 4..7 issue every row of the tiles
+    // from K(2) on (8 rows each, as a four-wave workgroup would), so that the
+    // head waves go from the barrier straight to their products; K(0) and
+    // K(1) go out before the loop from the waves that resolved their rows.
+    // (Not with rope: its extra addresses push that kernel's registers
+    // past the limit of two waves per SIMD; not with wave pairs, whose small
+    // launches were measured faster with every wave issuing a share.)
+    using C4 = Pipe<4, DQK, VMODE>;
+    constexpr bool LD = !TILED && !PAIR && NW == 8 && !C::ROPE;
+    const bool loaders = LD && a.bpg <= 4;
     auto step = [&](int tt, char* sKc, char* sKn2) {
-      if (tt + 1 < nt) wait_vmcnt<C::NK>(); else wait_vmcnt<0>();   // K(tt) landed
+      if (!LD || !loaders) {
+        if (tt + 1 < nt) wait_vmcnt<C::NK>(); else wait_vmcnt<0>();   // K(tt) landed
+      } else if (w >= 4) {
+        if (tt + 1 >= nt) wait_vmcnt<0>();
+        else if (tt == 0) wait_vmcnt<C::NK>();          // K(1): this wave's own rows
+        else wait_vmcnt<C4::NK>();
+      } else {
+        if (tt == 0 && nt > 1) wait_vmcnt<C::NK>(); else wait_vmcnt<0>();
+      }
       wait_lgkm0();
       block_barrier();                                    // ... and tile tt-1 is consumed
-      if (tt + 2 < nt) issue_k<NW, DQK, VMODE>(a, sRow, (tt + 2) * T, lds_addr(sKn2), w, l);
-      if (wave_on) {
+      if (tt + 2 < nt) {
+        if (!LD || !loaders) issue_k<NW, DQK, VMODE>(a, sRow, (tt + 2) * T, lds_addr(sKn2), w, l);
+        else if (LD && w >= 4) issue_k<4, DQK, VMODE>(a, sRow, (tt + 2) * T, lds_addr(sKn2), w - 4, l);
+      }
+      if constexpr (PAIR) {
+        qk_softmax(sKc, tt * T);                          // (a barrier inside)
+        if (wave_on) pv(sKc);
+      } else if (wave_on) {
         qk_softmax(sKc, tt * T);
         pv(sKc);
       }
@@ -1354,15 +1432,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     const int h = h0 + 16 * hb + t;
     if (h >= a.qn) return;
     const float inv = den > 0.f ? scale / den : 0.f;
-    uint16_t* op = a.out + ((int64_t)orow * a.qn + h) * 512 + 4 * g;
+    uint16_t* op = a.out + ((int64_t)orow * a.qn + h) * 512 + 4 * g + 256 * hf;
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
       uint2 pk;
       pk.x = (uint32_t)to16<HALF>(o[hb][mb][0] * inv) | ((uint32_t)to16<HALF>(o[hb][mb][1] * inv) << 16);
       pk.y = (uint32_t)to16<HALF>(o[hb][mb][2] * inv) | ((uint32_t)to16<HALF>(o[hb][mb][3] * inv) << 16);
       *(uint2*)(op + 16 * mb) = pk;
     }
-    if (a.lse && g == 0) a.lse[(int64_t)orow * a.qn + h] = den > 0.f ? l2 * kLn2 : kNegInf;
+    if (a.lse && g == 0 && hf == 0) a.lse[(int64_t)orow * a.qn + h] = den > 0.f ? l2 * kLn2 : kNegInf;
   };
 
   if (nsplit == 1) {
@@ -1382,8 +1460,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // another group's heads).
   if (!wave_on) return;
   static_assert(NW * 8 <= kCounterInts, "arrival counters per row: head groups (<= 8) x waves");
-  const int HP = a.groups * NW * HPW;              // heads per row, padded
-  constexpr int WAVE_BYTES = HB * 16 * 64 * 16;    // one wave's partial
+  const int HP = a.groups * NPW * HPW;             // heads per row, padded
+  constexpr int NFR = NMB / 2;                      // 1 KB fragments per head block
+  constexpr int WAVE_BYTES = HB * NFR * 64 * 16;   // one wave's partial
   // every split, head group and wave of this query row (< 2^31 bytes: at
   // most 4096 splits x 128 heads x 1 KB)
   const int64_t row_bytes = (int64_t)a.max_splits * a.groups * NW * WAVE_BYTES;
@@ -1413,7 +1492,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // (only where every wave of the workgroup holds heads, so the shared
   // merge runs on all SIMDs: with fewer head waves the last split to
   // arrive merges sooner, measured)
-  const bool own_mode = !PK && !TILED && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
+  const bool own_mode = !PK && !TILED && !PAIR && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
                         n_on == NW && n_own > 0 && n_own * nsplit <= OSLOT;
   auto slot_addr = [&](int q) -> uint32_t {          // slot q: two per stage buffer
     const int b = q >> 1;
@@ -1431,7 +1510,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     // bytes per lane in flight: 16, or 32 where one wave per SIMD leaves the
     // registers); the first round travels together with the loads of the
     // LSEs, which give the max and the normaliser in one pass.
-    constexpr int MS = NW <= 4 ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = 16 / JB;
+    constexpr int MS = NW <= 4 ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = NFR / JB;
     const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
     const int R = NJ * ns4;                               // load rounds
     const int split_bytes = a.groups * NW * WAVE_BYTES;
@@ -1452,7 +1531,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     for (int hb = 0; hb < HB; ++hb) {
       const int h = h0 + 16 * hb + t;
       const float* lp = a.ws_lse + (int64_t)row * a.max_splits * HP + h;
-      const int off0 = (hg * NW + w) * WAVE_BYTES + ((hb * 16) * 64 + l) * 16;   // split 0
+      const int off0 = (hg * NW + w) * WAVE_BYTES + ((hb * NFR) * 64 + l) * 16;  // split 0
       u32x4 v[MS][JB];
       float wl[MS];
       auto issue = [&](int r) {
@@ -1494,7 +1573,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - Mu);
       const float inv = tot > 0.f ? 1.f / den : 0.f;
       const bool on = h < a.qn;
-      uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g;
+      uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g + 256 * hf;
       float acc[JB][8];
 #pragma unroll
       for (int j = 0; j < JB; ++j)
@@ -1542,7 +1621,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
       }
-      if (on && a.lse && g == 0)
+      if (on && a.lse && g == 0 && hf == 0)
         a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;
     }
     if (stage) {
@@ -1560,7 +1639,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   };
 
   bool owned_here = false;                          // this wave's heads are merged here
-  if constexpr (!PK) {
+  if constexpr (!PK && !PAIR) {
     static_assert(HB == 1, "owned merge: one 16-head block per wave");
     if (own_mode && w % nsplit == split) {
       const int ow = w / nsplit;
@@ -1649,7 +1728,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     for (int hb = 0; hb < HB; ++hb) {
       const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < NFR; ++j) {
         uint4 pk;
         pk.x = (uint32_t)to16<HALF>(o[hb][2 * j][0] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][1] * inv) << 16);
         pk.y = (uint32_t)to16<HALF>(o[hb][2 * j][2] * inv) | ((uint32_t)to16<HALF>(o[hb][2 * j][3] * inv) << 16);
@@ -1658,7 +1737,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         pk.w = (uint32_t)to16<HALF>(o[hb][2 * j + 1][2] * inv) |
                ((uint32_t)to16<HALF>(o[hb][2 * j + 1][3] * inv) << 16);
         const u32x4 d = {pk.x, pk.y, pk.z, pk.w};
-        __builtin_amdgcn_raw_buffer_store_b128(d, rs, wave_off + ((hb * 16 + j) * 64 + l) * 16, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b128(d, rs, wave_off + ((hb * NFR + j) * 64 + l) * 16, 0, kSc1);
       }
       if (g == 0)
         st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
@@ -1678,7 +1757,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  if constexpr (!PK) {
+  if constexpr (!PK && !PAIR) {
     if (own_mode) {
       // share of the owned heads' merge: fragment j (head t, value columns
       // [32 j, 32 j + 32)) of owned wave ow goes to head-holding wave
@@ -1867,6 +1946,25 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int groups, int merge_wait_us, 
   return hipGetLastError();
 }
 
+// Wave pairs (16-bit rows): eight waves, four pairs of 16 heads each
+template <int DQK, int VMODE, int FMT>
+static hipError_t launch_pair_t(const FwdArgs& a, int groups, hipStream_t s, hipEvent_t t0,
+                                hipEvent_t t1) {
+  FwdArgs b = a;
+  b.groups = groups;
+  if (b.bpg < 1 || b.bpg > 4) return hipErrorInvalidConfiguration;
+  const int64_t blocks = (int64_t)(a.q_t + 7) / 8 * 8 * a.max_splits * groups;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  b.merge_wait_ticks = 0;                           // no owned merges
+  if (t0 || t1)
+    hipExtLaunchKernelGGL((fwd_kernel<8, 1, DQK, VMODE, FMT, false, true>), dim3((unsigned)blocks),
+                          dim3(512), 0, s, t0, t1, 0, b);
+  else
+    hipLaunchKernelGGL((fwd_kernel<8, 1, DQK, VMODE, FMT, false, true>), dim3((unsigned)blocks),
+                       dim3(512), 0, s, b);
+  return hipGetLastError();
+}
+
 // Eight waves per workgroup for bf16 rows; four or eight for packed rows
 // (four: one wave per SIMD with the whole register file for the decode;
 // eight: every head of a row in one workgroup, each row gathered and
@@ -1883,8 +1981,24 @@ static hipError_t launch_packed(const FwdArgs& a, int nw, int dqk, int groups, i
   return hipErrorInvalidConfiguration;
 }
 
-hipError_t launch_forward(const FwdArgs& a, int nw, int dqk, int vmode, int fmt, int groups,
-                          int mw, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_forward(const FwdArgs& a, int nw, bool pair, int dqk, int vmode, int fmt,
+                          int groups, int mw, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (pair) {
+    if (nw != 8) return hipErrorInvalidConfiguration;
+    if (fmt == SFMLA_KV_BF16) {
+      if (dqk == 512) return vmode ? launch_pair_t<512, 1, 0>(a, groups, s, t0, t1)
+                                   : launch_pair_t<512, 0, 0>(a, groups, s, t0, t1);
+      return vmode ? launch_pair_t<576, 1, 0>(a, groups, s, t0, t1)
+                   : launch_pair_t<576, 0, 0>(a, groups, s, t0, t1);
+    }
+    if (fmt == SFMLA_KV_FP16) {
+      if (dqk == 512) return vmode ? launch_pair_t<512, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
+                                   : launch_pair_t<512, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
+      return vmode ? launch_pair_t<576, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
+                   : launch_pair_t<576, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
+    }
+    return hipErrorInvalidConfiguration;            // packed rows have no wave pairs
+  }
   switch (fmt) {
     case SFMLA_KV_INT8_PACKED:
       return launch_packed<SFMLA_KV_INT8_PACKED>(a, nw, dqk, groups, mw, s, t0, t1);

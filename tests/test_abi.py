@@ -173,8 +173,10 @@ def _expected_workspace(P):
     """The split partials' workspace from the host's documented policy:
     512-row splits for rows of 2 KB or more, 256 otherwise; head groups of
     1/2/4/8 16-head blocks (at most 4 per group for packed rows), halved
-    while the grid would have fewer than 256 workgroups; one bf16 partial
-    (1 KB per padded head) and one fp32 LSE per (row, split, padded head)."""
+    while the grid would have fewer than 256 workgroups; 16-bit rows with
+    fewer than 256 (row, split) units on wave pairs (groups of 1/2/4 pairs);
+    one bf16 partial (1 KB per padded head) and one fp32 LSE per (row,
+    split, padded head)."""
     p = P.params
     packed = p["kv_dtype"] not in ("bf16", "fp16")
     rope = p["rope_head_dim"]
@@ -187,14 +189,23 @@ def _expected_workspace(P):
     if splits <= 1:
         return 0
     blocks = -(-p["num_heads_q"] // 16)
-    wmax = 4 if packed else 8
-    per = 1
-    while per < wmax and per < blocks:
-        per *= 2
     units = p["q_t"] * splits
-    while per > 1 and units * -(-blocks // per) < 256:
-        per //= 2
-    heads = -(-blocks // per) * wmax * 16
+    if not packed and units < 256:
+        # wave pairs: groups of up to 4 pairs of 16 heads, eight waves of
+        # 16 heads x 256 columns of partial each
+        per = min(4, blocks)
+        per = 2 if per == 3 else per
+        while per > 1 and units * -(-blocks // per) < 256:
+            per //= 2
+        heads = -(-blocks // per) * 8 * 8
+    else:
+        wmax = 4 if packed else 8
+        per = 1
+        while per < wmax and per < blocks:
+            per *= 2
+        while per > 1 and units * -(-blocks // per) < 256:
+            per //= 2
+        heads = -(-blocks // per) * wmax * 16
     slots = p["q_t"] * splits * heads
     up = lambda x: -(-x // 256) * 256
     return up(slots * 1024) + up(slots * 4)
@@ -375,6 +386,43 @@ def test_tiled_call_lays_out_split_rows_with_every_head_in_one_group():
     # without tiles the 64 heads take 4 waves per group of the same size
     assert s.sfmla_workspace_size(s.make_params(dict(P.params, max_seqlen_cmp_kv=4096,
                                                      query_tile=1), P.arrays)) > 0
+
+
+# ---------------------------------------------------------------------------
+# wave pairs: host rule and workspace
+# ---------------------------------------------------------------------------
+
+def test_wave_pairs_override_is_validated():
+    P = synth.make_workload("csa_prefill")                # bf16, 64 heads, TopK lists
+    for bad in (3, -1):
+        with pytest.raises(s.SfmlaError, match="wave_pairs"):
+            _meta_ints(P, wave_pairs=bad)
+    assert _meta_ints(P, wave_pairs=2) == _meta_ints(P, wave_pairs=1)
+    _meta_ints(synth.make_workload("sfa_mla_rope"), wave_pairs=2)   # 128 heads: two groups
+    # refused where pairs do not apply: packed rows, query tiles
+    for name in ("c8_packed_int8", "hca_prefill"):
+        with pytest.raises(s.SfmlaError, match="wave_pairs"):
+            _meta_ints(synth.make_workload(name), wave_pairs=2)
+    _meta_ints(synth.make_workload("hca_prefill"), query_tile=1, wave_pairs=2)
+
+
+def test_wave_pair_workspace_and_rule():
+    """With pairs every wave's partial is 16 heads x 256 columns (the bytes of
+    8 heads x 512), eight waves per (row, split, head group): 64 heads of
+    partial per group, which holds four pairs.  The rule takes pairs where
+    the (row, split) units do not fill the GPU (a decode of 4 rows x 3
+    splits), not for csa_prefill (512 rows x 3 splits of its 640-row lists),
+    whose 64 heads take one eight-wave group (128 heads of slots) without."""
+    P = synth.make_workload("csa_prefill")
+    ws = lambda **o: s.sfmla_workspace_size(s.make_params(dict(P.params, **o), P.arrays))
+    up = lambda n: (n + 255) // 256 * 256
+    slots = lambda heads: P.params["q_t"] * 3 * heads
+    assert ws(wave_pairs=2) == up(slots(64) * 1024) + up(slots(64) * 4)
+    assert ws(wave_pairs=1) == up(slots(128) * 1024) + up(slots(128) * 4)
+    assert ws() == ws(wave_pairs=1)
+    D = synth.make_workload("csa_decode_paged")            # 4 rows, 64 heads
+    wd = lambda **o: s.sfmla_workspace_size(s.make_params(dict(D.params, **o), D.arrays))
+    assert wd() == wd(wave_pairs=2) != wd(wave_pairs=1)
 
 
 def test_q_rope_apart_is_validated():

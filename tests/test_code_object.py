@@ -101,15 +101,26 @@ def kernels():
     return out
 
 
+FWD_NAME = (r"_ZN5sfmla10fwd_kernelILi(\d+)ELi(\d)ELi(\d+)ELi(\d)ELi(\d)ELb(\d)ELb(\d)EEEv"
+            r"NS_7FwdArgsE")
+
+
+def _key(m):
+    """(waves, d_qk, separate V, format, query tiles, wave pairs); every
+    wave holds one 16-head block"""
+    waves, hb, dqk, vmode, fmt, tiled, pair = (int(x) for x in m.groups())
+    assert hb == 1, m.group(0)
+    return (waves, dqk, vmode, fmt, tiled, pair)
+
+
 def _fwd(kernels):
     """fwd_kernel instantiations as (waves, d_qk, separate V, format, query
-    tiles) -> fields."""
+    tiles, wave pairs) -> fields."""
     res = {}
     for name, f in kernels.items():
-        m = re.fullmatch(r"_ZN5sfmla10fwd_kernelILi(\d+)ELi1ELi(\d+)ELi(\d)ELi(\d)ELb(\d)EEEv"
-                         r"NS_7FwdArgsE", name)
+        m = re.fullmatch(FWD_NAME, name)
         if m:
-            res[tuple(int(x) for x in m.groups())] = f
+            res[_key(m)] = f
     return res
 
 
@@ -128,21 +139,25 @@ def test_every_forward_variant_is_built(kernels):
         for dqk in (512, 576):
             for vmode in (0, 1):
                 for tiled in (0, 1):
-                    assert (8, dqk, vmode, fmt, tiled) in fwd
+                    assert (8, dqk, vmode, fmt, tiled, 0) in fwd
+                # eight waves in four pairs (never tiled)
+                assert (8, dqk, vmode, fmt, 0, 1) in fwd
+                assert (8, dqk, vmode, fmt, 1, 1) not in fwd
     # packed INT8 / FP8 rows, with and without rope, on four or eight waves
     # (never tiled)
     for fmt in (1, 2):
         for dqk in (512, 576):
             for waves in (4, 8):
-                assert (waves, dqk, 0, fmt, 0) in fwd
-                assert (waves, dqk, 0, fmt, 1) not in fwd
+                assert (waves, dqk, 0, fmt, 0, 0) in fwd
+                assert (waves, dqk, 0, fmt, 1, 0) not in fwd
+                assert (waves, dqk, 0, fmt, 0, 1) not in fwd
     assert any("plan_kernel" in k for k in kernels)
     assert any("combine_kernel" in k for k in kernels)
 
 
 def test_forward_kernels_fit_their_waves_per_simd_and_the_lds(kernels):
     # one workgroup per CU: 8 waves are two per SIMD (256 VGPRs each), the
-    # 4-wave packed kernel is one per SIMD (up to 512)
+    # 4-wave packed kernel one per SIMD (up to 512)
     for key, f in _fwd(kernels).items():
         waves = key[0]
         assert f["max_flat_workgroup_size"] == 64 * waves, key
@@ -156,7 +171,7 @@ def test_forward_kernels_use_no_scratch_in_the_main_loop(kernels, disasm):
     instantiation (bf16, rope, separate V) has none at all."""
     fwd = _fwd(kernels)
     for key, f in fwd.items():
-        if key == (8, 576, 1, 0, 0):
+        if key == (8, 576, 1, 0, 0, 0):
             assert f["vgpr_spill_count"] == 0 and f["private_segment_fixed_size"] == 0, (key, f)
         if _eight_wave_packed(key):
             assert f["vgpr_spill_count"] <= 40 and f["private_segment_fixed_size"] <= 128, (key, f)
@@ -164,8 +179,7 @@ def test_forward_kernels_use_no_scratch_in_the_main_loop(kernels, disasm):
             assert f["vgpr_spill_count"] <= 16 and f["private_segment_fixed_size"] <= 64, (key, f)
     found = 0
     for name, body in disasm.items():
-        m = re.fullmatch(r"_ZN5sfmla10fwd_kernelILi(\d+)ELi1ELi(\d+)ELi(\d)ELi(\d)ELb(\d)EEEv"
-                         r"NS_7FwdArgsE", name)
+        m = re.fullmatch(FWD_NAME, name)
         if not m:
             continue
         found += 1

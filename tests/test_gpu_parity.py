@@ -714,3 +714,89 @@ def test_q_rope_apart_matches_concatenated_bitwise(kw):
     assert np.array_equal(one["lse"], two["lse"])
     rows = list(range(min(4, P.query_rows)))
     check_outputs(P, two, oracle.forward(P, rows=rows), rows)
+
+
+# ---------------------------------------------------------------------------
+# wave pairs (16-bit rows, at most 64 heads)
+# ---------------------------------------------------------------------------
+
+PAIR_CASES = [
+    # rope, separate V, 3 splits (last-arriver merge), sinks
+    dict(seed=950, family="sfa", max_kv=3000, topk=1100, num_heads_q=64, rope_head_dim=64,
+         separate_v=True, sinks=True, lse=True),
+    # V = K nope, 48 heads (three pairs over two head groups), varlen queries
+    dict(seed=951, family="swa", max_kv=600, num_heads_q=48, layout_q="TND", lse=True),
+    # 32 heads (two pairs, the other four waves only gather), float16, compressed TopK
+    dict(seed=952, family="csa", max_kv=2000, topk=700, num_heads_q=32, cmp_ratio=4,
+         kv_dtype="fp16", sinks=True, lse=True),
+    # a single head, all visible compressed rows, no LSE output
+    dict(seed=953, family="hca", max_kv=1500, num_heads_q=1, cmp_ratio=4, lse=False),
+    # paged KV, two pairs per head group (two groups), rope in the rows
+    dict(seed=954, family="sfa", max_kv=4000, topk=2048, num_heads_q=64, rope_head_dim=64,
+         separate_v=False, layout_kv="PA_BSND", block_size=64, head_blocks_per_group=2),
+    # float16, separate V without rope, repeated TopK entries
+    dict(seed=955, family="sfa", max_kv=2500, topk=900, num_heads_q=16, rope_head_dim=0,
+         separate_v=True, kv_dtype="fp16", duplicates=True, lse=True),
+    # 128 heads: two head groups of four pairs, rope, separate V, 4 splits
+    dict(seed=956, family="sfa", max_kv=4000, topk=2048, num_heads_q=128, rope_head_dim=64,
+         separate_v=True, sinks=True, lse=True),
+]
+
+
+@pytest.mark.parametrize("kw", PAIR_CASES, ids=lambda k: str(k["seed"]))
+def test_wave_pairs_match_single_waves_bitwise(kw):
+    """Two waves sharing 16 heads (each with the scores of half of every KV
+    tile and half of the value columns) give the bits of one wave holding
+    them, and the oracle's result on every row."""
+    import sparse_shared_kv_amd as s
+    kw = dict(kw)
+    bpg = kw.pop("head_blocks_per_group", 0)
+    P = synth.random_tiny(**kw)
+    outs = []
+    for wp in (1, 2):
+        say(f"wave pairs seed {kw['seed']} wave_pairs={wp}")
+        call = s.Call(dict(P.params, wave_pairs=wp, head_blocks_per_group=bpg), P.arrays)
+        outs.append([None if t is None else t.clone() for t in call.run()])
+        torch.cuda.synchronize()
+        assert int(call.status.item()) == 0
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert (outs[0][1] is None) == (outs[1][1] is None)
+    if outs[0][1] is not None:
+        assert torch.equal(outs[0][1], outs[1][1])
+    rows = list(range(P.query_rows))
+    res = dict(O=outs[1][0].float().cpu().numpy(), status=0,
+               lse=None if outs[1][1] is None else outs[1][1].cpu().numpy())
+    check_outputs(P, res, oracle.forward(P, rows=rows), rows)
+
+
+def test_wave_pairs_on_random_tiny_cases_bitwise():
+    """Random small problems of every family and layout (bf16 and float16):
+    wave pairs forced on and off give the same bits."""
+    import sparse_shared_kv_amd as s
+    for seed in range(960, 1000):
+        P = synth.random_tiny(seed, kv_dtype="fp16" if seed % 3 == 0 else "bf16", max_kv=800)
+        outs = []
+        for wp in (1, 2):
+            say(f"random tiny seed {seed} wave_pairs={wp}")
+            call = s.Call(dict(P.params, wave_pairs=wp), P.arrays)
+            outs.append([None if t is None else t.clone() for t in call.run()])
+            torch.cuda.synchronize()
+            assert int(call.status.item()) == 0, seed
+        assert torch.equal(outs[0][0], outs[1][0]), seed
+        if outs[0][1] is not None:
+            assert torch.equal(outs[0][1], outs[1][1]), seed
+
+
+def test_wave_pairs_at_full_size_bitwise():
+    """The prefill call example's TopK workload (4 x 128 query tokens, 64
+    heads) on wave pairs: the same bits as without."""
+    import sparse_shared_kv_amd as s
+    P = synth.make_workload("csa_prefill")
+    outs = []
+    for wp in (2, 1):
+        say(f"csa_prefill wave_pairs={wp}")
+        call = s.Call(dict(P.params, wave_pairs=wp), P.arrays)
+        outs.append([None if t is None else t.clone() for t in call.run()])
+        torch.cuda.synchronize()
+        assert int(call.status.item()) == 0
+    assert torch.equal(outs[0][0], outs[1][0])
