@@ -697,6 +697,36 @@ __device__ __forceinline__ void issue_raw(const FwdArgs& a, const uint32_t* sRow
   }
 }
 
+// Lane exchanges within a wave on the VALU (gfx950 v_permlane16_swap /
+// v_permlane32_swap, no LDS round trip).  Given the same value twice, the
+// 16-lane swap returns (x of lane l & ~16, x of lane l | 16) and the 32-lane
+// swap (x of lane l & ~32, x of lane l | 32), so every lane of a pair gets
+// the same operands in the same order.
+__device__ __forceinline__ void pair16(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one head's 32
+// rows of a tile in the score layout)
+__device__ __forceinline__ float max4(float x) {
+  float a, b;
+  pair16(x, a, b);
+  pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum4(float x) {
+  float a, b;
+  pair16(x, a, b);
+  pair32(a + b, a, b);
+  return a + b;
+}
+
 // Raw packed tile -> the bf16 K tile the MFMA path reads (codes decoded
 // exactly; rope copied into its swizzled region) and the tile's scales,
 // stored scale-tile major: sScale[32 * j + row] for columns [128 j, 128 j + 128).
@@ -1247,8 +1277,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         x[j] = v;
         mx = fmaxf(mx, v);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max4(mx);
       const bool grow = mx > m_run[hb] + kRescaleThreshold;
       alpha[hb] = grow ? __builtin_amdgcn_exp2f(m_run[hb] - mx) : 1.f;
       if (grow) m_run[hb] = mx;
@@ -1421,8 +1450,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   float lt[HB], lse2[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
-    float v = l_run[hb] + __shfl_xor(l_run[hb], 16);
-    lt[hb] = v + __shfl_xor(v, 32);
+    lt[hb] = sum4(l_run[hb]);
     lse2[hb] = lt[hb] > 0.f ? m_run[hb] + __builtin_log2f(lt[hb]) : kNegInf;   // log2 units
   }
 
