@@ -1166,7 +1166,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           const int c = 4 * (ks - 16) + g, r = 16 * half + t;
           return *(const bf16x8*)(sR + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
         };
-        constexpr int PF = NW * HB >= 8 ? (C::ROPE ? 1 : 2) : 4;
+        constexpr int PF = NW * HB >= 8 ? 2 : 4;
         bf16x8 kb[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i) kb[i] = kload(i);
@@ -1307,7 +1307,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   auto pv = [&](const char* sV) {
     // (wave pairs: this wave's 256 value columns)
     const char* vp = sV + (4 * g + (t >> 2)) * RS + 8 * (t & 3) + 512 * hf;
-    constexpr int PV = NW * HB >= 8 ? 2 : 4;
+    constexpr int PV = 4;
     s16x4 vb[PV][2];
     auto vload = [&](int mb, s16x4& lo, s16x4& hi) {
       lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * mb));
