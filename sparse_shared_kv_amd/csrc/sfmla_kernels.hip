@@ -1134,23 +1134,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // multiplies; sched_barrier fences pin that order.
   auto qk_softmax = [&](const char* sK, int tbase) {
     const char* sR = sK + T * RS;
-    bool valid[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      valid[i] = sRow[tbase + 4 * g + i] != kNoRow;
-      valid[4 + i] = sRow[tbase + 16 + 4 * g + i] != kNoRow;
-    }
+    // The tile rows that take part for this wave, one bit per row: a KV row
+    // behind the position (lanes l and l + 32 read row l mod 32), and with
+    // tiles the position in this wave's row's own list (two intervals of the
+    // union, intersected in scalar registers).  A full tile takes no
+    // per-element selects.
+    uint32_t vm = (uint32_t)__ballot(sRow[tbase + (l & 31)] != kNoRow);
     if constexpr (TILED) {
-      // union positions outside this wave's row's own list
-      auto mine = [&](int k) {
-        return (uint32_t)(k - m_a0) < (uint32_t)m_cnt || (uint32_t)(k - m_ucnt) < (uint32_t)m_cc;
+      auto span = [&](int lo, int cnt) -> uint32_t {
+        const int a0 = max(lo - tbase, 0), a1 = min(lo - tbase + cnt, 32);
+        return a1 > a0 ? (uint32_t)((((uint64_t)1 << a1) - 1) & ~(((uint64_t)1 << a0) - 1)) : 0u;
       };
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        valid[i] = valid[i] && mine(tbase + 4 * g + i);
-        valid[4 + i] = valid[4 + i] && mine(tbase + 16 + 4 * g + i);
-      }
+      vm &= span(m_a0, m_cnt) | span(m_ucnt, m_cc);
     }
+    const bool full = vm == 0xffffffffu;
+    // this lane's rows {4g + i, 16 + 4g + i}: bit j of nib <-> x[j] below
+    const uint32_t nib = ((vm >> (4 * g)) & 0xfu) | (((vm >> (16 + 4 * g)) & 0xfu) << 4);
     f32x4 s[HB][2];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1272,11 +1271,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       float x[8];
       float mx = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = valid[j] ? s[hb][j >> 2][j & 3] * a.scale_log2 : kNegInf;
-        x[j] = v;
-        mx = fmaxf(mx, v);
+      for (int j = 0; j < 8; ++j) x[j] = s[hb][j >> 2][j & 3] * a.scale_log2;
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (nib >> j) & 1u ? x[j] : kNegInf;
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, x[j]);
       mx = max4(mx);
       const bool grow = mx > m_run[hb] + kRescaleThreshold;
       alpha[hb] = grow ? __builtin_amdgcn_exp2f(m_run[hb] - mx) : 1.f;
