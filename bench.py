@@ -487,9 +487,9 @@ SUB_CONFIGS = {
     "c8_packed_int8_q32": "c5 shapes, 32 query tokens per sequence (throughput mode)",
     "hca_varlen_q32": "c3 shapes, 32 query tokens per sequence (throughput mode)",
     "csa_prefill": "prefill: the SparseAttnSharedkv call example's shapes",
-    "swa_prefill": "prefill, window only (query tiles of 2 rows at 64 heads)",
-    "swa_prefill_h16": "prefill, window only, 16 heads (query tiles of 8 rows)",
-    "hca_prefill": "prefill, window and every visible compressed row (query tiles of 2 rows)",
+    "swa_prefill": "prefill, window only (four-wave kernel, two workgroups per CU)",
+    "swa_prefill_h16": "prefill, window only, 16 heads (four-wave kernel, two workgroups per CU)",
+    "hca_prefill": "prefill, window and every visible compressed row (four-wave kernel)",
 }
 
 

@@ -173,7 +173,10 @@ typedef struct sfmla_params {
    * a tile's union to one split of 2048 rows (window: win_left + win_right +
    * rows per tile, else max_seqlen_ori_kv; plus max_seqlen_cmp_kv).
    * The rule tiles 8 / (16-head blocks rounded up to a power of two) rows,
-   * i.e. 2 rows at 64 heads, 8 at 16, when max_seqlen_q >= 16.
+   * i.e. 2 rows at 64 heads, 8 at 16, when max_seqlen_q >= 16 and the rows
+   * carry rope or a separate V (rope-free rows whose V is the K nope go to
+   * a four-wave kernel with two workgroups per CU instead, which was
+   * measured faster than tiles on every prefill shape).
    *   1        never tile;
    *   2, 4, 8  that many rows per tile (refused where the parameters do not
    *            allow tiles of that size).

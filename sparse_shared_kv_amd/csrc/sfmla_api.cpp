@@ -269,6 +269,16 @@ bool tile_eligible(const sfmla_params& p) {
          p.cmp_topk == 0 && tile_limit(p) >= 2;
 }
 
+// Rows the four-wave kernel with two workgroups per CU takes where the
+// launch fills the GPU: 16-bit, no rope, V = K nope, at most 64 heads.  It
+// was measured faster than query tiles on every prefill shape (hca_prefill
+// 94.3 vs 97.6 us, swa_prefill 27.2 vs 33.0, 16 heads 14.5 vs 20.5), so
+// tiles are not the rule there.
+bool four_wave_rows(const sfmla_params& p) {
+  return (p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_FP16) && !p.has_separate_v &&
+         p.rope_head_dim == 0 && p.num_heads_q <= 64;
+}
+
 // Most query rows per tile of this call (1: no tiles).  By rule: the most
 // the waves hold, where a sequence may be long enough to be a prefill.
 // Which sequences are tiled, and by rule with how many rows, is decided on
@@ -278,7 +288,7 @@ bool tile_eligible(const sfmla_params& p) {
 int query_tile(const sfmla_params& p) {
   if (p.query_tile == 1) return 1;
   if (p.query_tile > 1) return p.query_tile;        // validated
-  if (!tile_eligible(p) || p.max_seqlen_q < sfmla::kMinTileQueries) return 1;
+  if (!tile_eligible(p) || p.max_seqlen_q < sfmla::kMinTileQueries || four_wave_rows(p)) return 1;
   return tile_limit(p);
 }
 
@@ -387,6 +397,11 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg, bool* 
   // same bits (same per-wave arithmetic; the merge adds splits in order).
   int wmax = 8;
   if (packed && !(blocks >= 8 && units >= kMinGroups) && p.head_blocks_per_group != 8) wmax = 4;
+  // 16-bit rows without rope whose V is the K nope, at most 64 heads, in a
+  // launch that fills the GPU: four waves, two workgroups per CU (every
+  // SIMD then has two waves in the products; eight waves with four holding
+  // heads leave one per SIMD): csa_prefill 74.5 -> 61.0 us
+  if (four_wave_rows(p) && units >= kMinGroups && p.head_blocks_per_group == 0) wmax = 4;
   *nw = wmax;
   // params.head_blocks_per_group, when nonzero, overrides the rule
   if (p.head_blocks_per_group) {

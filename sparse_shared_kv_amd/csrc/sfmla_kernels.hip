@@ -810,8 +810,15 @@ __device__ __forceinline__ int posn_of(int i0, int u, int tid, int w, int l) {
 // heads keeps all eight waves, two per SIMD, in the products.  Every MFMA
 // and every softmax step is the one a single wave holding those heads would
 // take, so the results are the same bits.
+// Four waves with 16-bit rows (d_qk 512, V = K nope): a two-stage K ring
+// and no owned merge keep the workgroup within half the LDS and its waves
+// within 256 registers, so two workgroups share a CU and every SIMD has two
+// waves in the products.
+template <int NW, int FMT>
+constexpr bool kTwoPerCu = NW == 4 && (FMT == SFMLA_KV_BF16 || FMT == SFMLA_KV_FP16);
+
 template <int NW, int HB, int DQK, int VMODE, int FMT, bool TILED = false, bool PAIR = false>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   using C = Pipe<NW, DQK, VMODE>;
   using PP = PackedPipe<NW, DQK>;
   constexpr bool HALF = FMT == SFMLA_KV_FP16;     // float16 q / kv / P / output
@@ -819,6 +826,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   static_assert(!PK || VMODE == 0, "packed KV has no separate V");
   static_assert(!TILED || (!PK && NW == 8 && HB == 1), "query tiles: 16-bit rows, 8 waves");
   static_assert(!PAIR || (!PK && !TILED && NW == 8 && HB == 1), "wave pairs: 16-bit rows, 8 waves");
+  constexpr bool W4 = kTwoPerCu<NW, FMT>;
+  static_assert(!W4 || (VMODE == 0 && DQK == 512 && !TILED && !PAIR && HB == 1),
+                "four-wave 16-bit rows: d_qk 512, V = K nope");
   static_assert(FMT == SFMLA_KV_BF16 || FMT == SFMLA_KV_INT8_PACKED ||
                 FMT == SFMLA_KV_FP8_E4M3_PACKED || FMT == SFMLA_KV_FP16, "KV format");
   constexpr int T = C::T;
@@ -832,7 +842,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // stages; packed: three raw stages and one decoded K tile (sK0)
   __shared__ __align__(16) char sK0[C::KBYTES];
   __shared__ __align__(16) char sK1[PK ? 16 : C::KBYTES];
-  __shared__ __align__(16) char sK2[(VMODE || PK) ? 16 : C::KBYTES];
+  __shared__ __align__(16) char sK2[(VMODE || PK || W4) ? 16 : C::KBYTES];
   __shared__ __align__(16) char sV0[VMODE ? T * RS : 16];
   __shared__ __align__(16) char sV1[VMODE ? T * RS : 16];
   __shared__ __align__(16) char sW0[PK ? PP::RAWB : 16];
@@ -853,11 +863,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // V = K nope: two more landing slots for the owned merge (the separate-V
   // kernel has its V stages for them; the tiled kernel merges splits of its
   // untiled rows with the last split to arrive)
-  __shared__ __align__(16) char sM[(VMODE || PK || TILED || PAIR) ? 16 : 32768];
+  __shared__ __align__(16) char sM[(VMODE || PK || TILED || PAIR || W4) ? 16 : 32768];
   // owned merge: per owning wave, every split's weight and the normaliser
   // per head, and a flag (1: landed and weighted, 2: handed off)
-  __shared__ float sWs[(PK || TILED || PAIR) ? 1 : NW][(PK || TILED || PAIR) ? 1 : kMaxOwnerSplits][16];
-  __shared__ float sInv[(PK || TILED || PAIR) ? 1 : NW][16];
+  __shared__ float sWs[(PK || TILED || PAIR || W4) ? 1 : NW][(PK || TILED || PAIR || W4) ? 1 : kMaxOwnerSplits][16];
+  __shared__ float sInv[(PK || TILED || PAIR || W4) ? 1 : NW][16];
   // wave pairs: each wave's raw scores of its 16 tile rows, per head block
   __shared__ __align__(16) f32x4 sSx[PAIR ? NW : 1][PAIR ? HB : 1][64];
   __shared__ int32_t sReady[NW];
@@ -1246,7 +1256,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           k1v = *(const bf16x8*)(sR + (16 + t) * 128 + 16 * (c ^ (((16 + t) >> 1) & 7)));
         }
       };
-      constexpr int PF = NW * HB >= 8 ? (C::ROPE ? 1 : 2) : 4;   // 2 waves/SIMD: fewer registers
+      constexpr int PF = (NW * HB >= 8 || W4) ? (C::ROPE ? 1 : 2) : 4;   // 2 waves/SIMD: fewer registers
       bf16x8 kb[PF][2];
 #pragma unroll
       for (int i = 0; i < PF; ++i) kload(i, kb[i][0], kb[i][1]);
@@ -1434,12 +1444,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     };
     // Q lands first (its first use is here), then K(0) and K(1) go out
     settle(qreg);
-    if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
-    if (nt > 1) issue_k<NW, DQK, VMODE>(a, sRow, T, lds_addr(sK1), w, l);
-    for (int tt = 0; tt < nt; tt += 3) {
-      step(tt, sK0, sK2);
-      if (tt + 1 < nt) step(tt + 1, sK1, sK0);
-      if (tt + 2 < nt) step(tt + 2, sK2, sK1);
+    if constexpr (W4) {
+      // two stages, one tile in flight per workgroup (two per CU): K(tt+1)
+      // goes out once every wave is done with tile tt-1
+      if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
+      auto step2 = [&](int tt, char* sKc, char* sKn) {
+        wait_vmcnt<0>();                                  // K(tt) landed
+        wait_lgkm0();
+        block_barrier();                                  // ... and tile tt-1 is consumed
+        if (tt + 1 < nt) issue_k<NW, DQK, VMODE>(a, sRow, (tt + 1) * T, lds_addr(sKn), w, l);
+        if (wave_on) {
+          qk_softmax(sKc, tt * T);
+          pv(sKc);
+        }
+      };
+      for (int tt = 0; tt < nt; tt += 2) {
+        step2(tt, sK0, sK1);
+        if (tt + 1 < nt) step2(tt + 1, sK1, sK0);
+      }
+    } else {
+      if (nt > 0) issue_k<NW, DQK, VMODE>(a, sRow, 0, lds_addr(sK0), w, l);
+      if (nt > 1) issue_k<NW, DQK, VMODE>(a, sRow, T, lds_addr(sK1), w, l);
+      for (int tt = 0; tt < nt; tt += 3) {
+        step(tt, sK0, sK2);
+        if (tt + 1 < nt) step(tt + 1, sK1, sK0);
+        if (tt + 2 < nt) step(tt + 2, sK2, sK1);
+      }
     }
   }
 
@@ -1521,7 +1551,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   // (only where every wave of the workgroup holds heads, so the shared
   // merge runs on all SIMDs: with fewer head waves the last split to
   // arrive merges sooner, measured)
-  const bool own_mode = !PK && !TILED && !PAIR && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
+  const bool own_mode = !PK && !TILED && !PAIR && !W4 && a.merge_wait_ticks > 0 && nsplit <= kMaxOwnerSplits &&
                         n_on == NW && n_own > 0 && n_own * nsplit <= OSLOT;
   auto slot_addr = [&](int q) -> uint32_t {          // slot q: two per stage buffer
     const int b = q >> 1;
@@ -1539,7 +1569,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     // bytes per lane in flight: 16, or 32 where one wave per SIMD leaves the
     // registers); the first round travels together with the loads of the
     // LSEs, which give the max and the normaliser in one pass.
-    constexpr int MS = NW <= 4 ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = NFR / JB;
+    constexpr int MS = (NW <= 4 && !W4) ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = NFR / JB;
     const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
     const int R = NJ * ns4;                               // load rounds
     const int split_bytes = a.groups * NW * WAVE_BYTES;
@@ -2034,12 +2064,18 @@ hipError_t launch_forward(const FwdArgs& a, int nw, bool pair, int dqk, int vmod
     case SFMLA_KV_FP8_E4M3_PACKED:
       return launch_packed<SFMLA_KV_FP8_E4M3_PACKED>(a, nw, dqk, groups, mw, s, t0, t1);
     case SFMLA_KV_FP16:
+      if (nw == 4)   // d_qk 512, V = K nope: two workgroups per CU
+        return dqk == 512 && !vmode ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1)
+                                    : hipErrorInvalidConfiguration;
       if (nw != 8) return hipErrorInvalidConfiguration;
       if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1)
                                    : launch_fwd_t<8, 512, 0, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1);
       return vmode ? launch_fwd_t<8, 576, 1, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1)
                    : launch_fwd_t<8, 576, 0, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1);
     default:
+      if (nw == 4)
+        return dqk == 512 && !vmode ? launch_fwd_t<4, 512, 0, 0>(a, groups, mw, s, t0, t1)
+                                    : hipErrorInvalidConfiguration;
       if (nw != 8) return hipErrorInvalidConfiguration;
       if (dqk == 512) return vmode ? launch_fwd_t<8, 512, 1, 0>(a, groups, mw, s, t0, t1)
                                    : launch_fwd_t<8, 512, 0, 0>(a, groups, mw, s, t0, t1);

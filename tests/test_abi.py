@@ -332,19 +332,22 @@ def _meta_ints(P, **over):
 
 
 def test_query_tile_rule_sizes_the_tile_descriptors():
-    """Tiles by rule need rule lists, 16-bit rows, at most 64 heads and
-    max_seqlen_q >= 16; the plan then holds one (first row, row count) pair
-    per possible tile of the fewest rows (2 by rule, the forced count
-    otherwise): (q_t + b (tq - 1)) / tq, at most q_t, rounded up to a
-    multiple of 8."""
+    """Tiles by rule need rule lists, 16-bit rows with rope or a separate V
+    (rope-free rows whose V is the K nope take the four-wave kernel), at
+    most 64 heads and max_seqlen_q >= 16; the plan then holds one (first
+    row, row count) pair per possible tile of the fewest rows (2 by rule,
+    the forced count otherwise): (q_t + b (tq - 1)) / tq, at most q_t,
+    rounded up to a multiple of 8."""
     base_ints = lambda P: 16 + (16 + 64) * P.params["q_t"]
     up8 = lambda n: (n + 7) // 8 * 8
     bound = lambda P, tq: up8(min(P.params["q_t"], (P.params["q_t"] + P.params["batch_size"] *
                                                     (tq - 1)) // tq))
     for name in ("swa_prefill", "hca_prefill", "swa_prefill_h16"):
         P = synth.make_workload(name)
-        assert _meta_ints(P) == base_ints(P) + 2 * bound(P, 2), name
-        assert _meta_ints(P, query_tile=1) == base_ints(P), name      # tiles off
+        assert _meta_ints(P) == base_ints(P), name                    # four-wave rows
+        assert _meta_ints(P, rope_head_dim=64) == base_ints(P) + 2 * bound(P, 2), name
+        assert _meta_ints(P, rope_head_dim=64, query_tile=1) == base_ints(P), name
+        assert _meta_ints(P, query_tile=2) == base_ints(P) + 2 * bound(P, 2), name
     P = synth.make_workload("swa_prefill_h16")
     assert _meta_ints(P, query_tile=8) == base_ints(P) + 2 * bound(P, 8)
     # TopK lists (csa), packed rows and 128 heads are never tiled
@@ -377,15 +380,16 @@ def test_tiled_call_lays_out_split_rows_with_every_head_in_one_group():
     long for one split) are split as without tiles, with every head in one
     workgroup: the workspace is that of one head group of 8 waves."""
     P = synth.make_workload("hca_prefill")
-    q = s.make_params(dict(P.params, max_seqlen_cmp_kv=4096), P.arrays)
+    q = s.make_params(dict(P.params, max_seqlen_cmp_kv=4096, query_tile=2), P.arrays)
     ws = s.sfmla_workspace_size(q)
     splits = -(-(128 + 4096) // 256)                     # all-visible rows: 256-row splits
     slots = P.params["q_t"] * splits * 128                # 8 waves x 16 heads
     up = lambda n: (n + 255) // 256 * 256
     assert ws == up(slots * 1024) + up(slots * 4)
-    # without tiles the 64 heads take 4 waves per group of the same size
-    assert s.sfmla_workspace_size(s.make_params(dict(P.params, max_seqlen_cmp_kv=4096,
-                                                     query_tile=1), P.arrays)) > 0
+    # without tiles (the rule for these rope-free rows) the 64 heads take the
+    # four-wave kernel: 4 waves x 16 heads per row and split
+    q = s.make_params(dict(P.params, max_seqlen_cmp_kv=4096), P.arrays)
+    assert s.sfmla_workspace_size(q) == up(slots // 2 * 1024) + up(slots // 2 * 4)
 
 
 # ---------------------------------------------------------------------------
@@ -400,10 +404,11 @@ def test_wave_pairs_override_is_validated():
     assert _meta_ints(P, wave_pairs=2) == _meta_ints(P, wave_pairs=1)
     _meta_ints(synth.make_workload("sfa_mla_rope"), wave_pairs=2)   # 128 heads: two groups
     # refused where pairs do not apply: packed rows, query tiles
-    for name in ("c8_packed_int8", "hca_prefill"):
-        with pytest.raises(s.SfmlaError, match="wave_pairs"):
-            _meta_ints(synth.make_workload(name), wave_pairs=2)
-    _meta_ints(synth.make_workload("hca_prefill"), query_tile=1, wave_pairs=2)
+    with pytest.raises(s.SfmlaError, match="wave_pairs"):
+        _meta_ints(synth.make_workload("c8_packed_int8"), wave_pairs=2)
+    with pytest.raises(s.SfmlaError, match="wave_pairs"):
+        _meta_ints(synth.make_workload("hca_prefill"), query_tile=2, wave_pairs=2)
+    _meta_ints(synth.make_workload("hca_prefill"), wave_pairs=2)
 
 
 def test_wave_pair_workspace_and_rule():
@@ -412,13 +417,16 @@ def test_wave_pair_workspace_and_rule():
     partial per group, which holds four pairs.  The rule takes pairs where
     the (row, split) units do not fill the GPU (a decode of 4 rows x 3
     splits), not for csa_prefill (512 rows x 3 splits of its 640-row lists),
-    whose 64 heads take one eight-wave group (128 heads of slots) without."""
+    whose 64 heads take the four-wave kernel (4 waves x 16 heads of slots);
+    the eight-wave kernel (forced through head_blocks_per_group) lays out
+    128 heads, four of its waves only gathering."""
     P = synth.make_workload("csa_prefill")
     ws = lambda **o: s.sfmla_workspace_size(s.make_params(dict(P.params, **o), P.arrays))
     up = lambda n: (n + 255) // 256 * 256
     slots = lambda heads: P.params["q_t"] * 3 * heads
     assert ws(wave_pairs=2) == up(slots(64) * 1024) + up(slots(64) * 4)
-    assert ws(wave_pairs=1) == up(slots(128) * 1024) + up(slots(128) * 4)
+    assert ws(wave_pairs=1) == up(slots(64) * 1024) + up(slots(64) * 4)
+    assert ws(head_blocks_per_group=4) == up(slots(128) * 1024) + up(slots(128) * 4)
     assert ws() == ws(wave_pairs=1)
     D = synth.make_workload("csa_decode_paged")            # 4 rows, 64 heads
     wd = lambda **o: s.sfmla_workspace_size(s.make_params(dict(D.params, **o), D.arrays))

@@ -143,6 +143,9 @@ def test_every_forward_variant_is_built(kernels):
                 # eight waves in four pairs (never tiled)
                 assert (8, dqk, vmode, fmt, 0, 1) in fwd
                 assert (8, dqk, vmode, fmt, 1, 1) not in fwd
+        # four waves, two workgroups per CU: d_qk 512 with V = K nope only
+        assert (4, 512, 0, fmt, 0, 0) in fwd
+        assert (4, 576, 0, fmt, 0, 0) not in fwd and (4, 512, 1, fmt, 0, 0) not in fwd
     # packed INT8 / FP8 rows, with and without rope, on four or eight waves
     # (never tiled)
     for fmt in (1, 2):
@@ -163,6 +166,9 @@ def test_forward_kernels_fit_their_waves_per_simd_and_the_lds(kernels):
         assert f["max_flat_workgroup_size"] == 64 * waves, key
         assert f["vgpr_count"] <= 2048 // waves, (key, f)
         assert f["group_segment_fixed_size"] <= LDS_BYTES, key
+        if waves == 4 and key[3] in (0, 3):
+            # the 16-bit four-wave kernel runs two workgroups per CU
+            assert f["vgpr_count"] <= 256 and 2 * f["group_segment_fixed_size"] <= LDS_BYTES, (key, f)
 
 
 def test_forward_kernels_use_no_scratch_in_the_main_loop(kernels, disasm):

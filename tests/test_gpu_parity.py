@@ -617,11 +617,12 @@ def test_tiny_tiled_parity(kw):
 
 
 def _mixed_tile_batch():
-    """Sequences by rule: 20 queries with a short union (tiled), 3 queries
-    (too few: one workgroup per row), 18 queries whose visible compressed
-    rows exceed one split (rows split in 256-row chunks and merged)."""
+    """Sequences by rule (rows with rope: tiles are the rule): 20 queries
+    with a short union (tiled), 3 queries (too few: one workgroup per row),
+    18 queries whose visible compressed rows exceed one split (rows split
+    in 256-row chunks and merged)."""
     return logical(41, q_lens=[20, 3, 18], ori_lens=[600, 900, 9000], qn=16, ratio=4, cmp_topk=0,
-                   win=(127, 0))
+                   win=(127, 0), rope=64)
 
 
 def test_tiled_batch_matches_oracle_and_is_batch_invariant_bitwise():
@@ -659,8 +660,8 @@ def test_untiled_rows_of_a_tiled_launch_equal_the_untiled_launch_bitwise():
 def test_tiled_metadata_from_other_params_is_rejected():
     import sparse_shared_kv_amd as s
     P = synth.make_workload("swa_prefill")
-    call = s.Call(P.params, P.arrays)
-    other = dict(P.params, ori_win_left=63)
+    call = s.Call(dict(P.params, query_tile=2), P.arrays)
+    other = dict(P.params, query_tile=2, ori_win_left=63)
     call_b = s.Call(other, P.arrays)
     call_b.plan()
     call.metadata.copy_(call_b.metadata)       # plan of different parameters (same size)
