@@ -420,15 +420,19 @@ __device__ __forceinline__ void codes_to_bf16(uint4 c, uint4& lo, uint4& hi) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) f[e] = (float)(int8_t)((w[q] >> (8 * e)) & 0xff);
     } else {
-      f[0] = __builtin_amdgcn_cvt_f32_fp8((int)w[q], 0);
-      f[1] = __builtin_amdgcn_cvt_f32_fp8((int)w[q], 1);
-      f[2] = __builtin_amdgcn_cvt_f32_fp8((int)w[q], 2);
-      f[3] = __builtin_amdgcn_cvt_f32_fp8((int)w[q], 3);
+      typedef __attribute__((ext_vector_type(2))) float f32x2;
+      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+      const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+      f[0] = a.x;
+      f[1] = a.y;
+      f[2] = b.x;
+      f[3] = b.y;
     }
-    o[2 * q] = (__builtin_bit_cast(uint32_t, f[0]) >> 16) |
-               (__builtin_bit_cast(uint32_t, f[1]) & 0xffff0000u);
-    o[2 * q + 1] = (__builtin_bit_cast(uint32_t, f[2]) >> 16) |
-                   (__builtin_bit_cast(uint32_t, f[3]) & 0xffff0000u);
+    // pairs to bf16 (round to nearest even: exact, as every code's value
+    // has at most 8 significant bits)
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    o[2 * q] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)f[0], (__bf16)f[1]});
+    o[2 * q + 1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)f[2], (__bf16)f[3]});
   }
   lo = make_uint4(o[0], o[1], o[2], o[3]);
   hi = make_uint4(o[4], o[5], o[6], o[7]);
