@@ -801,3 +801,49 @@ def test_wave_pairs_at_full_size_bitwise():
         torch.cuda.synchronize()
         assert int(call.status.item()) == 0
     assert torch.equal(outs[0][0], outs[1][0])
+
+
+# ---------------------------------------------------------------------------
+# four waves, two workgroups per CU (rope-free 16-bit rows, V = K nope)
+# ---------------------------------------------------------------------------
+
+W4_CASES = [
+    # float16, 48 heads (the fourth wave holds none), 300-row windows in two splits
+    dict(seed=990, family="swa", num_heads_q=48, batch=64, max_q=8, max_kv=900, win=(300, 0),
+         kv_dtype="fp16", layout_q="TND", lse=True),
+    # every visible compressed row, sinks, 64 heads
+    dict(seed=991, family="hca", num_heads_q=64, batch=48, max_q=8, max_kv=1200, win=(127, 0),
+         cmp_ratio=4, lse=True, sinks=True),
+    # TopK compressed rows, 16 heads (one wave holds heads), no LSE output
+    dict(seed=992, family="csa", num_heads_q=16, batch=40, max_q=12, max_kv=1500, win=(63, 0),
+         cmp_ratio=2, topk=400, lse=False),
+]
+
+
+@pytest.mark.parametrize("kw", W4_CASES, ids=lambda k: str(k["seed"]))
+def test_four_wave_kernel_matches_eight_waves_bitwise(kw):
+    """Calls of at least 256 (row, split) units with rope-free rows whose V
+    is the K nope run on four waves, two workgroups per CU (the workspace
+    shows it: 64 heads of partial per row and split instead of 128); split
+    rows are merged by the last split to arrive.  Same bits as the
+    eight-wave kernel (forced through head_blocks_per_group) and the
+    oracle's result on sampled rows."""
+    import sparse_shared_kv_amd as s
+    P = synth.random_tiny(**kw)
+    ws = lambda **o: s.sfmla_workspace_size(s.make_params(dict(P.params, **o), P.arrays))
+    assert 0 < ws() < ws(head_blocks_per_group=4)
+    outs = []
+    for bpg in (0, 4):
+        say(f"four waves seed {kw['seed']} head_blocks_per_group={bpg}")
+        call = s.Call(dict(P.params, head_blocks_per_group=bpg), P.arrays)
+        outs.append([None if t is None else t.clone() for t in call.run()])
+        torch.cuda.synchronize()
+        assert int(call.status.item()) == 0
+    assert torch.equal(outs[0][0], outs[1][0])
+    if outs[0][1] is not None:
+        assert torch.equal(outs[0][1], outs[1][1])
+    n = P.query_rows
+    rows = sorted({0, 1, n // 3, n // 2, n - 2, n - 1})
+    res = dict(O=outs[0][0].float().cpu().numpy(), status=0,
+               lse=None if outs[0][1] is None else outs[0][1].cpu().numpy())
+    check_outputs(P, res, oracle.forward(P, rows=rows), rows)
