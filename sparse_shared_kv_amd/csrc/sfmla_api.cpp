@@ -388,15 +388,11 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg, bool* 
   }
   const int blocks = (p.num_heads_q + 15) / 16;       // 16-head blocks of one wave each
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
-  // Packed rows: four waves (one per SIMD, the whole register file for the
-  // decode), or eight where a row has eight head blocks and the launch keeps
-  // kMinGroups workgroups with all of them in one group: each row is then
-  // gathered and decoded once instead of once per head group (throughput
-  // mode: c8_packed_int8_q32 470 -> 280 us; at the packed configuration's
-  // 8 rows four waves stay faster, 40 vs 54 us).  The two kernels give the
-  // same bits (same per-wave arithmetic; the merge adds splits in order).
+  // Packed rows: eight waves, two per SIMD, the decode and the gather of a
+  // tile spread over all of them (a four-wave kernel with one wave per SIMD
+  // and the whole register file measured slower at every size:
+  // c8_packed_int8_q32 470 vs 280 us, c8_packed_int8 39.3 vs 37.6).
   int wmax = 8;
-  if (packed && !(blocks >= 8 && units >= kMinGroups) && p.head_blocks_per_group != 8) wmax = 4;
   // 16-bit rows without rope whose V is the K nope, at most 64 heads, in a
   // launch that fills the GPU: four waves, two workgroups per CU (every
   // SIMD then has two waves in the products; eight waves with four holding

@@ -2028,20 +2028,14 @@ static hipError_t launch_pair_t(const FwdArgs& a, int groups, hipStream_t s, hip
   return hipGetLastError();
 }
 
-// Eight waves per workgroup for bf16 rows; four or eight for packed rows
-// (four: one wave per SIMD with the whole register file for the decode;
-// eight: every head of a row in one workgroup, each row gathered and
-// decoded once).  Both give the same bits.
+// Packed rows: eight waves per workgroup (two per SIMD; the gather and the
+// decode of a tile spread over all of them)
 template <int FMT>
 static hipError_t launch_packed(const FwdArgs& a, int nw, int dqk, int groups, int mw,
                                 hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  if (nw == 8)
-    return dqk == 512 ? launch_fwd_t<8, 512, 0, FMT>(a, groups, mw, s, t0, t1)
-                      : launch_fwd_t<8, 576, 0, FMT>(a, groups, mw, s, t0, t1);
-  if (nw == 4)
-    return dqk == 512 ? launch_fwd_t<4, 512, 0, FMT>(a, groups, mw, s, t0, t1)
-                      : launch_fwd_t<4, 576, 0, FMT>(a, groups, mw, s, t0, t1);
-  return hipErrorInvalidConfiguration;
+  if (nw != 8) return hipErrorInvalidConfiguration;
+  return dqk == 512 ? launch_fwd_t<8, 512, 0, FMT>(a, groups, mw, s, t0, t1)
+                    : launch_fwd_t<8, 576, 0, FMT>(a, groups, mw, s, t0, t1);
 }
 
 hipError_t launch_forward(const FwdArgs& a, int nw, bool pair, int dqk, int vmode, int fmt,

@@ -172,8 +172,8 @@ def test_workspace_sizes():
 def _expected_workspace(P):
     """The split partials' workspace from the host's documented policy:
     512-row splits for rows of 2 KB or more, 256 otherwise; head groups of
-    1/2/4/8 16-head blocks (at most 4 per group for packed rows), halved
-    while the grid would have fewer than 256 workgroups; 16-bit rows with
+    1/2/4/8 16-head blocks on eight waves, halved while the grid would have
+    fewer than 256 workgroups; 16-bit rows with
     fewer than 256 (row, split) units on wave pairs (groups of 1/2/4 pairs);
     one bf16 partial (1 KB per padded head) and one fp32 LSE per (row,
     split, padded head)."""
@@ -199,7 +199,7 @@ def _expected_workspace(P):
             per //= 2
         heads = -(-blocks // per) * 8 * 8
     else:
-        wmax = 4 if packed else 8
+        wmax = 8
         per = 1
         while per < wmax and per < blocks:
             per *= 2

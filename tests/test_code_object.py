@@ -146,21 +146,20 @@ def test_every_forward_variant_is_built(kernels):
         # four waves, two workgroups per CU: d_qk 512 with V = K nope only
         assert (4, 512, 0, fmt, 0, 0) in fwd
         assert (4, 576, 0, fmt, 0, 0) not in fwd and (4, 512, 1, fmt, 0, 0) not in fwd
-    # packed INT8 / FP8 rows, with and without rope, on four or eight waves
-    # (never tiled)
+    # packed INT8 / FP8 rows, with and without rope, on eight waves (never
+    # tiled, no wave pairs)
     for fmt in (1, 2):
         for dqk in (512, 576):
-            for waves in (4, 8):
-                assert (waves, dqk, 0, fmt, 0, 0) in fwd
-                assert (waves, dqk, 0, fmt, 1, 0) not in fwd
-                assert (waves, dqk, 0, fmt, 0, 1) not in fwd
+            assert (8, dqk, 0, fmt, 0, 0) in fwd
+            assert (4, dqk, 0, fmt, 0, 0) not in fwd
+            assert (8, dqk, 0, fmt, 1, 0) not in fwd
+            assert (8, dqk, 0, fmt, 0, 1) not in fwd
     assert any("plan_kernel" in k for k in kernels)
     assert any("combine_kernel" in k for k in kernels)
 
 
 def test_forward_kernels_fit_their_waves_per_simd_and_the_lds(kernels):
-    # one workgroup per CU: 8 waves are two per SIMD (256 VGPRs each), the
-    # 4-wave packed kernel one per SIMD (up to 512)
+    # one workgroup per CU: 8 waves are two per SIMD (256 VGPRs each)
     for key, f in _fwd(kernels).items():
         waves = key[0]
         assert f["max_flat_workgroup_size"] == 64 * waves, key
