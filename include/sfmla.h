@@ -186,11 +186,11 @@ typedef struct sfmla_params {
    * and merge_wait_us have no effect on a tiled call, which needs no
    * workspace. */
   int32_t query_tile;
-  /* Wave pairs (0 = the library's rule) for calls without query tiles whose
-   * rows are bf16 or float16: two waves share 16 heads, each computes the
-   * scores of half of every 32-row KV tile and accumulates half of the 512
-   * value columns, so each wave's chain of products per tile is half as
-   * long.  Results are bitwise the same either way.
+  /* Wave pairs (0 = the library's rule) for calls without query tiles: two
+   * waves share 16 heads, each computes the scores of half of every 32-row
+   * KV tile and accumulates half of the 512 value columns, so each wave's
+   * chain of products per tile is half as long.  Results are bitwise the
+   * same either way.
    *   1  never;
    *   2  always (refused where the parameters do not allow pairs).
    * The rule takes pairs where the call has fewer than 256 (query row,

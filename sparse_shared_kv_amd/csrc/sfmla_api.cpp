@@ -149,7 +149,7 @@ sfmla_status validate(const sfmla_params* pp) {
   REQUIRE(p.wave_pairs >= 0 && p.wave_pairs <= 2, "wave_pairs must be 0, 1 or 2");
   if (p.wave_pairs == 2)
     REQUIRE(pair_eligible(p),
-            "wave_pairs 2 needs bf16 or float16 KV and no query tiles");
+            "wave_pairs 2 needs a call without query tiles");
   if (p.query_tile > 1) {
     REQUIRE(tile_eligible(p) && p.query_tile <= tile_limit(p),
             "query_tile %d needs rule lists (ori_topk = cmp_topk = 0), bf16 or float16 KV "
@@ -345,10 +345,8 @@ WsLayout workspace_layout(const sfmla_params& p) {
 
 size_t workspace_bytes(const sfmla_params& p) { return workspace_layout(p).total; }
 
-// Wave pairs: 16-bit rows in a call without query tiles.
-bool pair_eligible(const sfmla_params& p) {
-  return (p.kv_dtype == SFMLA_KV_BF16 || p.kv_dtype == SFMLA_KV_FP16) && query_tile(p) <= 1;
-}
+// Wave pairs: any call without query tiles (16-bit or packed rows).
+bool pair_eligible(const sfmla_params& p) { return query_tile(p) <= 1; }
 
 // Workgroup shape: nw waves; the heads of a query row are cut into `groups`
 // head groups of bpg 16-head blocks (bpg <= nw), one block per wave, and the

@@ -829,7 +829,7 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
   constexpr bool PK = FMT != SFMLA_KV_BF16 && !HALF;   // packed rows (V = decoded nope)
   static_assert(!PK || VMODE == 0, "packed KV has no separate V");
   static_assert(!TILED || (!PK && NW == 8 && HB == 1), "query tiles: 16-bit rows, 8 waves");
-  static_assert(!PAIR || (!PK && !TILED && NW == 8 && HB == 1), "wave pairs: 16-bit rows, 8 waves");
+  static_assert(!PAIR || (!TILED && NW == 8 && HB == 1), "wave pairs: 8 waves");
   constexpr bool W4 = kTwoPerCu<NW, FMT>;
   static_assert(!W4 || (VMODE == 0 && DQK == 512 && !TILED && !PAIR && HB == 1),
                 "four-wave 16-bit rows: d_qk 512, V = K nope");
@@ -1167,12 +1167,16 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
     f32x4 s[HB][2];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // wave pairs: this wave's 16-row half of the scores (the partner's comes
+    // through LDS below)
+    f32x4 sm[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) sm[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (PK) {
       // Packed rows: exact scaling, one partial product per 128-column scale
       // tile, taken one 16-row half of the tile at a time (the partial sums,
       // K operands and row scales of one half are live at once).
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      auto pk_half = [&](int half, auto&& acc) __attribute__((always_inline)) {
         const char* kp = sK + (16 * half + t) * RS + 16 * g;
         auto kload = [&](int ks) -> bf16x8 {
           if (!C::ROPE || ks < 16) return *(const bf16x8*)(kp + 64 * ks);
@@ -1199,20 +1203,24 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
             if (ks < 16) {
               const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
               sp[hb] = mfma16<HALF>(kv, qreg[hb][ks < NQR ? ks : 0], ks % 4 ? sp[hb] : z);
-              if (ks % 4 == 3) s[hb][half] += sp[hb] * scq;
+              if (ks % 4 == 3) acc(hb) += sp[hb] * scq;
             } else {
               const bf16x8 qv = ks < NQR ? qreg[hb][ks < NQR ? ks : 0] : qlds[ks >= NQR ? ks - NQR : 0];
-              s[hb][half] = mfma16<HALF>(kv, qv, s[hb][half]);
+              acc(hb) = mfma16<HALF>(kv, qv, acc(hb));
             }
           }
           if (ks + PF < NKS) kb[ks % PF] = kload(ks + PF);
         }
+      };
+      if constexpr (PAIR) {
+        if (wave_on) pk_half(hf, [&](int hb) -> f32x4& { return sm[hb]; });
+      } else {
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          pk_half(half, [&](int hb) -> f32x4& { return s[hb][half]; });
       }
     } else if constexpr (PAIR) {
-      // this wave's 16 rows of the tile; the partner's scores come through LDS
-      f32x4 sm[HB];
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) sm[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // this wave's 16 rows of the tile
       if (wave_on) {
         const int r = 16 * hf + t;
         const char* kp = sK + r * RS + 16 * g;
@@ -1234,18 +1242,6 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
           if (ks + PF < NKS) kb[ks % PF] = kload(ks + PF);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) sSx[w][hb][l] = sm[hb];
-      }
-      wait_lgkm0();
-      block_barrier();                              // both halves' scores are in
-      if (wave_on) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          const f32x4 so = sSx[w ^ 1][hb][l];
-          s[hb][0] = hf ? so : sm[hb];
-          s[hb][1] = hf ? sm[hb] : so;
-        }
       }
     } else {
       const char* kp0 = sK + t * RS + 16 * g;
@@ -1274,6 +1270,23 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
           s[hb][1] = mfma16<HALF>(k1v, qreg[hb][ks < NQR ? ks : 0], s[hb][1]);
         }
         if (ks + PF < NKS) kload(ks + PF, kb[ks % PF][0], kb[ks % PF][1]);
+      }
+    }
+    if constexpr (PAIR) {
+      // swap the halves' raw scores within the pair
+      if (wave_on) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) sSx[w][hb][l] = sm[hb];
+      }
+      wait_lgkm0();
+      block_barrier();                              // both halves' scores are in
+      if (wave_on) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const f32x4 so = sSx[w ^ 1][hb][l];
+          s[hb][0] = hf ? so : sm[hb];
+          s[hb][1] = hf ? sm[hb] : so;
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1334,8 +1347,9 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       if (PK && mb % 8 == 0) {
-        const f32x4 c0 = *(const f32x4*)(sScale + (mb / 8) * T + 4 * g);
-        const f32x4 c1 = *(const f32x4*)(sScale + (mb / 8) * T + 16 + 4 * g);
+        const int grp = mb / 8 + (PAIR ? 2 * hf : 0);   // 128-column scale tile
+        const f32x4 c0 = *(const f32x4*)(sScale + grp * T + 4 * g);
+        const f32x4 c1 = *(const f32x4*)(sScale + grp * T + 16 + 4 * g);
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -1363,7 +1377,10 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
       decode_tile<NW, DQK, FMT>(sWc, sK0, sScale, tid);
       wait_lgkm0();
       block_barrier();                          // decoded tile complete
-      if (wave_on) {
+      if constexpr (PAIR) {
+        qk_softmax(sK0, tt * T);                // (a barrier inside)
+        if (wave_on) pv(sK0);
+      } else if (wave_on) {
         qk_softmax(sK0, tt * T);
         pv(sK0);
       }
@@ -2054,7 +2071,13 @@ hipError_t launch_forward(const FwdArgs& a, int nw, bool pair, int dqk, int vmod
       return vmode ? launch_pair_t<576, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
                    : launch_pair_t<576, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
     }
-    return hipErrorInvalidConfiguration;            // packed rows have no wave pairs
+    if (fmt == SFMLA_KV_INT8_PACKED)
+      return dqk == 512 ? launch_pair_t<512, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1)
+                        : launch_pair_t<576, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1);
+    if (fmt == SFMLA_KV_FP8_E4M3_PACKED)
+      return dqk == 512 ? launch_pair_t<512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1)
+                        : launch_pair_t<576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1);
+    return hipErrorInvalidConfiguration;
   }
   switch (fmt) {
     case SFMLA_KV_INT8_PACKED:

@@ -173,8 +173,8 @@ def _expected_workspace(P):
     """The split partials' workspace from the host's documented policy:
     512-row splits for rows of 2 KB or more, 256 otherwise; head groups of
     1/2/4/8 16-head blocks on eight waves, halved while the grid would have
-    fewer than 256 workgroups; 16-bit rows with
-    fewer than 256 (row, split) units on wave pairs (groups of 1/2/4 pairs);
+    fewer than 256 workgroups; calls with fewer than 256 (row, split)
+    units on wave pairs (groups of 1/2/4 pairs);
     one bf16 partial (1 KB per padded head) and one fp32 LSE per (row,
     split, padded head)."""
     p = P.params
@@ -190,7 +190,7 @@ def _expected_workspace(P):
         return 0
     blocks = -(-p["num_heads_q"] // 16)
     units = p["q_t"] * splits
-    if not packed and units < 256:
+    if units < 256:
         # wave pairs: groups of up to 4 pairs of 16 heads, eight waves of
         # 16 heads x 256 columns of partial each
         per = min(4, blocks)
@@ -403,9 +403,8 @@ def test_wave_pairs_override_is_validated():
             _meta_ints(P, wave_pairs=bad)
     assert _meta_ints(P, wave_pairs=2) == _meta_ints(P, wave_pairs=1)
     _meta_ints(synth.make_workload("sfa_mla_rope"), wave_pairs=2)   # 128 heads: two groups
-    # refused where pairs do not apply: packed rows, query tiles
-    with pytest.raises(s.SfmlaError, match="wave_pairs"):
-        _meta_ints(synth.make_workload("c8_packed_int8"), wave_pairs=2)
+    _meta_ints(synth.make_workload("c8_packed_int8"), wave_pairs=2)  # packed rows
+    # refused where pairs do not apply: query tiles
     with pytest.raises(s.SfmlaError, match="wave_pairs"):
         _meta_ints(synth.make_workload("hca_prefill"), query_tile=2, wave_pairs=2)
     _meta_ints(synth.make_workload("hca_prefill"), wave_pairs=2)

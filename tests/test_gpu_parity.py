@@ -741,6 +741,12 @@ PAIR_CASES = [
     # 128 heads: two head groups of four pairs, rope, separate V, 4 splits
     dict(seed=956, family="sfa", max_kv=4000, topk=2048, num_heads_q=128, rope_head_dim=64,
          separate_v=True, sinks=True, lse=True),
+    # packed rows: INT8 with rope (8 splits of the TopK list), FP8 without
+    # rope, 20 heads (the second pair of its group half empty)
+    dict(seed=957, family="sfa", kv_dtype="int8_packed", max_kv=3000, topk=2048,
+         num_heads_q=128, rope_head_dim=64, sinks=True, lse=True),
+    dict(seed=958, family="sfa", kv_dtype="fp8_e4m3_packed", max_kv=1500, topk=700, num_heads_q=20,
+         rope_head_dim=0, lse=True),
 ]
 
 
