@@ -22,7 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import decode as _decode
-from .decode import bf16_to_f64, decode_packed
+from .decode import bf16_to_f64, decode_packed, decode_packed_value
 
 
 def elem_to_f64(P):
@@ -38,7 +38,8 @@ def _rows_kv(P, phys: np.ndarray):
     bf16 KV: K is the row's first 512 + rope values; V is the first 512
     (K~ = V~, API page 功能说明) unless the original side carries its own
     value tensor (SparseFlashAttention page, 参数说明 value).  Packed KV:
-    decode.decode_packed.
+    decode.decode_packed, or with a value tensor of codes,
+    decode.decode_packed_value (KV quant blog, 参数说明 value).
     """
     p = P.params
     rope = int(p["rope_head_dim"])
@@ -62,6 +63,9 @@ def _rows_kv(P, phys: np.ndarray):
                 v = k[:, :512]
         else:
             k, v = decode_packed(rows, rope, p["kv_dtype"])
+            if side == "ori" and p.get("separate_v"):
+                v = decode_packed_value(np.asarray(P.arrays["ori_v"])[rid[sel]], rows, rope,
+                                        p["kv_dtype"])
         K[sel] = k
         V[sel] = v
     return K, V

@@ -93,7 +93,19 @@ def _decode(P, side, phys):
         else:
             v = k[:, :512]
         return k, v
-    return _packed(src, rope, p["kv_dtype"])
+    k, v = _packed(src, rope, p["kv_dtype"])
+    if side == "ori" and p.get("separate_v"):
+        # value codes (dtype of the key's codes), scaled per 128 columns by the
+        # key row's scales
+        vc = torch.from_numpy(np.ascontiguousarray(np.asarray(P.arrays["ori_v"])[phys][:, :512],
+                                                   dtype=np.uint8))
+        dt = torch.int8 if p["kv_dtype"] == "int8_packed" else torch.float8_e4m3fn
+        x = vc.view(dt).to(torch.float64)
+        sc_at = 512 + 2 * rope
+        sc = torch.from_numpy(np.ascontiguousarray(src[:, sc_at:sc_at + 16], dtype=np.uint8))
+        sc = sc.view(torch.float32).to(torch.float64).reshape(-1, 4)
+        v = (x.reshape(-1, 4, 128) * sc[:, :, None]).reshape(-1, 512).numpy()
+    return k, v
 
 
 def brute_force(P):

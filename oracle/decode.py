@@ -95,3 +95,31 @@ def decode_packed(rows_u8: np.ndarray, rope_dim: int, fmt: str):
     else:
         k = nope
     return k, nope
+
+
+def decode_packed_value(value_u8: np.ndarray, key_rows_u8: np.ndarray, rope_dim: int, fmt: str):
+    """V rows from a value tensor of 512 codes per row (same format as the key's
+    codes), each 128-column tile scaled by the matching key row's fp32 scale.
+
+    Reading: the blog's value parameter may be a 512-wide NoPE tensor instead
+    of the packed key cache itself; its dtype follows the key, its quant mode
+    is per-tile and its own dequant-scale input is reserved, while the
+    effective V is stated to be the key's dequantised NoPE, so the scales are
+    the key row's.  With the key's own codes in it, V equals decode_packed's.
+    """
+    value_u8 = np.asarray(value_u8, dtype=np.uint8)
+    key_rows_u8 = np.asarray(key_rows_u8, dtype=np.uint8)
+    n = value_u8.shape[0]
+    if value_u8.shape[1] < 512:
+        raise ValueError("value rows narrower than 512 bytes")
+    codes = value_u8[:, :512]
+    if fmt == "int8_packed":
+        x = int8_to_f64(codes)
+    elif fmt == "fp8_e4m3_packed":
+        x = fp8_e4m3fn_to_f64(codes)
+    else:
+        raise ValueError(fmt)
+    _, scale_off, _ = packed_layout(rope_dim)
+    scales = np.ascontiguousarray(key_rows_u8[:, scale_off:scale_off + 16]).view("<f4")
+    scales = scales.astype(np.float64).reshape(n, 4)
+    return x * np.repeat(scales, 128, axis=1)

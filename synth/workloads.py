@@ -504,7 +504,14 @@ def random_tiny(seed, *, family=None, layout_q=None, layout_kv=None,
     elif any(n != params["ori_kv_s"] for n in ori_lens) or g.integers(0, 2):
         arrays["seqused_ori_kv"] = np.asarray(ori_lens, np.int32)
     if separate_v:
-        arrays["ori_v"] = kv_rows(s_v, arrays["ori_kv"].shape[0], 512)
+        if packed:
+            # a value tensor of 512 codes per row in the key's format (codes
+            # of an independent quantised draw)
+            arrays["ori_v"] = np.ascontiguousarray(
+                packed_rows(s_v, arrays["ori_kv"].shape[0], 0,
+                            "int8" if kv_dtype == "int8_packed" else "fp8")[:, :512])
+        else:
+            arrays["ori_v"] = kv_rows(s_v, arrays["ori_kv"].shape[0], 512)
 
     if has_cmp:
         kind, table = place("cmp_kv", cmp_lens, s_cmp,

@@ -98,6 +98,10 @@ for s in range(8):                                  # float16 q / kv / output
 for s in range(9):                                  # block-wise TopK (R18)
     CASES.append(dict(seed=400 + s, family="sfa", sparse_block_size=[2, 4, 16][s % 3],
                       max_kv=90, duplicates=bool(s % 4 == 3)))
+for s in range(6):                                  # packed rows with a value tensor (R20)
+    CASES.append(dict(seed=600 + s, family="sfa", separate_v=True,
+                      kv_dtype=["int8_packed", "fp8_e4m3_packed"][s % 2],
+                      rope_head_dim=[0, 64][(s // 2) % 2], duplicates=bool(s == 5)))
 
 
 @pytest.mark.parametrize("kw", CASES, ids=lambda k: "-".join("%s" % v for v in k.values()))
@@ -347,6 +351,58 @@ def test_packed_equals_float_on_dequantised_values(fmt, rope):
     F.params["kv_dtype"] = "bf16"
     F.arrays["ori_kv"] = np.concatenate(parts, axis=1)
     assert np.array_equal(deq.to(torch.bfloat16).double().numpy(), deq.numpy())  # exact in bf16
+    a, b = oracle.forward(P), oracle.forward(F)
+    assert np.array_equal(a["O"], b["O"]) and np.array_equal(a["lse"], b["lse"])
+
+
+@pytest.mark.parametrize("fmt", ["int8_packed", "fp8_e4m3_packed"])
+@pytest.mark.parametrize("rope", [0, 64])
+def test_packed_value_tensor_of_the_key_codes_equals_the_aliased_value(fmt, rope):
+    """A value tensor holding the key rows' own 512 codes gives the same
+    result, bit for bit, as taking V from the packed key rows (KV quant blog,
+    参数说明 value: key and value may be the same packed cache)."""
+    P = synth.random_tiny(41, family="sfa", kv_dtype=fmt, rope_head_dim=rope, num_heads_q=3,
+                          separate_v=False)
+    V = P.copy()
+    V.params["separate_v"] = True
+    V.arrays["ori_v"] = np.ascontiguousarray(P.arrays["ori_kv"][:, :512])
+    a, b = oracle.forward(P), oracle.forward(V)
+    assert np.array_equal(a["O"], b["O"]) and np.array_equal(a["lse"], b["lse"])
+    # a value tensor with other codes changes O but not the scores' LSE
+    W = V.copy()
+    W.arrays["ori_v"] = np.ascontiguousarray(W.arrays["ori_v"][::-1])
+    c = oracle.forward(W)
+    assert np.array_equal(a["lse"], c["lse"]) and not np.allclose(a["O"], c["O"])
+
+
+@pytest.mark.parametrize("fmt", ["int8_packed", "fp8_e4m3_packed"])
+@pytest.mark.parametrize("rope", [0, 64])
+def test_packed_value_tensor_equals_float_value_on_dequantised_codes(fmt, rope):
+    """Value codes scaled by the key row's per-tile scales: with power-of-two
+    scales the products are exact in bf16, so the packed problem equals the
+    bf16 problem with a separate V of those products (the bf16 separate-V
+    path is pinned by brute force and SDPA)."""
+    P = synth.random_tiny(43, family="sfa", kv_dtype=fmt, rope_head_dim=rope, num_heads_q=3,
+                          separate_v=True)
+    rows = P.arrays["ori_kv"].copy()
+    n = rows.shape[0]
+    so = 512 + 2 * rope
+    exps = np.random.default_rng(2).integers(-8, 3, size=(n, 4))
+    rows[:, so:so + 16] = (2.0 ** exps).astype("<f4").view(np.uint8).reshape(n, 16)
+    P.arrays["ori_kv"] = rows
+    dt = torch.int8 if fmt == "int8_packed" else torch.float8_e4m3fn
+    scale = torch.from_numpy(np.repeat(2.0 ** exps, 128, axis=1))
+    kx = torch.from_numpy(rows[:, :512].copy()).view(dt).double() * scale
+    vx = torch.from_numpy(np.ascontiguousarray(P.arrays["ori_v"])).view(dt).double() * scale
+    for t in (kx, vx):
+        assert np.array_equal(t.to(torch.bfloat16).double().numpy(), t.numpy())   # exact
+    parts = [kx.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)]
+    if rope:
+        parts.append(rows[:, 512:512 + 2 * rope].copy().view(np.uint16))
+    F = P.copy()
+    F.params["kv_dtype"] = "bf16"
+    F.arrays["ori_kv"] = np.concatenate(parts, axis=1)
+    F.arrays["ori_v"] = vx.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     a, b = oracle.forward(P), oracle.forward(F)
     assert np.array_equal(a["O"], b["O"]) and np.array_equal(a["lse"], b["lse"])
 

@@ -25,6 +25,8 @@ def _pins():
         ("fp8", T.test_fp8_decoder_matches_torch_all_codes),
         ("fp16", T.test_fp16_decoder_matches_torch_all_codes),
         ("packed", lambda: T.test_packed_equals_float_on_dequantised_values("int8_packed", 64)),
+        ("packed_value", lambda: T.test_packed_value_tensor_equals_float_value_on_dequantised_codes(
+            "fp8_e4m3_packed", 0)),
         ("layout", lambda: T.test_layout_and_block_permutation_invariance("csa")),
         ("sink", T.test_sink_closed_form),
         ("merge", T.test_split_merge_equals_unsplit),
@@ -52,6 +54,7 @@ _orig_fp8 = odec.fp8_e4m3fn_to_f64
 _orig_packed = odec.decode_packed
 _orig_block_tokens = ores.block_tokens
 _orig_fp16 = odec.fp16_to_f64
+_orig_packed_value = odec.decode_packed_value
 
 
 def _band_exclusive(mode, j, p, n, left, right):
@@ -108,6 +111,19 @@ def _fp16_bias16(bits):
     return _orig_fp16(bits) * 0.5                       # exponent bias 16 instead of 15
 
 
+def _packed_value_ignored(value_u8, key_rows_u8, rope_dim, fmt):
+    return _orig_packed(key_rows_u8, rope_dim, fmt)[1]  # V from the key's own codes
+
+
+def _packed_value_one_scale(value_u8, key_rows_u8, rope_dim, fmt):
+    rows = np.array(key_rows_u8, copy=True)
+    so = 512 + 2 * rope_dim
+    sc = rows[:, so:so + 4].copy()
+    for t in range(1, 4):                               # every tile takes tile 0's scale
+        rows[:, so + 4 * t:so + 4 * t + 4] = sc
+    return _orig_packed_value(value_u8, rows, rope_dim, fmt)
+
+
 def _block_offset_dropped(v, sbs):
     return [v + u for u in range(sbs)]                  # forgets the block stride
 
@@ -124,6 +140,8 @@ MUTANTS = {
     "value_taken_from_wrong_columns": (oatt, "attend", _v_from_rope),
     "block_offset_dropped": (ores, "block_tokens", _block_offset_dropped),
     "fp16_exponent_bias_off_by_one": (odec, "fp16_to_f64", _fp16_bias16),
+    "packed_value_tensor_ignored": (oatt, "decode_packed_value", _packed_value_ignored),
+    "packed_value_one_scale_for_all_tiles": (oatt, "decode_packed_value", _packed_value_one_scale),
 }
 
 
