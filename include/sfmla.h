@@ -135,7 +135,8 @@ typedef struct sfmla_params {
   int32_t has_ori_kv;    /* must be 1                                         */
   int32_t has_cmp_kv;    /* 0 or 1                                            */
   int32_t kv_dtype;      /* SFMLA_KV_*                                        */
-  int32_t has_separate_v;      /* bf16 ori side only: V read from ori_v       */
+  int32_t has_separate_v;      /* ori side: V read from ori_v (16-bit rows, or
+                                  packed KV's value codes)                     */
   int32_t has_sinks;           /* sinks pointer present                       */
   int32_t return_softmax_lse;  /* softmax_lse pointer present                 */
   int32_t has_seqused_q;       /* which optional length tensors are passed    */
@@ -240,7 +241,12 @@ typedef struct sfmla_lengths {
  *                ori_rope is NULL) 64 rope values; packed rows: 512 codes,
  *                2*rope bytes of bf16 rope, 16 bytes of fp32 scales
  *   ori_rope     bf16 rope rows (64 values) when stored apart; else NULL
- *   ori_v        bf16 value rows (512) when has_separate_v; else NULL
+ *   ori_v        when has_separate_v (else NULL), rows indexed like ori_kv's
+ *                (at least ori_kv_rows of them): bf16 / fp16 value rows of
+ *                512 values; with packed KV, 512 value codes per row in the
+ *                key's format, each 128-column tile scaled by the key row's
+ *                scale of that tile (KV quant blog, 参数说明 value: a 512-wide
+ *                NoPE value tensor whose own dequant scale is reserved)
  *   cmp_kv / cmp_rope   as ori_kv / ori_rope (no separate V)
  *   ori_block_table / cmp_block_table   int32 (b, *_block_table_cols), PA only
  *   ori_sparse_indices  int32 (q_t, 1, ori_topk) when ori_topk > 0

@@ -269,7 +269,8 @@ class Call:
         kv_types = (torch.uint8,) if packed else (half, torch.int16)
         for name in ("ori_kv", "cmp_kv"):
             _require_rows(d.get(name), name, kv_types)
-        for name in ("ori_v", "ori_rope", "cmp_rope"):
+        _require_rows(d.get("ori_v"), "ori_v", kv_types)   # packed: value codes
+        for name in ("ori_rope", "cmp_rope"):
             _require_rows(d.get(name), name, (half, torch.int16))
 
     def _tensors(self) -> Tensors:

@@ -132,6 +132,9 @@ sfmla_status validate(const sfmla_params* pp) {
               p.kv_dtype == SFMLA_KV_INT8_PACKED ||
               p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED,
           "unknown kv_dtype");
+  REQUIRE(!(p.has_separate_v && p.has_cmp_kv &&
+            (p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED)),
+          "a value tensor with packed KV is for the token-wise TopK form (no cmp_kv)");
   REQUIRE(p.split_rows == 0 ||
               (p.split_rows >= sfmla::kTile && p.split_rows <= sfmla::kMaxSplitRows &&
                p.split_rows % sfmla::kTile == 0),
@@ -156,8 +159,6 @@ sfmla_status validate(const sfmla_params* pp) {
             "and %d rows x 16-head blocks <= 8",
             p.query_tile, p.query_tile);
   }
-  REQUIRE(!(p.has_separate_v && p.kv_dtype != SFMLA_KV_BF16 && p.kv_dtype != SFMLA_KV_FP16),
-          "a separate V is only supported for bf16 KV (packed V is the dequantised nope)");
   if (p.layout_kv == SFMLA_LAYOUT_BSND) REQUIRE(p.ori_kv_s > 0, "BSND ori_kv needs ori_kv_s > 0");
   if (p.layout_kv == SFMLA_LAYOUT_PA_BSND) {
     REQUIRE(p.ori_block_size >= 1 && p.ori_block_size <= 1024, "ori_block_size must be in 1..1024");
@@ -226,6 +227,7 @@ int split_rows(const sfmla_params& p) {
   const bool packed = p.kv_dtype == SFMLA_KV_INT8_PACKED || p.kv_dtype == SFMLA_KV_FP8_E4M3_PACKED;
   const int row_bytes = packed ? 512 + 2 * p.rope_head_dim + 16
                                : 2 * (512 + p.rope_head_dim) + (p.has_separate_v ? 1024 : 0);
+  // (packed rows with a value tensor add 512 code bytes: still below 2 KB)
   const int base = row_bytes >= 2048 ? 512 : 256;
   // Where the parameters alone bound the list (TopK slot counts, a window
   // open on both sides), the longest list is cut into even splits of at most
@@ -441,9 +443,12 @@ sfmla_status fill_fwd_args(const sfmla_params& p, const sfmla_tensors* t, const 
             "ori_rope must be 16-byte aligned with a stride >= 128, multiple of 16");
   }
   REQUIRE((p.has_separate_v != 0) == (t->ori_v != nullptr), "has_separate_v must match ori_v");
-  if (t->ori_v)
-    REQUIRE(aligned16(t->ori_v) && t->ori_v_stride >= 1024 && t->ori_v_stride % 16 == 0,
-            "ori_v must be 16-byte aligned with a stride >= 1024, multiple of 16");
+  if (t->ori_v) {
+    // 16-bit V rows (512 values), or packed KV's value codes (512 bytes)
+    const int64_t vmin = packed ? 512 : 1024;
+    REQUIRE(aligned16(t->ori_v) && t->ori_v_stride >= vmin && t->ori_v_stride % 16 == 0,
+            "ori_v must be 16-byte aligned with a stride >= %lld, multiple of 16", (long long)vmin);
+  }
   if (p.has_cmp_kv) {
     REQUIRE(t->cmp_kv && aligned16(t->cmp_kv), "cmp_kv must be a 16-byte aligned device pointer");
     const int64_t need_c = packed ? 512 + 2 * p.rope_head_dim + 16

@@ -665,19 +665,22 @@ __device__ __forceinline__ int fresh(int x) {
   return x;
 }
 
-template <int NW, int DQK>
+template <int NW, int DQK, int VC = 0>
 struct PackedPipe {
   static constexpr int ROPE = DQK - 512;                     // rope values per row
-  static constexpr int CPR = (512 + 2 * ROPE + 16) / 16;      // 16-byte chunks per row
+  static constexpr int KC = (512 + 2 * ROPE + 16) / 16;       // 16-byte chunks of a key row
+  // chunks per row in the stage: the key row, then (VC) the row's 512 value
+  // codes from the value tensor
+  static constexpr int CPR = KC + (VC ? 32 : 0);
   static constexpr int NI = (kTile * CPR + 63) / 64;          // instructions per tile
   static constexpr int PER = (NI + NW - 1) / NW;              // per wave
   static constexpr int RAWB = PER * NW * 1024;                // LDS bytes per stage
 };
 
-template <int NW, int DQK>
+template <int NW, int DQK, int VC = 0>
 __device__ __forceinline__ void issue_raw(const FwdArgs& a, const uint32_t* sRow, int tbase,
                                           uint32_t ldsRaw, int w, int l) {
-  using P = PackedPipe<NW, DQK>;
+  using P = PackedPipe<NW, DQK, VC>;
   if constexpr (NW == 8) l = fresh(l);   // two waves per SIMD: no room for hoisted addresses
   const uint32_t base = __builtin_amdgcn_readfirstlane(ldsRaw + w * P::PER * 1024);
   // every row entry first (one LDS round trip for all), then branch-free
@@ -693,11 +696,22 @@ __device__ __forceinline__ void issue_raw(const FwdArgs& a, const uint32_t* sRow
   for (int q = 0; q < P::PER; ++q) {
     const int c = (w * P::PER + q) * 64 + l;
     const int r = c / P::CPR;
-    const bool cmp = e[q] & kCmpBit;
-    const char* rowp = row_at(cmp ? a.cmp_kv : a.ori_kv, e[q] & ~kCmpBit,
-                              cmp ? a.cmp_stride : a.ori_stride);
+    const int j = c - r * P::CPR;                             // chunk within the row
+    const char* rowp;
+    if constexpr (VC) {
+      // chunks past the key row: the value tensor's row, chunk j - KC of its
+      // 512 code bytes (only original-KV rows: the host refuses a value
+      // tensor with a compressed KV)
+      const bool vc = j >= P::KC;
+      rowp = row_at(vc ? a.ori_v : a.ori_kv, e[q], vc ? a.ori_v_stride : a.ori_stride) +
+             16 * (vc ? j - P::KC : j);
+    } else {
+      const bool cmp = e[q] & kCmpBit;
+      rowp = row_at(cmp ? a.cmp_kv : a.ori_kv, e[q] & ~kCmpBit,
+                    cmp ? a.cmp_stride : a.ori_stride) + 16 * j;
+    }
     const bool zero = e[q] == kNoRow || c >= kTile * P::CPR;
-    dma16(zero ? (const char*)g_zero_row : rowp + 16 * (c - r * P::CPR), base + q * 1024);
+    dma16(zero ? (const char*)g_zero_row : rowp, base + q * 1024);
   }
 }
 
@@ -734,9 +748,9 @@ __device__ __forceinline__ float sum4(float x) {
 // Raw packed tile -> the bf16 K tile the MFMA path reads (codes decoded
 // exactly; rope copied into its swizzled region) and the tile's scales,
 // stored scale-tile major: sScale[32 * j + row] for columns [128 j, 128 j + 128).
-template <int NW, int DQK, int FMT>
+template <int NW, int DQK, int FMT, int VC = 0>
 __device__ __forceinline__ void decode_tile(const char* raw, char* kbf, float* sScale, int tid) {
-  using P = PackedPipe<NW, DQK>;
+  using P = PackedPipe<NW, DQK, VC>;
   constexpr int NTHR = NW * 64;
   constexpr int RB = P::CPR * 16;
   constexpr int RS = 1024 + 32;
@@ -774,6 +788,38 @@ __device__ __forceinline__ void decode_tile(const char* raw, char* kbf, float* s
     sScale[kTile + i] = sc.y;
     sScale[2 * kTile + i] = sc.z;
     sScale[3 * kTile + i] = sc.w;
+  }
+}
+
+// The value tensor's codes of a raw tile (stored after each key row in the
+// stage) -> the nope columns of the bf16 tile, where the key's codes were;
+// the rope columns and the row scales (the key row's) stay.
+template <int NW, int DQK, int FMT>
+__device__ __forceinline__ void decode_value(const char* raw, char* kbf, int tid) {
+  using P = PackedPipe<NW, DQK, 1>;
+  constexpr int NTHR = NW * 64;
+  constexpr int RB = P::CPR * 16;
+  constexpr int RS = 1024 + 32;
+  constexpr int NIT = kTile * 32 / NTHR;          // 16-code chunks per thread
+  constexpr int U = NIT < 4 ? NIT : 4;
+  static_assert(kTile * 32 % NTHR == 0 && NIT % U == 0, "decode split");
+  if constexpr (NW == 8) tid = fresh(tid);
+#pragma unroll
+  for (int i0 = 0; i0 < NIT; i0 += U) {
+    uint4 c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = tid + (i0 + u) * NTHR;
+      c[u] = *(const uint4*)(raw + (i >> 5) * RB + 16 * P::KC + 16 * (i & 31));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = tid + (i0 + u) * NTHR;
+      uint4 lo, hi;
+      codes_to_bf16<FMT>(c[u], lo, hi);
+      *(uint4*)(kbf + (i >> 5) * RS + 32 * (i & 31)) = lo;
+      *(uint4*)(kbf + (i >> 5) * RS + 32 * (i & 31) + 16) = hi;
+    }
   }
 }
 
@@ -824,10 +870,11 @@ constexpr bool kTwoPerCu = NW == 4 && (FMT == SFMLA_KV_BF16 || FMT == SFMLA_KV_F
 template <int NW, int HB, int DQK, int VMODE, int FMT, bool TILED = false, bool PAIR = false>
 __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   using C = Pipe<NW, DQK, VMODE>;
-  using PP = PackedPipe<NW, DQK>;
   constexpr bool HALF = FMT == SFMLA_KV_FP16;     // float16 q / kv / P / output
   constexpr bool PK = FMT != SFMLA_KV_BF16 && !HALF;   // packed rows (V = decoded nope)
-  static_assert(!PK || VMODE == 0, "packed KV has no separate V");
+  // packed KV with VMODE: the value codes come from their own tensor
+  constexpr bool PKV = PK && VMODE;
+  using PP = PackedPipe<NW, DQK, PKV ? 1 : 0>;
   static_assert(!TILED || (!PK && NW == 8 && HB == 1), "query tiles: 16-bit rows, 8 waves");
   static_assert(!PAIR || (!TILED && NW == 8 && HB == 1), "wave pairs: 8 waves");
   constexpr bool W4 = kTwoPerCu<NW, FMT>;
@@ -847,11 +894,11 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
   __shared__ __align__(16) char sK0[C::KBYTES];
   __shared__ __align__(16) char sK1[PK ? 16 : C::KBYTES];
   __shared__ __align__(16) char sK2[(VMODE || PK || W4) ? 16 : C::KBYTES];
-  __shared__ __align__(16) char sV0[VMODE ? T * RS : 16];
-  __shared__ __align__(16) char sV1[VMODE ? T * RS : 16];
+  __shared__ __align__(16) char sV0[(VMODE && !PK) ? T * RS : 16];
+  __shared__ __align__(16) char sV1[(VMODE && !PK) ? T * RS : 16];
   __shared__ __align__(16) char sW0[PK ? PP::RAWB : 16];
   __shared__ __align__(16) char sW1[PK ? PP::RAWB : 16];
-  __shared__ __align__(16) char sW2[PK ? PP::RAWB : 16];
+  __shared__ __align__(16) char sW2[(PK && !PKV) ? PP::RAWB : 16];
   __shared__ __align__(16) float sScale[PK ? 4 * T : 4];
   __shared__ uint32_t sRow[kMaxSplitRows + T];      // resolved positions of the split
   // bf16 / fp16 with a separate V: a merging wave stages its output in the
@@ -1367,7 +1414,47 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if constexpr (PK) {
+  if constexpr (PKV) {
+    // Packed rows with a value tensor: each raw stage holds a tile's key rows
+    // and its value codes (W0, W1: the next tile streams in while this one is
+    // used).  Per tile: the key codes are decoded into sK0 for the scores,
+    // then the value codes overwrite its nope columns for the values (the
+    // key row's scales apply to both), and only then is the stage refilled
+    // with the tile two ahead.  Every wave takes the same four barriers per
+    // tile (the wave pairs' score exchange adds one inside the scores).
+    auto step = [&](int tt, char* sWc) {
+      if (tt + 1 < nt) wait_vmcnt<PP::PER>(); else wait_vmcnt<0>();   // raw(tt) landed
+      wait_lgkm0();
+      block_barrier();                          // ... and the values of tile tt-1 are consumed
+      decode_tile<NW, DQK, FMT, 1>(sWc, sK0, sScale, tid);
+      wait_lgkm0();
+      block_barrier();                          // K(tt) decoded
+      if constexpr (PAIR) {
+        qk_softmax(sK0, tt * T);                // (a barrier inside)
+      } else if (wave_on) {
+        qk_softmax(sK0, tt * T);
+      }
+      wait_lgkm0();
+      block_barrier();                          // every wave is done with K(tt)
+      decode_value<NW, DQK, FMT>(sWc, sK0, tid);
+      wait_lgkm0();
+      block_barrier();                          // V(tt) decoded; stage sWc is free
+      if (tt + 2 < nt) issue_raw<NW, DQK, 1>(a, sRow, (tt + 2) * T, lds_addr(sWc), w, l);
+      if (wave_on) pv(sK0);
+    };
+    if (nt > 0) issue_raw<NW, DQK, 1>(a, sRow, 0, lds_addr(sW0), w, l);
+    wait_vmcnt<0>();                            // raw(0) and the Q slices
+    settle(qreg);
+    if constexpr (NQR < NKS) {                  // the rope slices to this wave's LDS rows
+#pragma unroll
+      for (int i = 0; i < NKS - NQR; ++i) sQr[w][i][l] = qrt[i];
+    }
+    if (nt > 1) issue_raw<NW, DQK, 1>(a, sRow, T, lds_addr(sW1), w, l);
+    for (int tt = 0; tt < nt; tt += 2) {
+      step(tt, sW0);
+      if (tt + 1 < nt) step(tt + 1, sW1);
+    }
+  } else if constexpr (PK) {
     // raw stages W0..W2 (two tiles in flight); the decoded tile lives in sK0
     auto step = [&](int tt, char* sWc, char* sWn2) {
       if (tt + 1 < nt) wait_vmcnt<PP::PER>(); else wait_vmcnt<0>();   // raw(tt) landed
@@ -2048,9 +2135,12 @@ static hipError_t launch_pair_t(const FwdArgs& a, int groups, hipStream_t s, hip
 // Packed rows: eight waves per workgroup (two per SIMD; the gather and the
 // decode of a tile spread over all of them)
 template <int FMT>
-static hipError_t launch_packed(const FwdArgs& a, int nw, int dqk, int groups, int mw,
+static hipError_t launch_packed(const FwdArgs& a, int nw, int dqk, int vmode, int groups, int mw,
                                 hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if (nw != 8) return hipErrorInvalidConfiguration;
+  if (vmode)   // value codes from their own tensor
+    return dqk == 512 ? launch_fwd_t<8, 512, 1, FMT>(a, groups, mw, s, t0, t1)
+                      : launch_fwd_t<8, 576, 1, FMT>(a, groups, mw, s, t0, t1);
   return dqk == 512 ? launch_fwd_t<8, 512, 0, FMT>(a, groups, mw, s, t0, t1)
                     : launch_fwd_t<8, 576, 0, FMT>(a, groups, mw, s, t0, t1);
 }
@@ -2071,19 +2161,27 @@ hipError_t launch_forward(const FwdArgs& a, int nw, bool pair, int dqk, int vmod
       return vmode ? launch_pair_t<576, 1, SFMLA_KV_FP16>(a, groups, s, t0, t1)
                    : launch_pair_t<576, 0, SFMLA_KV_FP16>(a, groups, s, t0, t1);
     }
-    if (fmt == SFMLA_KV_INT8_PACKED)
+    if (fmt == SFMLA_KV_INT8_PACKED) {
+      if (vmode)
+        return dqk == 512 ? launch_pair_t<512, 1, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1)
+                          : launch_pair_t<576, 1, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1);
       return dqk == 512 ? launch_pair_t<512, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1)
                         : launch_pair_t<576, 0, SFMLA_KV_INT8_PACKED>(a, groups, s, t0, t1);
-    if (fmt == SFMLA_KV_FP8_E4M3_PACKED)
+    }
+    if (fmt == SFMLA_KV_FP8_E4M3_PACKED) {
+      if (vmode)
+        return dqk == 512 ? launch_pair_t<512, 1, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1)
+                          : launch_pair_t<576, 1, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1);
       return dqk == 512 ? launch_pair_t<512, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1)
                         : launch_pair_t<576, 0, SFMLA_KV_FP8_E4M3_PACKED>(a, groups, s, t0, t1);
+    }
     return hipErrorInvalidConfiguration;
   }
   switch (fmt) {
     case SFMLA_KV_INT8_PACKED:
-      return launch_packed<SFMLA_KV_INT8_PACKED>(a, nw, dqk, groups, mw, s, t0, t1);
+      return launch_packed<SFMLA_KV_INT8_PACKED>(a, nw, dqk, vmode, groups, mw, s, t0, t1);
     case SFMLA_KV_FP8_E4M3_PACKED:
-      return launch_packed<SFMLA_KV_FP8_E4M3_PACKED>(a, nw, dqk, groups, mw, s, t0, t1);
+      return launch_packed<SFMLA_KV_FP8_E4M3_PACKED>(a, nw, dqk, vmode, groups, mw, s, t0, t1);
     case SFMLA_KV_FP16:
       if (nw == 4)   // d_qk 512, V = K nope: two workgroups per CU
         return dqk == 512 && !vmode ? launch_fwd_t<4, 512, 0, SFMLA_KV_FP16>(a, groups, mw, s, t0, t1)

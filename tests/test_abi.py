@@ -100,6 +100,22 @@ def test_invalid_params_rejected_on_host(field, value, msg):
     assert e.value.status == 1 and msg in str(e.value)
 
 
+def test_packed_value_tensor_needs_the_token_wise_form():
+    """A value tensor with packed KV (KV quant blog, 参数说明 value) is taken for
+    the token-wise TopK form; with a compressed KV it is refused on the host,
+    without it the parameters are valid."""
+    P = synth.random_tiny(3, family="sfa", kv_dtype="int8_packed", rope_head_dim=64,
+                          separate_v=True)
+    p = s.make_params(P.params, P.arrays)
+    assert p.has_separate_v == 1
+    s.sfmla_metadata_size(p)
+    Q = synth.random_tiny(4, family="csa", kv_dtype="int8_packed", rope_head_dim=64)
+    q = s.make_params(Q.params, Q.arrays)
+    q.has_separate_v = 1
+    with pytest.raises(s.SfmlaError, match="token-wise TopK"):
+        s.sfmla_metadata_size(q)
+
+
 def test_paged_needs_block_table_and_seqused():
     P = synth.make_workload("csa_decode_paged")
     p = s.make_params(P.params, P.arrays)

@@ -853,3 +853,69 @@ def test_four_wave_kernel_matches_eight_waves_bitwise(kw):
     res = dict(O=outs[0][0].float().cpu().numpy(), status=0,
                lse=None if outs[0][1] is None else outs[0][1].cpu().numpy())
     check_outputs(P, res, oracle.forward(P, rows=rows), rows)
+
+
+# ---------------------------------------------------------------------------
+# packed KV with a value tensor of codes (KV quant blog, 参数说明 value: a
+# 512-wide NoPE value tensor in the key's format; its tiles take the key
+# row's scales)
+# ---------------------------------------------------------------------------
+
+PKV_CASES = [
+    dict(seed=1100, kv_dtype="int8_packed", rope_head_dim=64, num_heads_q=16),
+    dict(seed=1101, kv_dtype="fp8_e4m3_packed", rope_head_dim=0, num_heads_q=1),
+    dict(seed=1102, kv_dtype="int8_packed", rope_head_dim=0, num_heads_q=20, duplicates=True),
+    dict(seed=1103, kv_dtype="fp8_e4m3_packed", rope_head_dim=64, num_heads_q=128),
+    # long lists: several splits and a ragged last tile
+    dict(seed=1104, kv_dtype="int8_packed", rope_head_dim=64, num_heads_q=128, max_kv=2100,
+         topk=2048, sinks=True, lse=True),
+    dict(seed=1105, kv_dtype="fp8_e4m3_packed", rope_head_dim=0, num_heads_q=64, max_kv=1700,
+         topk=1030, layout_q="TND", layout_kv="PA_BSND", block_size=64),
+]
+
+
+def _both_kernels(P):
+    """Outputs of the eight-wave kernel (wave pairs off) and of wave pairs."""
+    import sparse_shared_kv_amd as s
+    outs = []
+    for wp in (1, 2):
+        call = s.Call(dict(P.params, wave_pairs=wp), P.arrays)
+        outs.append([None if t is None else t.clone() for t in call.run()])
+        torch.cuda.synchronize()
+        assert int(call.status.item()) == 0
+    return outs
+
+
+@pytest.mark.parametrize("kw", PKV_CASES, ids=lambda k: str(k["seed"]))
+def test_packed_value_tensor_parity(kw):
+    """Both packed kernels with a value tensor against the oracle on every
+    row, and the same bits from either."""
+    P = synth.random_tiny(family="sfa", separate_v=True, **kw)
+    say("packed value tensor seed", kw["seed"])
+    outs = _both_kernels(P)
+    assert torch.equal(outs[0][0], outs[1][0])
+    if outs[0][1] is not None:
+        assert torch.equal(outs[0][1], outs[1][1])
+    rows = list(range(P.query_rows))
+    ref = oracle.forward(P, rows=rows)
+    for o in outs:
+        res = dict(O=o[0].float().cpu().numpy(), status=0,
+                   lse=None if o[1] is None else o[1].cpu().numpy())
+        check_outputs(P, res, ref, rows)
+
+
+@pytest.mark.parametrize("fmt,rope", [("int8_packed", 64), ("fp8_e4m3_packed", 0)])
+def test_packed_value_tensor_of_the_key_codes_equals_aliased_bitwise(fmt, rope):
+    """A value tensor holding the key rows' own codes gives the bits of V
+    taken from the packed key rows, on both kernels."""
+    P = synth.random_tiny(1110 + rope, family="sfa", kv_dtype=fmt, rope_head_dim=rope,
+                          num_heads_q=128, max_kv=1200, topk=1000, separate_v=False)
+    V = P.copy()
+    V.params["separate_v"] = True
+    V.arrays["ori_v"] = np.ascontiguousarray(P.arrays["ori_kv"][:, :512])
+    say("packed value tensor = key codes", fmt, rope)
+    a, b = _both_kernels(P), _both_kernels(V)
+    for x, y in zip(a, b):
+        assert torch.equal(x[0], y[0])
+        if x[1] is not None:
+            assert torch.equal(x[1], y[1])

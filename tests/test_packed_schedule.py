@@ -124,6 +124,41 @@ def lockstep(nt, n_waves=8, raw_stages=3):
     return ev
 
 
+def lockstep_value(nt, n_waves=8, raw_stages=2):
+    """The packed kernels with a value tensor: two raw stages, each holding a
+    tile's key rows and value codes, one decoded buffer:
+
+      prologue : all issue raw(0) -> R0 and wait, issue raw(1) -> R1
+      step(t)  : every wave waits for its own raw(t); barrier; decode the key
+                 codes of raw(t) (a share) into D0; barrier; scores of tile t
+                 (K from D0); barrier; decode the value codes of raw(t) into
+                 D0's nope columns; barrier; issue raw(t+2) -> R[t%2];
+                 values of tile t (V from D0)
+    """
+    ev = {w: [] for w in range(n_waves)}
+    for w in range(n_waves):
+        e = ev[w]
+        if nt > 0:
+            e.append(("issue", 0, 0))
+        e.append(("wait", 0))
+        if nt > 1:
+            e.append(("issue", 1, 1 % raw_stages))
+        for t in range(nt):
+            r = t % raw_stages
+            e.append(("wait", t))
+            e.append(("barrier",))
+            e.append(("decode_share", t, r, 0))
+            e.append(("barrier",))
+            e.append(("k", t, 0))
+            e.append(("barrier",))
+            e.append(("decode_value_share", t, r, 0))
+            e.append(("barrier",))
+            if t + 2 < nt:
+                e.append(("issue", t + 2, r))
+            e.append(("v", t, 0))
+    return ev
+
+
 # ---------------------------------------------------------------------------
 # the checker
 # ---------------------------------------------------------------------------
@@ -205,6 +240,28 @@ def check(ev, nt, head_waves):
             if kr == k and xr[2] == x[3]:
                 raise ScheduleError("interval %d: buffer %d decoded into while wave %d reads it"
                                     % (k, x[3], wr))
+    # value decodes (value codes over the nope columns of the key tile): after
+    # every wave's scores of that tile, before any wave's values of it, and
+    # reading a raw stage that still holds the tile (not refilled yet)
+    vdec = [(k, w, x) for k, w, x in placed if x[0] == "decode_value_share"]
+    for t in sorted(set(x[1] for k, w, x in vdec)):
+        ks = [k for k, w, x in vdec if x[1] == t]
+        if len(set(ks)) != 1:
+            raise ScheduleError("value codes of tile %d decoded in several intervals" % t)
+        kv = ks[0]
+        for kr, wr, xr in reads:
+            if xr[1] == t and xr[0] == "k" and kr >= kv:
+                raise ScheduleError("wave %d reads K of tile %d after its values replaced it" % (wr, t))
+            if xr[1] == t and xr[0] == "v" and kr <= kv:
+                raise ScheduleError("wave %d reads V of tile %d before it is decoded" % (wr, t))
+        r = [x[2] for k, w, x in vdec if x[1] == t][0]
+        k_iss = min(k for k, w, x in issues if x[1] == t)
+        for kk, w2, xx in issues:
+            if xx[2] == r and xx[1] != t and k_iss <= kk <= kv:
+                raise ScheduleError("stage %d refilled with tile %d before tile %d's value codes "
+                                    "are decoded" % (r, xx[1], t))
+    if vdec and sorted(set(x[1] for k, w, x in vdec)) != list(range(nt)):
+        raise ScheduleError("value codes decoded for tiles %s" % sorted(set(x[1] for k, w, x in vdec)))
     # every head wave: k(0) v(0) k(1) v(1) ... in order
     for w in head_waves:
         seq = [(x[0], x[1]) for x in ev[w] if x[0] in ("k", "v")]
@@ -235,6 +292,33 @@ def test_staggered_schedule_is_sound(nt, head_waves):
 @pytest.mark.parametrize("nt", TILES)
 def test_lockstep_schedule_is_sound(nt):
     check(lockstep(nt), nt, range(8))
+
+
+@pytest.mark.parametrize("nt", TILES)
+@pytest.mark.parametrize("head_waves", [8, 2, 0])
+def test_value_tensor_schedule_is_sound(nt, head_waves):
+    ev = lockstep_value(nt)
+    for w in range(head_waves, 8):
+        ev[w] = [x for x in ev[w] if x[0] not in ("k", "v")]
+    check(ev, nt, range(head_waves))
+
+
+def test_value_tensor_schedule_mistakes_are_caught():
+    """Refilling the stage before the value codes are decoded (issuing the
+    tile two ahead right after the key decode), or one raw stage, must fail."""
+    for nt in (3, 4):
+        ev = lockstep_value(nt)
+        for w in ev:                               # move each issue before the value decode
+            e = ev[w]
+            for i, x in enumerate(list(e)):
+                if x[0] == "issue" and x[1] >= 2:
+                    e.remove(x)
+                    j = max(k for k, y in enumerate(e[:i]) if y[0] == "decode_share")
+                    e.insert(j + 1, x)
+        with pytest.raises(ScheduleError):
+            check(ev, nt, range(8))
+        with pytest.raises(ScheduleError):
+            check(lockstep_value(nt, raw_stages=1), nt, range(8))
 
 
 @pytest.mark.parametrize("plant", ["gather_past_end", "missing_barrier", "decode_into_live_buffer"])
