@@ -47,6 +47,9 @@ DESCR = {
                   "(ratio 128), contexts 16K-131K, sinks",
     "c8_packed_int8_rope0": "INT8 packed KV without rope (528-B rows), TND B=8, q_n=128, "
                             "d_qk=512, TopK 2048 of 16K-131K tokens",
+    "c8_packed_int8_value": "INT8 packed KV (656-B rows) with a value tensor of 512 INT8 codes per "
+                            "row (scaled by the key rows' tiles), TND B=8, q_n=128, d_qk=576, "
+                            "TopK 2048 of 16K-131K tokens",
     "hca_prefill": "HCA prefill (the SparseAttnSharedkv call example's shapes with all "
                    "visible compressed rows): B=4 x 128 query tokens, q_n=64, window 128 + "
                    "<=1024 compressed rows (ratio 4), 4096 cached tokens, PA block 128, sinks",
@@ -84,7 +87,7 @@ def row_bytes(P) -> tuple:
     if p["kv_dtype"] in ("bf16", "fp16"):
         b = 2 * d_qk + (1024 if p.get("separate_v") else 0)
     else:
-        b = 512 + 2 * int(p["rope_head_dim"]) + 16
+        b = 512 + 2 * int(p["rope_head_dim"]) + 16 + (512 if p.get("separate_v") else 0)
     return b, 2 * (d_qk + 512)
 
 
@@ -484,6 +487,7 @@ SUB_CONFIGS = {
     "hca_varlen": "c3 HCA varlen decode",
     "c8_packed_int8": "c5 packed INT8 KV",
     "c8_packed_fp8": "c5 packed FP8-E4M3 KV",
+    "c8_packed_int8_value": "c5 packed INT8 KV with a value tensor of codes",
     "c8_packed_int8_q32": "c5 shapes, 32 query tokens per sequence (throughput mode)",
     "hca_varlen_q32": "c3 shapes, 32 query tokens per sequence (throughput mode)",
     "csa_prefill": "prefill: the SparseAttnSharedkv call example's shapes",

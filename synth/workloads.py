@@ -298,15 +298,17 @@ def _c8_indices(seq, L, topk, qps=1):
     return idx.reshape(len(L) * qps, 1, topk)
 
 
-def c8_packed(seed=5, fmt="int8", topk=2048, qps=1, rope=64):
+def c8_packed(seed=5, fmt="int8", topk=2048, qps=1, rope=64, value=False):
     """Quantised packed KV: the HCA-varlen shapes (TND, B=8, q_n=128, the same
     context lengths) with Q_D=576 and 656-byte packed rows (512 INT8 or
     FP8-E4M3 codes, 64 bf16 rope values, 4 fp32 per-128-tile scales), V =
     dequantised nope; TopK 2048 over each sequence's positions.  qps > 1:
     qps query tokens per sequence (the last qps positions, each with its own
     causal TopK list), a throughput-mode variant of the decode.  rope 0: the
-    528-byte rope-free rows (Q_D = 512)."""
-    s_q, s_kv, s_idx = _seqs(seed, 3)
+    528-byte rope-free rows (Q_D = 512).  value: V from a value tensor of 512
+    codes per row (an independent quantised draw in the same format), scaled
+    by the key rows' tiles."""
+    s_q, s_kv, s_idx, s_v = _seqs(seed, 4)
     B, qn, dq = 8, 128, 512 + rope
     L = _varlen_lengths(3)
     idx = _c8_indices(s_idx, L, topk, qps)
@@ -317,14 +319,18 @@ def c8_packed(seed=5, fmt="int8", topk=2048, qps=1, rope=64):
         cu_seqlens_ori_kv=_prefix(L),
         ori_sparse_indices=idx,
     )
+    if value:
+        arrays["ori_v"] = banked_rows(
+            s_v, int(L.sum()), lambda s, n: np.ascontiguousarray(packed_rows(s, n, 0, fmt)[:, :512]))
     params = _base_params(
         num_heads_q=qn, rope_head_dim=rope, batch_size=B, layout_q="TND",
         layout_kv="TND", q_t=B * qps, max_seqlen_q=qps,
         max_seqlen_ori_kv=int(L.max()), ori_topk=topk, ori_mask_mode=3,
-        has_cmp_kv=False,
+        has_cmp_kv=False, separate_v=value,
         kv_dtype="int8_packed" if fmt == "int8" else "fp8_e4m3_packed",
         softmax_scale=1.0 / math.sqrt(dq))
-    name = "c8_packed_" + fmt + ("" if rope else "_rope0") + ("" if qps == 1 else "_q%d" % qps)
+    name = ("c8_packed_" + fmt + ("" if rope else "_rope0") + ("_value" if value else "") +
+            ("" if qps == 1 else "_q%d" % qps))
     return Problem(name, seed, params, arrays,
                    "packed %s rows, contexts %s" % (fmt, L.tolist()))
 
@@ -340,6 +346,7 @@ WORKLOADS = {
     "c8_packed_int8": lambda seed=5: c8_packed(seed, "int8"),
     "c8_packed_fp8": lambda seed=5: c8_packed(seed, "fp8"),
     "c8_packed_int8_rope0": lambda seed=5: c8_packed(seed, "int8", rope=0),
+    "c8_packed_int8_value": lambda seed=5: c8_packed(seed, "int8", value=True),
     "hca_prefill": lambda seed=7: rule_prefill(seed, "hca"),
     "swa_prefill": lambda seed=8: rule_prefill(seed, "swa"),
     "swa_prefill_h16": lambda seed=9: rule_prefill(seed, "swa", qn=16),

@@ -32,7 +32,7 @@ def _gpu():
 FULL = ["swa_decode", "csa_decode_paged", "hca_varlen", "sfa_mla_rope", "c8_packed_int8",
         "c8_packed_fp8", "csa_prefill", "sfa_mla_rope_fp16", "sfa_mla_rope_block16",
         "c8_packed_int8_q32", "hca_varlen_q32", "hca_prefill", "swa_prefill", "swa_prefill_h16",
-        "c8_packed_int8_rope0"]
+        "c8_packed_int8_rope0", "c8_packed_int8_value"]
 
 
 @pytest.mark.parametrize("name", FULL)
