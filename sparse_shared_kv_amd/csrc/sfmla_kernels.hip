@@ -1234,7 +1234,11 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
         bf16x8 kb[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i) kb[i] = kload(i);
-        f32x4 sp[HB], scq;
+        // The partial product of scale tile j lives in sp[j & 1]; it is scaled
+        // into acc one k-step after its last MFMA (after the first MFMA of
+        // tile j + 1 is issued), so that the VALU does not wait on the MFMA
+        // that just wrote it.  The additions into acc keep their order.
+        f32x4 sp[2][HB], scq;
         bf16x8 qlds[NQR < NKS ? NKS - NQR : 1];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -1243,20 +1247,26 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
             if (ks + 2 >= NQR && ks + 2 < NKS) qlds[ks + 2 - NQR] = sQr[w][ks + 2 - NQR][l];
           }
           const bf16x8 kv = kb[ks % PF];
-          if (ks < 16 && ks % 4 == 0)   // this lane's rows' scales of the tile
-            scq = *(const f32x4*)(sScale + (ks / 4) * T + 16 * half + 4 * g);
+          const int jt = ks / 4;                       // scale tile of this k-step
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
             if (ks < 16) {
               const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-              sp[hb] = mfma16<HALF>(kv, qreg[hb][ks < NQR ? ks : 0], ks % 4 ? sp[hb] : z);
-              if (ks % 4 == 3) acc(hb) += sp[hb] * scq;
+              sp[jt & 1][hb] = mfma16<HALF>(kv, qreg[hb][ks < NQR ? ks : 0], ks % 4 ? sp[jt & 1][hb] : z);
+              if (ks % 4 == 0 && ks > 0) acc(hb) += sp[(jt - 1) & 1][hb] * scq;   // tile jt - 1
             } else {
+              if (ks == 16) acc(hb) += sp[1][hb] * scq;                              // tile 3
               const bf16x8 qv = ks < NQR ? qreg[hb][ks < NQR ? ks : 0] : qlds[ks >= NQR ? ks - NQR : 0];
               acc(hb) = mfma16<HALF>(kv, qv, acc(hb));
             }
           }
+          if (ks < 16 && ks % 4 == 0)   // this lane's rows' scales of tile jt (read after tile jt - 1 used them)
+            scq = *(const f32x4*)(sScale + jt * T + 16 * half + 4 * g);
           if (ks + PF < NKS) kb[ks % PF] = kload(ks + PF);
+        }
+        if constexpr (NKS == 16) {      // no rope k-steps: tile 3 is scaled here
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) acc(hb) += sp[1][hb] * scq;
         }
       };
       if constexpr (PAIR) {
