@@ -327,10 +327,11 @@ def test_rope_free_rows_equal_zero_rope_rows_bitwise(fmt):
 
 GRAPH_CASES = [dict(),                                        # bf16, separate V (staged merge)
                dict(kv_dtype="int8_packed", rope_head_dim=64),
-               dict(separate_v=False, rope_head_dim=0)]         # V = K nope
+               dict(separate_v=False, rope_head_dim=0),         # V = K nope
+               dict(kv_dtype="fp8_e4m3_packed", rope_head_dim=64, separate_v=True)]  # value codes
 
 
-@pytest.mark.parametrize("kw", GRAPH_CASES, ids=["separate_v", "packed", "shared_v"])
+@pytest.mark.parametrize("kw", GRAPH_CASES, ids=["separate_v", "packed", "shared_v", "packed_value"])
 def test_graph_replay_matches_eager(kw):
     """plan + forward captured in one HIP graph: every replay, with other
     eager work and synchronisations in between, reproduces the eager result
