@@ -52,7 +52,7 @@ def test_recipe_rows_match_the_oracle(name, make):
 
 
 @pytest.mark.parametrize("name", ["hca_varlen", "c8_packed_int8", "c8_packed_int8_q32",
-                                  "hca_varlen_q32"])
+                                  "hca_varlen_q32", "c8_packed_int8_value"])
 def test_recipe_rows_match_the_oracle_full_size(name):
     P = synth.make_workload(name)
     got = bench.recipe_rows(P)
@@ -60,3 +60,10 @@ def test_recipe_rows_match_the_oracle_full_size(name):
     ref = _oracle_counts(P, rows)
     assert all(got[r] == n for r, n in ref.items()), name
     assert (got > 0).all()
+
+
+def test_row_bytes_of_the_packed_value_workload():
+    """A packed row with a value tensor moves its 656 key bytes and 512 value
+    code bytes (the gathered bytes the roofline counts)."""
+    P = synth.make_workload("c8_packed_int8_value")
+    assert bench.row_bytes(P) == (656 + 512, 2 * (576 + 512))
