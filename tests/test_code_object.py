@@ -146,14 +146,16 @@ def test_every_forward_variant_is_built(kernels):
         # four waves, two workgroups per CU: d_qk 512 with V = K nope only
         assert (4, 512, 0, fmt, 0, 0) in fwd
         assert (4, 576, 0, fmt, 0, 0) not in fwd and (4, 512, 1, fmt, 0, 0) not in fwd
-    # packed INT8 / FP8 rows, with and without rope, on eight waves, with and
-    # without wave pairs (never tiled)
+    # packed INT8 / FP8 rows, with and without rope, V the key codes or a
+    # value tensor of codes, on eight waves, with and without wave pairs
+    # (never tiled)
     for fmt in (1, 2):
         for dqk in (512, 576):
-            assert (8, dqk, 0, fmt, 0, 0) in fwd
-            assert (8, dqk, 0, fmt, 0, 1) in fwd
-            assert (4, dqk, 0, fmt, 0, 0) not in fwd
-            assert (8, dqk, 0, fmt, 1, 0) not in fwd
+            for vmode in (0, 1):
+                assert (8, dqk, vmode, fmt, 0, 0) in fwd
+                assert (8, dqk, vmode, fmt, 0, 1) in fwd
+                assert (4, dqk, vmode, fmt, 0, 0) not in fwd
+                assert (8, dqk, vmode, fmt, 1, 0) not in fwd
     assert any("plan_kernel" in k for k in kernels)
     assert any("combine_kernel" in k for k in kernels)
 
