@@ -830,6 +830,10 @@ __device__ __forceinline__ void decode_value(const char* raw, char* kbf, int tid
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kMergeSplits = 4;       // splits whose partials one merge round loads (8 waves)
 constexpr int kMaxOwnerSplits = 8;    // splits of a row whose partials an owning wave merges
+template <int N>
+struct IntC {                         // a compile-time int passed as an argument
+  static constexpr int value = N;
+};
 
 // Position of slot u of a resolve batch starting at i0 (PPT slots per thread).
 // bf16 rows: wave w resolves exactly the rows it gathers (row w*NR + l%NR of
@@ -1681,13 +1685,18 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
   };
   // the last-arriver merge of this wave's heads (every split's partial from
   // memory, this split's own included)
-  auto merge_last = [&]() __attribute__((always_inline)) {
+  auto merge_last = [&](auto ms_c, auto jb_c, auto one_c) __attribute__((always_inline)) {
     // merge from the stored partials (this split's own included).  Round r
     // loads column blocks [JB*(r / ns4), +JB) of MS splits (MS*JB loads of 16
-    // bytes per lane in flight: 16, or 32 where one wave per SIMD leaves the
-    // registers); the first round travels together with the loads of the
-    // LSEs, which give the max and the normaliser in one pass.
-    constexpr int MS = (NW <= 4 && !W4) ? 2 * kMergeSplits : kMergeSplits, JB = 4, NJ = NFR / JB;
+    // bytes per lane in flight: 16, or 32 where one wave per SIMD or a wave
+    // pair's half-width partials leave the registers); the first round
+    // travels together with the loads of the LSEs, which give the max and
+    // the normaliser in one pass.  MS only groups the loads: the splits are
+    // added in the same order whatever its value.  ONE: MS >= nsplit, so a
+    // round holds every split of its columns and each column block is
+    // finished (and its accumulators free) before the next.
+    constexpr int MS = decltype(ms_c)::value, JB = decltype(jb_c)::value, NJ = NFR / JB;
+    constexpr bool ONE = decltype(one_c)::value;
     const int ns4 = (nsplit + MS - 1) / MS;               // split chunks per column round
     const int R = NJ * ns4;                               // load rounds
     const int split_bytes = a.groups * NW * WAVE_BYTES;
@@ -1751,7 +1760,23 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
       const float inv = tot > 0.f ? 1.f / den : 0.f;
       const bool on = h < a.qn;
       uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g + 256 * hf;
-      float acc[JB][8];
+      // column block jj of this head from the merged accumulators c
+      auto put = [&](int jj, const float* c) __attribute__((always_inline)) {
+        uint2 p0, p1;
+        p0.x = (uint32_t)to16<HALF>(c[0] * inv) | ((uint32_t)to16<HALF>(c[1] * inv) << 16);
+        p0.y = (uint32_t)to16<HALF>(c[2] * inv) | ((uint32_t)to16<HALF>(c[3] * inv) << 16);
+        p1.x = (uint32_t)to16<HALF>(c[4] * inv) | ((uint32_t)to16<HALF>(c[5] * inv) << 16);
+        p1.y = (uint32_t)to16<HALF>(c[6] * inv) | ((uint32_t)to16<HALF>(c[7] * inv) << 16);
+        if (stage) {
+          char* sp = stg + (16 * hb + t) * kStgRow + 2 * (32 * jj + 4 * g);
+          *(uint2*)sp = p0;
+          *(uint2*)(sp + 32) = p1;
+        } else {
+          *(uint2*)(op + 16 * (2 * jj)) = p0;
+          *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
+        }
+      };
+      float acc[JB][8];                                    // (unused where ONE)
 #pragma unroll
       for (int j = 0; j < JB; ++j)
 #pragma unroll
@@ -1760,6 +1785,26 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
       for (int r = 0; r < R; ++r) {
         if (r > 0) issue(r);
         const int jr = r / ns4, s0 = (r - jr * ns4) * MS;
+        if constexpr (ONE) {
+          float ws[MS];
+#pragma unroll
+          for (int q = 0; q < MS; ++q) ws[q] = q < nsplit ? __builtin_amdgcn_exp2f(wl[q] - Mu) : 0.f;
+#pragma unroll
+          for (int j = 0; j < JB; ++j) {
+            float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < MS; ++q) {
+              const uint32_t u[4] = {v[q][j].x, v[q][j].y, v[q][j].z, v[q][j].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                c[2 * e] = __builtin_fmaf(ws[q], lo16<HALF>(u[e]), c[2 * e]);
+                c[2 * e + 1] = __builtin_fmaf(ws[q], hi16<HALF>(u[e]), c[2 * e + 1]);
+              }
+            }
+            if (stage || on) put(jr * JB + j, c);
+          }
+          continue;
+        }
 #pragma unroll
         for (int q = 0; q < MS; ++q) {
           const float ws = s0 + q < nsplit ? __builtin_amdgcn_exp2f(wl[q] - Mu) : 0.f;
@@ -1776,22 +1821,7 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
         if (s0 + MS < nsplit) continue;                    // more splits for these columns
         if (stage || on) {
 #pragma unroll
-          for (int j = 0; j < JB; ++j) {
-            const int jj = jr * JB + j;
-            uint2 p0, p1;
-            p0.x = (uint32_t)to16<HALF>(acc[j][0] * inv) | ((uint32_t)to16<HALF>(acc[j][1] * inv) << 16);
-            p0.y = (uint32_t)to16<HALF>(acc[j][2] * inv) | ((uint32_t)to16<HALF>(acc[j][3] * inv) << 16);
-            p1.x = (uint32_t)to16<HALF>(acc[j][4] * inv) | ((uint32_t)to16<HALF>(acc[j][5] * inv) << 16);
-            p1.y = (uint32_t)to16<HALF>(acc[j][6] * inv) | ((uint32_t)to16<HALF>(acc[j][7] * inv) << 16);
-            if (stage) {
-              char* sp = stg + (16 * hb + t) * kStgRow + 2 * (32 * jj + 4 * g);
-              *(uint2*)sp = p0;
-              *(uint2*)(sp + 32) = p1;
-            } else {
-              *(uint2*)(op + 16 * (2 * jj)) = p0;
-              *(uint2*)(op + 16 * (2 * jj + 1)) = p1;
-            }
-          }
+          for (int j = 0; j < JB; ++j) put(jr * JB + j, acc[j]);
         }
 #pragma unroll
         for (int j = 0; j < JB; ++j)
@@ -1930,7 +1960,21 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
     if (__builtin_amdgcn_readfirstlane(last)) {
       if (l == 0)                                   // ready for the next call
         __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      merge_last();
+      // splits per round: two where the row has at most two (every column
+      // block in one or two rounds, no spare slot), else four, or eight for
+      // the half-width partials of wave pairs (32 loads per lane: more
+      // registers are free than where a wave holds all 512 columns).  Spare
+      // slots load the last split again and weigh it zero.
+      if constexpr (PAIR) {
+        if (nsplit <= 2) merge_last(IntC<2>{}, IntC<8>{}, IntC<1>{});
+        else if (nsplit <= 4) merge_last(IntC<4>{}, IntC<4>{}, IntC<0>{});
+        else merge_last(IntC<8>{}, IntC<4>{}, IntC<0>{});
+      } else if constexpr (NW <= 4 && !W4) {
+        merge_last(IntC<8>{}, IntC<4>{}, IntC<0>{});
+      } else {
+        if (nsplit <= 2) merge_last(IntC<2>{}, IntC<8>{}, IntC<1>{});
+        else merge_last(IntC<4>{}, IntC<4>{}, IntC<0>{});
+      }
     }
   }
 

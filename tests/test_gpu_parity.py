@@ -452,7 +452,9 @@ def _relayout(P, split_rope, pad):
         else:
             arrays[side + "_kv"] = _strided(a, a.shape[1], pk if pad else 0, dev, nan16)
     if P.arrays.get("ori_v") is not None:
-        arrays["ori_v"] = _strided(P.arrays["ori_v"], 512, 512 if pad else 0, dev, nan16)
+        # 16-bit values, or the value codes of packed rows (512 bytes)
+        arrays["ori_v"] = _strided(P.arrays["ori_v"], 512, 512 if pad else 0, dev,
+                                   junk8 if packed else nan16)
     return arrays
 
 
@@ -478,6 +480,12 @@ LAYOUT_CASES = [
          num_heads_q=128, max_kv=900, topk=600),
     dict(seed=915, family="sfa", kv_dtype="fp8_e4m3_packed", rope_head_dim=0, pad=16,
          num_heads_q=16),
+    # packed rows with a value tensor of codes, both strides padded (0xFF in
+    # the padding: a NaN code in E4M3, -1 in INT8)
+    dict(seed=916, family="sfa", kv_dtype="int8_packed", rope_head_dim=64, separate_v=True,
+         pad=8, num_heads_q=64, max_kv=900, topk=600),
+    dict(seed=917, family="sfa", kv_dtype="fp8_e4m3_packed", rope_head_dim=0, separate_v=True,
+         pad=16, num_heads_q=128, max_kv=1300, topk=1100),
 ]
 
 
