@@ -1971,6 +1971,10 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
         else merge_last(IntC<8>{}, IntC<4>{}, IntC<0>{});
       } else if constexpr (NW <= 4 && !W4) {
         merge_last(IntC<8>{}, IntC<4>{}, IntC<0>{});
+      } else if constexpr (W4) {
+        // (prefill rows, one split: the kernel stays as small as it was,
+        // measured faster)
+        merge_last(IntC<4>{}, IntC<4>{}, IntC<0>{});
       } else {
         if (nsplit <= 2) merge_last(IntC<2>{}, IntC<8>{}, IntC<1>{});
         else merge_last(IntC<4>{}, IntC<4>{}, IntC<0>{});
