@@ -785,6 +785,37 @@ def test_wave_pairs_match_single_waves_bitwise(kw):
     check_outputs(P, res, oracle.forward(P, rows=rows), rows)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "int8_packed"])
+def test_merge_rounds_for_every_split_count_bitwise(fmt):
+    """A 1024-position TopK list cut into 1 to 16 splits: the merge by the
+    last split to arrive loads its partials in rounds whose shape follows the
+    split count (and differs between one wave and a wave pair per 16 heads);
+    for each split count both kernels give the same bits, and the oracle's
+    result on every row."""
+    import sparse_shared_kv_amd as s
+    kw = dict(family="sfa", max_kv=3000, topk=1024, num_heads_q=128, rope_head_dim=64,
+              separate_v=False, sinks=True, lse=True)
+    if fmt != "bf16":
+        kw.update(kv_dtype=fmt)
+    P = synth.random_tiny(1200, **kw)
+    rows = list(range(P.query_rows))
+    ref = oracle.forward(P, rows=rows)
+    for split_rows, nsplit in ((1024, 1), (512, 2), (352, 3), (256, 4), (224, 5), (160, 7),
+                               (128, 8), (96, 11), (64, 16)):
+        assert -(-1024 // split_rows) == nsplit
+        outs = []
+        for wp in (1, 2):
+            say(f"merge rounds {fmt} split_rows={split_rows} wave_pairs={wp}")
+            call = s.Call(dict(P.params, split_rows=split_rows, wave_pairs=wp), P.arrays)
+            outs.append([None if t is None else t.clone() for t in call.run()])
+            torch.cuda.synchronize()
+            assert int(call.status.item()) == 0
+        assert torch.equal(outs[0][0], outs[1][0]), split_rows
+        assert torch.equal(outs[0][1], outs[1][1]), split_rows
+        res = dict(O=outs[1][0].float().cpu().numpy(), status=0, lse=outs[1][1].cpu().numpy())
+        check_outputs(P, res, ref, rows)
+
+
 def test_wave_pairs_on_random_tiny_cases_bitwise():
     """Random small problems of every family and layout (bf16 and float16):
     wave pairs forced on and off give the same bits."""
