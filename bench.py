@@ -373,6 +373,10 @@ def main():
                     help="sfmla_params.split_rows (0: the library's rule)")
     ap.add_argument("--query-tile", type=int, default=0,
                     help="sfmla_params.query_tile (0: the library's rule; 1: no query tiles)")
+    ap.add_argument("--head-blocks-per-group", type=int, default=0,
+                    help="sfmla_params.head_blocks_per_group (0: the library's rule)")
+    ap.add_argument("--wave-pairs", type=int, default=0,
+                    help="sfmla_params.wave_pairs (0: the library's rule; 1: off; 2: on)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--profile-commands", metavar="OUTDIR",
@@ -509,7 +513,8 @@ def measure(P, args, dev, steps, warmup, settle_ms, time_every, replicas):
     import synth
 
     spec = dict(P.params, merge_wait_us=args.merge_wait_us, split_rows=args.split_rows,
-                query_tile=args.query_tile)
+                query_tile=args.query_tile, head_blocks_per_group=args.head_blocks_per_group,
+                wave_pairs=args.wave_pairs)
     call = s.Call(spec, P.arrays, device=dev)
     reps = synth.index_replicas(P, replicas - 1) if replicas > 1 else []
     idx_sets, counts_all = [], [recipe_rows(P)]
