@@ -1927,10 +1927,9 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
     }
   }
 
-  if (!owned_here) {
-    // store this split's partial (bf16, in the lanes' fragment order:
-    // instruction j of a wave writes 1 KB contiguously), count in; the last
-    // to arrive merges every split's partial of these heads
+  // this split's partial (bf16, in the lanes' fragment order: instruction j
+  // of a wave writes 1 KB contiguously) and its LSEs
+  auto store_partial = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const float inv = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;
@@ -1949,6 +1948,106 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
       if (g == 0)
         st_agent(a.ws_lse + ((int64_t)row * a.max_splits + split) * HP + h0 + 16 * hb + t, lse2[hb]);
     }
+  };
+
+  // Rows of two splits (no owned merge): arrival is counted before the
+  // partial is stored.  The first split to arrive stores its partial and
+  // then counts it stored (the counter's upper half); the second waits for
+  // that count and merges the stored partial with its own, still in
+  // registers, so it neither stores its own partial nor loads it back.  Its
+  // own partial's bits are formed as the store forms them and the two are
+  // added in split order, so the result is the bits of the merge below.
+  // (Not in the four-wave kernel, whose rows take one split, nor with wave
+  // pairs, whose small launches measured slower with it.)
+  auto two_splits = [&]() __attribute__((always_inline)) {
+    int old = 0;
+    if (l == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((__builtin_amdgcn_readfirstlane(old) & 0xffff) == 0) {
+      store_partial();
+      drain_vmem();                                 // stored before it is counted
+      if (l == 0) __hip_atomic_fetch_add(ctr, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // the other split has arrived and is storing (it waits for nothing)
+    for (;;) {
+      const int c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_readfirstlane(c) >> 16) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (l == 0)                                     // ready for the next call
+      __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int other = 1 - split;
+    const int split_bytes = a.groups * NW * WAVE_BYTES;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = h0 + 16 * hb + t;
+      const float* lp = a.ws_lse + (int64_t)row * a.max_splits * HP + h;
+      const int off = other * split_bytes + (hg * NW + w) * WAVE_BYTES + ((hb * NFR) * 64 + l) * 16;
+      const float lx = ld_agent(lp + (int64_t)other * HP);
+      u32x4 v[NFR];
+#pragma unroll
+      for (int j = 0; j < NFR; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + j * 64 * 16, 0, kSc1);
+      const float l0 = split == 0 ? lse2[hb] : lx, l1 = split == 0 ? lx : lse2[hb];
+      const float M = fmaxf(fmaxf(kNegInf, l0), l1);
+      const float Mu = M == kNegInf ? 0.f : M;
+      const float e0 = __builtin_amdgcn_exp2f(l0 - Mu), e1 = __builtin_amdgcn_exp2f(l1 - Mu);
+      float tot = 0.f;
+      tot += e0;
+      tot += e1;
+      float den = tot;
+      if (a.has_sinks && h < a.qn && tot > 0.f)
+        den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - Mu);
+      const float inv = tot > 0.f ? 1.f / den : 0.f;
+      const float io = lt[hb] > 0.f ? 1.f / lt[hb] : 0.f;   // as the store scales it
+      const bool on = h < a.qn;
+      uint16_t* op = a.out + ((int64_t)row * a.qn + (on ? h : 0)) * 512 + 4 * g + 256 * hf;
+#pragma unroll
+      for (int j = 0; j < NFR; ++j) {
+        uint32_t own[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4& oc = o[hb][2 * j + (e >> 1)];
+          own[e] = (uint32_t)to16<HALF>(oc[2 * (e & 1)] * io) |
+                   ((uint32_t)to16<HALF>(oc[2 * (e & 1) + 1] * io) << 16);
+        }
+        const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x0 = split == 0 ? own[e] : u[e];
+          c[2 * e] = __builtin_fmaf(e0, lo16<HALF>(x0), c[2 * e]);
+          c[2 * e + 1] = __builtin_fmaf(e0, hi16<HALF>(x0), c[2 * e + 1]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x1 = split == 0 ? u[e] : own[e];
+          c[2 * e] = __builtin_fmaf(e1, lo16<HALF>(x1), c[2 * e]);
+          c[2 * e + 1] = __builtin_fmaf(e1, hi16<HALF>(x1), c[2 * e + 1]);
+        }
+        if (on) {
+          uint2 p0, p1;
+          p0.x = (uint32_t)to16<HALF>(c[0] * inv) | ((uint32_t)to16<HALF>(c[1] * inv) << 16);
+          p0.y = (uint32_t)to16<HALF>(c[2] * inv) | ((uint32_t)to16<HALF>(c[3] * inv) << 16);
+          p1.x = (uint32_t)to16<HALF>(c[4] * inv) | ((uint32_t)to16<HALF>(c[5] * inv) << 16);
+          p1.y = (uint32_t)to16<HALF>(c[6] * inv) | ((uint32_t)to16<HALF>(c[7] * inv) << 16);
+          *(uint2*)(op + 16 * (2 * j)) = p0;
+          *(uint2*)(op + 16 * (2 * j + 1)) = p1;
+        }
+      }
+      if (on && a.lse && g == 0 && hf == 0)
+        a.lse[(int64_t)row * a.qn + h] = tot > 0.f ? (Mu + __builtin_log2f(tot)) * kLn2 : kNegInf;
+    }
+  };
+
+  bool two = false;
+  if constexpr (!W4 && !PAIR) two = nsplit == 2 && !own_mode;
+  if (two) {
+    two_splits();
+  } else if (!owned_here) {
+    // store this split's partial, count in; the last to arrive merges every
+    // split's partial of these heads
+    store_partial();
     drain_vmem();                                   // this wave's partial is stored
     // Arrival is counted per (row, head group, wave): the last of the
     // splits' waves for these 16 heads merges them (unless their owner
