@@ -2060,10 +2060,11 @@ __global__ __launch_bounds__(NW * 64, (kTwoPerCu<NW, FMT> ? 2 : 1)) void fwd_ker
       if (l == 0)                                   // ready for the next call
         __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // splits per round: two where the row has at most two (every column
-      // block in one or two rounds, no spare slot), else four, or eight for
-      // the half-width partials of wave pairs (32 loads per lane: more
-      // registers are free than where a wave holds all 512 columns).  Spare
-      // slots load the last split again and weigh it zero.
+      // block in one or two rounds, no spare slot), else four; eight where
+      // a wave pair's row has more than four (32 loads per lane of its
+      // half-width partials: more registers are free than where a wave
+      // holds all 512 columns).  Spare slots load the last split again and
+      // weigh it zero.
       if constexpr (PAIR) {
         if (nsplit <= 2) merge_last(IntC<2>{}, IntC<8>{}, IntC<1>{});
         else if (nsplit <= 4) merge_last(IntC<4>{}, IntC<4>{}, IntC<0>{});
