@@ -265,6 +265,39 @@ def test_metadata_from_other_params_is_rejected():
     assert int(call.status.item()) & 1
 
 
+@pytest.mark.parametrize("fmt,split_rows,wp", [("bf16", 512, 1), ("bf16", 512, 2),
+                                              ("int8_packed", 512, 1), ("int8_packed", 256, 2),
+                                              ("bf16", 256, 1)])
+def test_forward_reuses_metadata_across_calls_bitwise(fmt, split_rows, wp):
+    """One plan, then the forward called again and again on it (as the
+    layers of a model step would): the merges leave their arrival counters
+    ready for the next call, so every call rewrites the same bits (two
+    splits, merged from registers; four splits, merged by the last to
+    arrive or by their owners)."""
+    import sparse_shared_kv_amd as s
+    kw = dict(family="sfa", max_kv=3000, topk=1024, num_heads_q=128, rope_head_dim=64,
+              separate_v=False, sinks=True, lse=True)
+    if fmt != "bf16":
+        kw.update(kv_dtype=fmt)
+    P = synth.random_tiny(1210, **kw)
+    call = s.Call(dict(P.params, split_rows=split_rows, wave_pairs=wp), P.arrays)
+    first = [t.clone() for t in call.run() if t is not None]
+    torch.cuda.synchronize()
+    assert int(call.status.item()) == 0
+    for rep in range(3):
+        say(f"forward again {fmt} split_rows={split_rows} wave_pairs={wp} call {rep + 2}")
+        for t in (call.out, call.lse):
+            t.fill_(float("nan"))
+        call.forward()
+        torch.cuda.synchronize()
+        assert int(call.status.item()) == 0
+        for e, x in zip(first, (call.out, call.lse)):
+            assert torch.equal(e, x), rep
+    rows = list(range(P.query_rows))
+    res = dict(O=first[0].float().cpu().numpy(), status=0, lse=first[1].cpu().numpy())
+    check_outputs(P, res, oracle.forward(P, rows=rows), rows)
+
+
 @pytest.mark.parametrize("far_sink", [False, True])
 def test_combine_entry_point_matches_oracle_merge(far_sink):
     """sfmla_combine (the LSE merge of caller-supplied partials) against the
