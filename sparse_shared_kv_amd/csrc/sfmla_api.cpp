@@ -321,7 +321,11 @@ size_t metadata_ints(const sfmla_params& p) {
 // past this bound it hands the merge to the last split to arrive).
 constexpr int kMergeWaitUs = 40;
 
-// Workgroups below which a launch spreads a row's heads over several groups.
+// Workgroups below which a launch spreads a row's heads over several groups,
+// and the most it spreads them to: one workgroup per CU of the eight-wave
+// kernels, a single round (a grouping past it runs its workgroups in two
+// rounds: packed decode with 6 splits of 8 rows, 384 workgroups of one wave
+// pair each, took 54 us against 31 for 192 of two pairs).
 constexpr int64_t kMinGroups = 256;
 
 // Split partials: normalised bf16 partial O for every (row, split, padded
@@ -381,7 +385,9 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg, bool* 
     per = std::min(per, pblocks);
     if (per == 3) per = 2;
     if (!p.head_blocks_per_group)
-      while (per > 1 && units * ((pblocks + per - 1) / per) < kMinGroups) per /= 2;
+      while (per > 1 && units * ((pblocks + per - 1) / per) < kMinGroups &&
+             units * ((pblocks + per / 2 - 1) / (per / 2)) <= kMinGroups)
+        per /= 2;
     *bpg = per;
     *groups = (pblocks + per - 1) / per;
     return;
@@ -407,7 +413,9 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg, bool* 
   }
   int per = 1;                                         // blocks per group: 1, 2, 4 or 8
   while (per < wmax && per < blocks) per *= 2;
-  while (per > 1 && units * ((blocks + per - 1) / per) < kMinGroups) per /= 2;
+  while (per > 1 && units * ((blocks + per - 1) / per) < kMinGroups &&
+         units * ((blocks + per / 2 - 1) / (per / 2)) <= kMinGroups)
+    per /= 2;
   *bpg = per;
   *groups = (blocks + per - 1) / per;
 }
