@@ -474,3 +474,30 @@ def test_q_rope_apart_is_validated():
     st = lib.sfmla_forward(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(4096), n.value,
                            ctypes.c_float(0.05), None, 0, None)
     assert st == 1 and b"q_rope" in lib.sfmla_last_error()
+
+
+@pytest.mark.parametrize("topk", [1024, 1280, 1536, 1792, 2048])
+def test_head_grouping_stays_within_one_round_of_workgroups(topk):
+    """Packed decode of 8 rows, 128 heads: the heads are spread over head
+    groups (wave pairs) only as far as one round of 256 workgroups allows.
+    Read back from the workspace size: q_t * splits * heads-as-laid-out
+    slots of 1 KB of partial O and one LSE each."""
+    P = synth.random_tiny(77, family="sfa", kv_dtype="int8_packed", rope_head_dim=64,
+                          num_heads_q=128, max_kv=4096, topk=topk, batch=8, q_lens=[1] * 8,
+                          ori_lens=[4096] * 8, layout_q="BSND", layout_kv="PA_BSND",
+                          block_size=64, separate_v=False)
+    splits = -(-topk // 256)                          # 256-row splits of packed rows
+    ws = s.sfmla_workspace_size(s.make_params(P.params, P.arrays))
+    slots = 8 * splits
+    heads = None
+    for h in range(1, 1025):                          # the one padded head count that fits
+        o = (slots * h * 1024 + 255) // 256 * 256
+        lse = (slots * h * 4 + 255) // 256 * 256
+        if o + lse == ws:
+            heads = h
+            break
+    assert heads is not None and heads % 64 == 0, (ws, heads)
+    groups = heads // 64                              # eight waves of 8 pair-heads each
+    assert slots * groups <= 256, (topk, groups)
+    # and the heads are spread as far as that allows (pairs of 16 heads: 8 blocks)
+    assert slots * min(8, 2 * groups) > 256 or groups == 8, (topk, groups)
