@@ -373,10 +373,14 @@ void choose_groups(const sfmla_params& p, int* nw, int* groups, int* bpg, bool* 
   }
   const int64_t units = (int64_t)p.q_t * max_splits(p);
   // Wave pairs: eight waves, bpg pairs of 16 heads per head group (every
-  // wave's partial is 16 heads x 256 columns)
+  // wave's partial is 16 heads x 256 columns).  By rule only where even
+  // four pairs per group keep the launch within one round (packed rows, 40
+  // rows of 4 splits, 128 heads: 320 workgroups of pairs took 67 us, 160
+  // without pairs 54)
+  const int64_t pair_groups = ((p.num_heads_q + 15) / 16 + 3) / 4;
   const bool pairs = p.wave_pairs == 2 ||
                      (p.wave_pairs == 0 && pair_eligible(p) && p.head_blocks_per_group == 0 &&
-                      units < kMinGroups);
+                      units < kMinGroups && units * pair_groups <= kMinGroups);
   if (pairs) {
     if (pair) *pair = true;
     *nw = 8;
